@@ -1,0 +1,240 @@
+"""Paged block-table attention for AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over ``libpba.so`` (declared in ``include/pba.h``).  The
+functions below only marshal torch tensors into the C ABI: every step of
+kv_append, block_copy and paged_decode runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream.  There is no CPU
+fallback: if the library is missing, importing this package raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_plan",
+           "paged_decode_workspace_bytes", "set_validate", "PBAError", "lib_path", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libpba.so")
+
+
+if not os.path.exists(lib_path()):
+    raise ImportError(
+        f"{lib_path()} is missing: build it with `python -m block_table_attention_amd.build` "
+        "(or __graft_entry__.build()); there is no fallback path")
+
+_lib = ctypes.CDLL(lib_path())
+
+PBA_F32, PBA_BF16 = 0, 1
+STATUS = {0: "PBA_OK", -1: "PBA_ERR_NULL_ARG", -2: "PBA_ERR_BAD_DTYPE", -3: "PBA_ERR_BAD_SHAPE",
+          -4: "PBA_ERR_UNSUPPORTED", -5: "PBA_ERR_WORKSPACE_TOO_SMALL",
+          -6: "PBA_ERR_OUT_OF_RANGE", -7: "PBA_ERR_OVERLAP", -8: "PBA_ERR_HIP"}
+_DTYPES = {torch.float32: PBA_F32, torch.bfloat16: PBA_BF16}
+
+
+class PoolDesc(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32), ("k_stride_block", ctypes.c_int64),
+                ("k_stride_head", ctypes.c_int64), ("v_stride_block", ctypes.c_int64),
+                ("v_stride_head", ctypes.c_int64)]
+
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_P = ctypes.POINTER(PoolDesc)
+_SIGS = {
+    "pba_kv_append": (ctypes.c_int, [_P, _vp, _i64, _vp, _vp, _vp]),
+    "pba_block_copy": (ctypes.c_int, [_P, _vp, _vp, _i64, _vp]),
+    "pba_paged_decode": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float, _vp,
+                                        _vp, _i32, _vp, _sz, _vp]),
+    "pba_paged_decode_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _i32]),
+    "pba_paged_decode_plan": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32,
+                                             ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "pba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pba_set_validate": (ctypes.c_int, [ctypes.c_int]),
+    "pba_version": (ctypes.c_int, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTED = tuple(_SIGS)
+
+
+class PBAError(RuntimeError):
+    def __init__(self, call: str, status: int):
+        msg = _lib.pba_status_string(status).decode()
+        super().__init__(f"{call}: {STATUS.get(status, status)} ({msg})")
+        self.status = status
+
+
+def _check(call: str, status: int) -> None:
+    if status != 0:
+        raise PBAError(call, status)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return int(stream.cuda_stream)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+@dataclass
+class KVPool:
+    """One layer's K/V pool: K [NB, H_kv, P, d] (token-major tiles) and
+    V [NB, H_kv, d, P] (dim-major tiles), both of the pool dtype."""
+
+    k: torch.Tensor
+    v: torch.Tensor
+
+    @classmethod
+    def empty(cls, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
+              dtype=torch.bfloat16, device="cuda") -> "KVPool":
+        k = torch.empty((num_blocks, num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
+        v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+        return cls(k, v)
+
+    @property
+    def num_blocks(self) -> int:
+        return self.k.shape[0]
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.k.shape[1]
+
+    @property
+    def block_size(self) -> int:
+        return self.k.shape[2]
+
+    @property
+    def head_dim(self) -> int:
+        return self.k.shape[3]
+
+    @property
+    def dtype(self):
+        return self.k.dtype
+
+    def desc(self) -> PoolDesc:
+        k, v = self.k, self.v
+        nb, h, p, d = k.shape
+        if v.shape != (nb, h, d, p) or v.dtype != k.dtype or v.device != k.device:
+            raise ValueError("V pool must be [num_blocks, H_kv, head_dim, block_size] of K's dtype")
+        if k.dtype not in _DTYPES:
+            raise TypeError(f"pool dtype {k.dtype} not supported")
+        if k.stride(2) != d or k.stride(3) != 1 or v.stride(2) != p or v.stride(3) != 1:
+            raise ValueError("pool tiles must be dense ([P][d] for K, [d][P] for V)")
+        return PoolDesc(k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], nb, p, h, d, 0,
+                        k.stride(0), k.stride(1), v.stride(0), v.stride(1))
+
+
+def _require(t: torch.Tensor, name: str, dtype, device, ndim: int):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if t.dim() != ndim or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous rank-{ndim} tensor")
+
+
+def kv_append(pool: KVPool, slot_mapping: torch.Tensor, k_new: torch.Tensor,
+              v_new: torch.Tensor, stream=None) -> None:
+    """Write row i of k_new/v_new [n, H_kv, d] at slot_mapping[i] (int64; < 0 skips)."""
+    dev = pool.k.device
+    _require(slot_mapping, "slot_mapping", torch.int64, dev, 1)
+    _require(k_new, "k_new", pool.dtype, dev, 3)
+    _require(v_new, "v_new", pool.dtype, dev, 3)
+    n = slot_mapping.shape[0]
+    if k_new.shape != (n, pool.num_kv_heads, pool.head_dim) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [n_tokens, H_kv, head_dim]")
+    d = pool.desc()
+    _check("pba_kv_append", _lib.pba_kv_append(ctypes.byref(d), _ptr(slot_mapping), n,
+                                               _ptr(k_new), _ptr(v_new), _stream(stream)))
+
+
+def block_copy(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    """Copy whole physical blocks src[k] -> dst[k] (int32 ids), K and V."""
+    dev = pool.k.device
+    _require(src, "src", torch.int32, dev, 1)
+    _require(dst, "dst", torch.int32, dev, 1)
+    if src.shape != dst.shape:
+        raise ValueError("src and dst must have the same length")
+    d = pool.desc()
+    _check("pba_block_copy", _lib.pba_block_copy(ctypes.byref(d), _ptr(src), _ptr(dst),
+                                                 src.shape[0], _stream(stream)))
+
+
+def paged_decode_plan(pool: KVPool, num_q_heads: int, batch: int, max_blocks_per_seq: int,
+                      partition_tokens: int = 0) -> Tuple[int, int]:
+    d = pool.desc()
+    pt, npart = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check("pba_paged_decode_plan", _lib.pba_paged_decode_plan(
+        ctypes.byref(d), num_q_heads, batch, max_blocks_per_seq, partition_tokens,
+        ctypes.byref(pt), ctypes.byref(npart)))
+    return pt.value, npart.value
+
+
+def paged_decode_workspace_bytes(pool: KVPool, num_q_heads: int, batch: int,
+                                 max_blocks_per_seq: int, partition_tokens: int = 0) -> int:
+    d = pool.desc()
+    return int(_lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), num_q_heads, batch,
+                                                     max_blocks_per_seq, partition_tokens))
+
+
+def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
+                 seq_lens: torch.Tensor, scale: Optional[float] = None,
+                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                 want_lse: bool = True, partition_tokens: int = 0,
+                 workspace: Optional[torch.Tensor] = None, stream=None):
+    """q [B, H_q, d] (pool dtype), block_tables int32 [B, max_blocks], seq_lens int32 [B].
+
+    Returns (out float32 [B, H_q, d], lse float32 [B, H_q] or None).
+    """
+    dev = pool.k.device
+    _require(q, "q", pool.dtype, dev, 3)
+    _require(block_tables, "block_tables", torch.int32, dev, 2)
+    _require(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, block_tables, seq_lens and the pool")
+    max_blocks = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    _require(out, "out", torch.float32, dev, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if lse is not None:
+        _require(lse, "lse", torch.float32, dev, 2)
+    d = pool.desc()
+    need = _lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), Hq, B, max_blocks, partition_tokens)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pba_paged_decode", _lib.pba_paged_decode(
+        ctypes.byref(d), _ptr(q), Hq, _ptr(block_tables), max_blocks, _ptr(seq_lens), B,
+        ctypes.c_float(scale), _ptr(out), _ptr(lse), partition_tokens, _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return out, lse
+
+
+def set_validate(on: bool) -> bool:
+    return bool(_lib.pba_set_validate(1 if on else 0))
+
+
+def version() -> int:
+    return int(_lib.pba_version())

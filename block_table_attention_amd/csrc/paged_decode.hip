@@ -1,0 +1,460 @@
+// paged_decode: one decode query row per request over its logical K/V history.
+//
+// The method ("M5.3 - KV Memory Layout and Exact Reuse", 0x0A): for each logical
+// block of the request, translate it through the block table, read its visible
+// rows (all P, or T mod P in the last block), score them against q, and fold
+// them into an online-softmax state (m, l, u); finally O = u / l.  Long rows
+// are cut into partitions of `part_tokens` tokens whose states are merged with
+// the log-sum-exp rule of 0x0BA (an empty partition is the identity; outputs
+// are never averaged).
+//
+// Work decomposition on gfx950 (256 CUs, 64-lane waves):
+//   work-group = (partition, kv head h, request r), 4 waves.  Wave w walks
+//   the partition's 32-token chunks w, w+4, w+8, ...; the four waves merge
+//   their states through LDS at the end, and the work-group writes either the
+//   final row (single partition) or its partition state (merged by
+//   pba_decode_merge_kernel).
+//
+// bf16 path: the G query heads of kv head h are processed together, so the
+// scores of a chunk are the small dense product S^T[32 tokens x G] =
+// K[32 x d] Q^T[d x G] and the value update is O^T[d x G] += V^T[d x 32]
+// P^T[32 x G].  Both run on v_mfma_f32_16x16x32_bf16 (G padded to 16 columns):
+//   * K tile is token major, so each lane's A-operand fragment (one token row,
+//     8 consecutive dims) is one 16-byte load straight from HBM;
+//   * V tile is dim major ([d][P]), so each lane's A-operand fragment for the
+//     value product (one dim, 8 consecutive tokens) is again one 16-byte load;
+//   * the token order inside a chunk is permuted so that the score fragment a
+//     lane receives (tokens 8g..8g+7 for its head) is exactly the B-operand
+//     fragment it needs for the value product: no cross-lane traffic.
+// No LDS staging: every loaded byte feeds exactly one MFMA of the wave that
+// loaded it.  Probabilities enter the value MFMA as a bf16 pair p = hi + lo
+// (hi = bf16(p), lo = bf16(p - hi)), which keeps ~16 significant bits.
+//
+// Visibility: positions t >= T (tail padding, rows materialised in a shared
+// block by a longer request, stale rows) are removed by selects -- scores to
+// -inf, V scalars to 0 -- never by multiplying by zero, since they may hold NaN.
+// Table entries at j >= ceil(T/P) are never read.
+#include "pba_internal.h"
+
+namespace pba {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+__device__ __forceinline__ float wave_max_xor(float x, int mask) {
+  return fmaxf(x, __shfl_xor(x, mask, 64));
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per-wave partial state, staged in LDS for the work-group merge.
+template <int D>
+struct WaveStates {
+  float m[kWaves][16];
+  float l[kWaves][16];
+  float o[kWaves][D][17];  // [dim][head], padded against bank conflicts
+};
+
+// Merge the 4 wave states of one work-group and write the final row or the
+// partition state.  Every thread participates.
+template <int D>
+__device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, int h, int part) {
+  const int G = a.G;
+  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+    const int n = idx / D;
+    const int c = idx - n * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st.m[w][n]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = st.m[w][n];
+        if (mw == -INFINITY) continue;  // a wave that saw no chunk: identity
+        const float wt = fast_exp2(mw - M);
+        L += wt * st.l[w][n];
+        O += wt * st.o[w][c][n];
+      }
+    }
+    const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
+    if (a.n_parts == 1) {
+      a.out[row * D + c] = (L > 0.f) ? O / L : 0.f;
+      if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t prow = row * a.n_parts + part;
+      a.ws_u[prow * D + c] = O;
+      if (c == 0) {
+        a.ws_ml[prow * 2 + 0] = M;
+        a.ws_ml[prow * 2 + 1] = L;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bf16 K/V, MFMA path
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int KK = D / 32;  // k-steps of the score product
+  constexpr int MT = D / 16;  // 16-dim tiles of the value product
+  constexpr int CH = 32;      // tokens per chunk
+
+  __shared__ WaveStates<D> st;
+
+  const int wg = blockIdx.x;
+  const int part = wg % a.n_parts;
+  const int rest = wg / a.n_parts;
+  const int h = rest % a.num_kv_heads;
+  const int r = rest / a.num_kv_heads;
+
+  const int T = a.seq_lens[r];
+  const int p_begin = part * a.part_tokens;
+  if (p_begin >= T) return;  // empty partition: the merge never reads it
+  const int p_end = min(T, p_begin + a.part_tokens);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;  // head column of this lane
+  const int g = lane >> 4;  // k-group of this lane
+  const int G = a.G;
+  const int log2P = a.log2P;
+  const int P = 1 << log2P;
+  const int nblk = (T + P - 1) >> log2P;
+
+  // Q^T fragments (B operand of the score product): lane holds dims
+  // 32kk + 8g .. +8 of query head n; padding heads are zero.
+  bf16x8 qf[KK];
+  {
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)r * a.num_q_heads + (int64_t)h * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
+      if (n >= G) raw = u32x4{0u, 0u, 0u, 0u};
+      qf[kk] = __builtin_bit_cast(bf16x8, raw);
+    }
+  }
+
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
+  const int32_t* trow = a.tables + (int64_t)r * a.max_blocks;
+
+  float m_run = -INFINITY;  // running max (log2 domain) of head n
+  float l_run = 0.f;        // this lane's share of the running sum
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int t0 = p_begin + wave * CH; t0 < p_end; t0 += kWaves * CH) {
+    // Physical blocks of the chunk: one when P >= 32, two when P == 16.
+    const int j0 = t0 >> log2P;
+    const int64_t pb0 = trow[j0];
+    int64_t pb1 = pb0;
+    if (log2P == 4 && j0 + 1 < nblk) pb1 = trow[j0 + 1];
+
+    // K fragments.  Tile a, A-operand row m = lane & 15 holds chunk token
+    // 8(m>>2) + 4a + (m&3); dims 32kk + 8g .. +8.
+    u32x4 kf[2][KK];
+#pragma unroll
+    for (int at = 0; at < 2; ++at) {
+      const int tk = 8 * (n >> 2) + 4 * at + (n & 3);
+      const int64_t pb = (tk >= 16 && log2P == 4) ? pb1 : pb0;
+      const int off = (t0 + tk) & (P - 1);
+      const uint16_t* kp = kpool + pb * a.k_sb + (int64_t)h * a.k_sh + (int64_t)off * D + 8 * g;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) kf[at][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
+    }
+    // V^T fragments.  Tile mt, A-operand row = dim 16mt + (lane & 15), k-slots
+    // = chunk tokens 8g .. 8g+7.
+    u32x4 vf[MT];
+    {
+      const int tv = 8 * g;
+      const int64_t pb = (tv >= 16 && log2P == 4) ? pb1 : pb0;
+      const int off = (t0 + tv) & (P - 1);
+      const uint16_t* vp = vpool + pb * a.v_sb + (int64_t)h * a.v_sh + (int64_t)n * P + off;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
+    }
+
+    // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
+    f32x4 s[2];
+#pragma unroll
+    for (int at = 0; at < 2; ++at) {
+      s[at] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[at][kk]),
+                                                         qf[kk], s[at], 0, 0, 0);
+    }
+
+    const int tbase = t0 + 8 * g;  // token of slot j = 0 of this lane
+    float x[8];
+#pragma unroll
+    for (int at = 0; at < 2; ++at)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * at + i;
+        const float v = s[at][i] * a.scale_log2;
+        x[j] = (tbase + j < T) ? v : -INFINITY;
+      }
+    float cmax = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
+    cmax = wave_max_xor(cmax, 16);
+    cmax = wave_max_xor(cmax, 32);
+    const float m_new = fmaxf(m_run, cmax);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = (n < G) ? fast_exp2(x[j] - m_new) : 0.f;
+      psum += p[j];
+    }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+
+    bf16x8 phi, plo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 hi = (__bf16)p[j];
+      phi[j] = hi;
+      plo[j] = (__bf16)(p[j] - (float)hi);
+    }
+
+    // Tail chunk: zero the V scalars of tokens >= T (they may hold NaN).
+    if (t0 + CH > T) {
+      const int cnt = T - tbase;  // valid tokens among this lane's 8
+      u32x4 mask;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        mask[q] = (cnt >= 2 * q + 2) ? 0xFFFFFFFFu : ((cnt == 2 * q + 1) ? 0x0000FFFFu : 0u);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) vf[mt] &= mask;
+    }
+
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const bf16x8 va = __builtin_bit_cast(bf16x8, vf[mt]);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[mt], 0, 0, 0);
+      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[mt], 0, 0, 0);
+    }
+  }
+
+  // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n].
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (g == 0) {
+    st.m[wave][n] = m_run;
+    st.l[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st.o[wave][16 * mt + 4 * g + i][n] = acc[mt][i];
+  __syncthreads();
+  finish_workgroup<D>(a, st, r, h, part);
+}
+
+// ---------------------------------------------------------------------------
+// fp32 K/V, VALU path (64-token chunks; lane = token for scores, lane = dim
+// for the value update)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int CH = 64;
+  constexpr int DPL = D / 64;  // dims per lane in the value update
+
+  __shared__ WaveStates<D> st;
+  __shared__ float sq[16][D];
+  __shared__ float sp[kWaves][16][CH];
+
+  const int wg = blockIdx.x;
+  const int part = wg % a.n_parts;
+  const int rest = wg / a.n_parts;
+  const int h = rest % a.num_kv_heads;
+  const int r = rest / a.num_kv_heads;
+
+  const int T = a.seq_lens[r];
+  const int p_begin = part * a.part_tokens;
+  if (p_begin >= T) return;
+  const int p_end = min(T, p_begin + a.part_tokens);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int G = a.G;
+  const int log2P = a.log2P;
+  const int P = 1 << log2P;
+  const int nblk = (T + P - 1) >> log2P;
+
+  const float* qsrc = static_cast<const float*>(a.q) + ((int64_t)r * a.num_q_heads + (int64_t)h * G) * D;
+  for (int i = threadIdx.x; i < 16 * D; i += kThreads) {
+    const int gg = i / D;
+    sq[gg][i - gg * D] = (gg < G) ? qsrc[i] : 0.f;
+  }
+  __syncthreads();
+
+  const float* kpool = static_cast<const float*>(a.k);
+  const float* vpool = static_cast<const float*>(a.v);
+  const int32_t* trow = a.tables + (int64_t)r * a.max_blocks;
+
+  float m_run[16], l_run[16], u[16][DPL];
+#pragma unroll
+  for (int gg = 0; gg < 16; ++gg) {
+    m_run[gg] = -INFINITY;
+    l_run[gg] = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) u[gg][e] = 0.f;
+  }
+
+  for (int t0 = p_begin + wave * CH; t0 < p_end; t0 += kWaves * CH) {
+    const int t = t0 + lane;
+    const bool valid = t < T;
+    const int j = min(t >> log2P, nblk - 1);
+    const int64_t pb = trow[j];
+    const float* krow = kpool + pb * a.k_sb + (int64_t)h * a.k_sh + (int64_t)(t & (P - 1)) * D;
+    float s[16];
+#pragma unroll
+    for (int gg = 0; gg < 16; ++gg) s[gg] = 0.f;
+    for (int c = 0; c < D; c += 4) {
+      const f32x4v kv = *reinterpret_cast<const f32x4v*>(krow + c);
+#pragma unroll
+      for (int gg = 0; gg < 16; ++gg)
+        if (gg < G) s[gg] += sq[gg][c] * kv[0] + sq[gg][c + 1] * kv[1] + sq[gg][c + 2] * kv[2] +
+                             sq[gg][c + 3] * kv[3];
+    }
+    float alpha[16];
+#pragma unroll
+    for (int gg = 0; gg < 16; ++gg) {
+      if (gg >= G) continue;
+      const float x = valid ? s[gg] * a.scale_log2 : -INFINITY;
+      float cm = x;
+#pragma unroll
+      for (int msk = 32; msk >= 1; msk >>= 1) cm = wave_max_xor(cm, msk);
+      const float m_new = fmaxf(m_run[gg], cm);
+      alpha[gg] = fast_exp2(m_run[gg] - m_new);
+      m_run[gg] = m_new;
+      const float pv = fast_exp2(x - m_new);
+      l_run[gg] = l_run[gg] * alpha[gg] + pv;
+      sp[wave][gg][lane] = pv;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int gg = 0; gg < 16; ++gg)
+      if (gg < G)
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) u[gg][e] *= alpha[gg];
+    // Value update: lane = dim c (+64), tokens t0 .. t0+63 in runs of 4.
+    for (int t4 = 0; t4 < CH; t4 += 4) {
+      const int tt = t0 + t4;
+      if (tt >= T) break;
+      const int jj = tt >> log2P;
+      const int64_t pbv = trow[jj];
+      const int off = tt & (P - 1);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const int c = lane + 64 * e;
+        f32x4v vv = *reinterpret_cast<const f32x4v*>(vpool + pbv * a.v_sb + (int64_t)h * a.v_sh +
+                                                     (int64_t)c * P + off);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (tt + q >= T) vv[q] = 0.f;
+#pragma unroll
+        for (int gg = 0; gg < 16; ++gg)
+          if (gg < G)
+            u[gg][e] += sp[wave][gg][t4] * vv[0] + sp[wave][gg][t4 + 1] * vv[1] +
+                        sp[wave][gg][t4 + 2] * vv[2] + sp[wave][gg][t4 + 3] * vv[3];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Wave state -> LDS: lane-partial sums reduce across the wave.
+#pragma unroll
+  for (int gg = 0; gg < 16; ++gg) {
+    if (gg >= G) continue;
+    float l = l_run[gg];
+#pragma unroll
+    for (int msk = 32; msk >= 1; msk >>= 1) l += __shfl_xor(l, msk, 64);
+    if (lane == 0) {
+      st.m[wave][gg] = m_run[gg];
+      st.l[wave][gg] = l;
+    }
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) st.o[wave][lane + 64 * e][gg] = u[gg][e];
+  }
+  __syncthreads();
+  finish_workgroup<D>(a, st, r, h, part);
+}
+
+// ---------------------------------------------------------------------------
+// Partition merge: O = sum_p w_p u_p / sum_p w_p l_p, w_p = 2^(m_p - M).
+// One work-group of D threads per (request, q head); partitions in index
+// order, so the result is deterministic.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
+  const int64_t row = blockIdx.x;  // r * H_q + head
+  const int r = (int)(row / a.num_q_heads);
+  const int c = threadIdx.x;
+  const int T = a.seq_lens[r];
+  const int np = min(a.n_parts, (T + a.part_tokens - 1) / a.part_tokens);
+  const float* ml = a.ws_ml + row * a.n_parts * 2;
+  const float* uu = a.ws_u + row * a.n_parts * D;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  float L = 0.f, O = 0.f;
+  if (M != -INFINITY) {
+    for (int p = 0; p < np; ++p) {
+      const float mp = ml[2 * p];
+      if (mp == -INFINITY) continue;
+      const float w = fast_exp2(mp - M);
+      L += w * ml[2 * p + 1];
+      O += w * uu[(int64_t)p * D + c];
+    }
+  }
+  a.out[row * D + c] = (L > 0.f) ? O / L : 0.f;
+  if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
+hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
+  const int64_t wgs = (int64_t)a.n_parts * a.num_kv_heads * a.batch;
+  const dim3 grid((unsigned)wgs), block(kThreads);
+  if (dtype == PBA_BF16) {
+    if (head_dim == 128)
+      hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, block, 0, stream, a);
+  } else {
+    if (head_dim == 128)
+      hipLaunchKernelGGL(decode_f32_kernel<128>, grid, block, 0, stream, a);
+    else
+      hipLaunchKernelGGL(decode_f32_kernel<64>, grid, block, 0, stream, a);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_parts == 1) return e;
+  const dim3 mgrid((unsigned)((int64_t)a.batch * a.num_q_heads));
+  if (head_dim == 128)
+    hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(128), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace pba

@@ -1,0 +1,318 @@
+// Host side of libpba.so: argument checks, the split planner, validate mode
+// and kernel launches.  Everything the host can check is checked before any
+// launch, so a rejected call leaves every device byte unchanged ("M5.3 - KV
+// Memory Layout and Exact Reuse", 0x05G: rejected operations preserve the
+// predecessor state; "Cache Concepts: Prefix Matching vs. Storage": validate
+// every id before touching bytes).
+#include <atomic>
+#include <cstring>
+#include <mutex>
+#include <unordered_set>
+#include <vector>
+
+#include "pba_internal.h"
+
+namespace {
+
+std::atomic<int> g_validate{0};
+
+constexpr int kPartGranule = 256;  // partition lengths are multiples of this
+
+int log2_exact(int x) {
+  if (x <= 0 || (x & (x - 1))) return -1;
+  int l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+int esize_of(int dtype) { return dtype == PBA_BF16 ? 2 : 4; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Checks the pool descriptor; everything here is host-visible.
+int check_pool(const pba_kv_pool* pool) {
+  if (!pool) return PBA_ERR_NULL_ARG;
+  if (pool->dtype != PBA_F32 && pool->dtype != PBA_BF16) return PBA_ERR_BAD_DTYPE;
+  if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0 || pool->block_size <= 0 ||
+      pool->head_dim <= 0 || pool->reserved0 != 0)
+    return PBA_ERR_BAD_SHAPE;
+  const int lp = log2_exact(pool->block_size);
+  if (lp < 4 || lp > 8) return PBA_ERR_UNSUPPORTED;  // P in {16, ..., 256}
+  if (pool->head_dim != 64 && pool->head_dim != 128) return PBA_ERR_UNSUPPORTED;
+  if (!pool->k || !pool->v) return PBA_ERR_NULL_ARG;
+  const int64_t tile = (int64_t)pool->block_size * pool->head_dim;
+  const int es = esize_of(pool->dtype);
+  const int64_t strides[4] = {pool->k_stride_block, pool->k_stride_head, pool->v_stride_block,
+                              pool->v_stride_head};
+  for (int64_t s : strides) {
+    if (s < 0) return PBA_ERR_BAD_SHAPE;
+    if ((s * es) % 16) return PBA_ERR_UNSUPPORTED;
+  }
+  // A tile must fit in its stride, and the heads of one block in the block stride.
+  if (pool->num_kv_heads > 1 && (pool->k_stride_head < tile || pool->v_stride_head < tile))
+    return PBA_ERR_BAD_SHAPE;
+  if (pool->num_blocks > 1 &&
+      (pool->k_stride_block < tile || pool->v_stride_block < tile))
+    return PBA_ERR_BAD_SHAPE;
+  if (!aligned16(pool->k) || !aligned16(pool->v)) return PBA_ERR_UNSUPPORTED;
+  return PBA_OK;
+}
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// Split planner.  Partitions are multiples of 256 tokens (so every block size
+// P <= 256 divides them and 32/64-token chunks never straddle one).  Without
+// an explicit length the planner aims at ~4 work-groups per CU over the
+// longest row the table can describe (the host does not see seq_lens).
+int plan_partitions(const pba_kv_pool* pool, int32_t batch, int32_t max_blocks, int32_t requested,
+                    int32_t* part_tokens, int32_t* n_parts) {
+  const int64_t max_T = (int64_t)max_blocks * pool->block_size;
+  if (max_T <= 0) return PBA_ERR_BAD_SHAPE;
+  int64_t pt;
+  if (requested > 0) {
+    if (requested % kPartGranule) return PBA_ERR_UNSUPPORTED;
+    pt = requested;
+  } else if (requested < 0) {
+    return PBA_ERR_BAD_SHAPE;
+  } else {
+    const int64_t units = (int64_t)batch * pool->num_kv_heads;
+    const int64_t target = 4LL * device_cu_count();
+    const int64_t max_splits = (max_T + kPartGranule - 1) / kPartGranule;
+    int64_t splits = (target + units - 1) / units;
+    if (splits < 1) splits = 1;
+    if (splits > max_splits) splits = max_splits;
+    const int64_t per = (max_T + splits - 1) / splits;
+    pt = (per + kPartGranule - 1) / kPartGranule * kPartGranule;
+  }
+  const int64_t np = (max_T + pt - 1) / pt;
+  if (pt > INT32_MAX || np > INT32_MAX) return PBA_ERR_UNSUPPORTED;
+  *part_tokens = (int32_t)pt;
+  *n_parts = (int32_t)np;
+  return PBA_OK;
+}
+
+size_t workspace_layout(int64_t rows, int32_t n_parts, int head_dim, size_t* u_offset) {
+  if (n_parts <= 1) {
+    *u_offset = 0;
+    return 0;
+  }
+  const size_t ml = (size_t)rows * n_parts * 2 * sizeof(float);
+  const size_t off = (ml + 255) / 256 * 256;
+  *u_offset = off;
+  return off + (size_t)rows * n_parts * head_dim * sizeof(float);
+}
+
+template <typename T>
+bool copy_to_host(std::vector<T>& dst, const T* src, int64_t n, hipStream_t stream) {
+  dst.resize((size_t)n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(dst.data(), src, (size_t)n * sizeof(T), hipMemcpyDeviceToHost, stream) !=
+      hipSuccess)
+    return false;
+  return hipStreamSynchronize(stream) == hipSuccess;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pba_version(void) { return 100; }
+
+int pba_set_validate(int on) { return g_validate.exchange(on ? 1 : 0); }
+
+const char* pba_status_string(int status) {
+  switch (status) {
+    case PBA_OK: return "ok";
+    case PBA_ERR_NULL_ARG: return "a required pointer is NULL";
+    case PBA_ERR_BAD_DTYPE: return "unsupported or unknown dtype";
+    case PBA_ERR_BAD_SHAPE: return "bad size, head count or stride";
+    case PBA_ERR_UNSUPPORTED: return "block size, head_dim, head ratio, alignment or partition length not supported";
+    case PBA_ERR_WORKSPACE_TOO_SMALL: return "workspace missing or too small";
+    case PBA_ERR_OUT_OF_RANGE: return "block id, slot or sequence length out of range";
+    case PBA_ERR_OVERLAP: return "duplicate slot or overlapping copy pairs";
+    case PBA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int pba_kv_append(const pba_kv_pool* pool, const int64_t* slot_mapping, int64_t n_tokens,
+                  const void* k_new, const void* v_new, void* stream) {
+  int st = check_pool(pool);
+  if (st) return st;
+  if (n_tokens < 0) return PBA_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return PBA_OK;
+  if (!slot_mapping || !k_new || !v_new) return PBA_ERR_NULL_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PBA_ERR_UNSUPPORTED;
+  if ((n_tokens + 63) / 64 > INT32_MAX || pool->num_kv_heads > 65535) return PBA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    std::vector<int64_t> slots;
+    if (!copy_to_host(slots, slot_mapping, n_tokens, s)) return PBA_ERR_HIP;
+    const int64_t limit = (int64_t)pool->num_blocks * pool->block_size;
+    std::unordered_set<int64_t> seen;
+    for (int64_t x : slots) {
+      if (x < 0) continue;
+      if (x >= limit) return PBA_ERR_OUT_OF_RANGE;
+      if (!seen.insert(x).second) return PBA_ERR_OVERLAP;
+    }
+  }
+  pba::AppendArgs a;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_sb = pool->k_stride_block;
+  a.k_sh = pool->k_stride_head;
+  a.v_sb = pool->v_stride_block;
+  a.v_sh = pool->v_stride_head;
+  a.slots = slot_mapping;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.n = n_tokens;
+  a.log2P = log2_exact(pool->block_size);
+  a.head_dim = pool->head_dim;
+  a.kv_heads = pool->num_kv_heads;
+  return pba::launch_kv_append(a, esize_of(pool->dtype), s) == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* dst,
+                   int64_t n_pairs, void* stream) {
+  int st = check_pool(pool);
+  if (st) return st;
+  if (n_pairs < 0) return PBA_ERR_BAD_SHAPE;
+  if (n_pairs == 0) return PBA_OK;
+  if (!src || !dst) return PBA_ERR_NULL_ARG;
+  if (n_pairs > INT32_MAX || 2LL * pool->num_kv_heads > 65535) return PBA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    std::vector<int32_t> hs, hd;
+    if (!copy_to_host(hs, src, n_pairs, s) || !copy_to_host(hd, dst, n_pairs, s)) return PBA_ERR_HIP;
+    std::unordered_set<int32_t> dsts, srcs(hs.begin(), hs.end());
+    for (int64_t i = 0; i < n_pairs; ++i) {
+      if (hs[i] < 0 || hs[i] >= pool->num_blocks || hd[i] < 0 || hd[i] >= pool->num_blocks)
+        return PBA_ERR_OUT_OF_RANGE;
+      if (!dsts.insert(hd[i]).second || srcs.count(hd[i])) return PBA_ERR_OVERLAP;
+    }
+  }
+  pba::CopyArgs a;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_sb = pool->k_stride_block;
+  a.k_sh = pool->k_stride_head;
+  a.v_sb = pool->v_stride_block;
+  a.v_sh = pool->v_stride_head;
+  a.src = src;
+  a.dst = dst;
+  a.esize = esize_of(pool->dtype);
+  a.tile_bytes = (int64_t)pool->block_size * pool->head_dim * a.esize;
+  return pba::launch_block_copy(a, n_pairs, pool->num_kv_heads, s) == hipSuccess ? PBA_OK
+                                                                                 : PBA_ERR_HIP;
+}
+
+int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
+                          int32_t max_blocks_per_seq, int32_t partition_tokens,
+                          int32_t* partition_tokens_out, int32_t* num_partitions_out) {
+  int st = check_pool(pool);
+  if (st) return st;
+  if (num_q_heads <= 0 || batch < 0 || max_blocks_per_seq <= 0) return PBA_ERR_BAD_SHAPE;
+  if (num_q_heads % pool->num_kv_heads) return PBA_ERR_BAD_SHAPE;
+  if (num_q_heads / pool->num_kv_heads > 16) return PBA_ERR_UNSUPPORTED;
+  int32_t pt = 0, np = 0;
+  st = plan_partitions(pool, batch > 0 ? batch : 1, max_blocks_per_seq, partition_tokens, &pt, &np);
+  if (st) return st;
+  if (partition_tokens_out) *partition_tokens_out = pt;
+  if (num_partitions_out) *num_partitions_out = np;
+  return PBA_OK;
+}
+
+size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_heads,
+                                        int32_t batch, int32_t max_blocks_per_seq,
+                                        int32_t partition_tokens) {
+  int32_t pt = 0, np = 0;
+  if (pba_paged_decode_plan(pool, num_q_heads, batch, max_blocks_per_seq, partition_tokens, &pt,
+                            &np))
+    return 0;
+  size_t off = 0;
+  return workspace_layout((int64_t)batch * num_q_heads, np, pool->head_dim, &off);
+}
+
+int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t batch, float scale, float* out, float* lse,
+                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  int st = check_pool(pool);
+  if (st) return st;
+  if (batch < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PBA_ERR_BAD_SHAPE;
+  if (num_q_heads % pool->num_kv_heads) return PBA_ERR_BAD_SHAPE;
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G > 16) return PBA_ERR_UNSUPPORTED;
+  if (batch == 0) return PBA_OK;
+  if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
+  if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
+  int32_t pt = 0, np = 0;
+  st = plan_partitions(pool, batch, max_blocks_per_seq, partition_tokens, &pt, &np);
+  if (st) return st;
+  const int64_t rows = (int64_t)batch * num_q_heads;
+  const int64_t wgs = (int64_t)np * pool->num_kv_heads * batch;
+  if (wgs > INT32_MAX || rows > INT32_MAX) return PBA_ERR_UNSUPPORTED;
+  size_t u_off = 0;
+  const size_t need = workspace_layout(rows, np, pool->head_dim, &u_off);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PBA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    std::vector<int32_t> lens, tab;
+    if (!copy_to_host(lens, seq_lens, batch, s)) return PBA_ERR_HIP;
+    if (!copy_to_host(tab, block_tables, (int64_t)batch * max_blocks_per_seq, s)) return PBA_ERR_HIP;
+    const int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
+    for (int32_t r = 0; r < batch; ++r) {
+      const int64_t T = lens[r];
+      if (T < 1 || T > cap) return PBA_ERR_OUT_OF_RANGE;
+      const int64_t nb = (T + pool->block_size - 1) / pool->block_size;
+      for (int64_t j = 0; j < nb; ++j) {
+        const int32_t b = tab[(size_t)r * max_blocks_per_seq + j];
+        if (b < 0 || b >= pool->num_blocks) return PBA_ERR_OUT_OF_RANGE;
+      }
+    }
+  }
+  pba::DecodeArgs a;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_sb = pool->k_stride_block;
+  a.k_sh = pool->k_stride_head;
+  a.v_sb = pool->v_stride_block;
+  a.v_sh = pool->v_stride_head;
+  a.q = q;
+  a.tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.ws_u = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + u_off) : nullptr;
+  a.max_blocks = max_blocks_per_seq;
+  a.log2P = log2_exact(pool->block_size);
+  a.G = G;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.batch = batch;
+  a.part_tokens = pt;
+  a.n_parts = np;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return pba::launch_paged_decode(a, pool->dtype, pool->head_dim, s) == hipSuccess ? PBA_OK
+                                                                                  : PBA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+// Internal declarations shared by the libpba.so translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pba.h"
+
+namespace pba {
+
+// Argument bundle of the append kernel (all pointers device, strides elements).
+struct AppendArgs {
+  void* k;
+  void* v;
+  int64_t k_sb, k_sh, v_sb, v_sh;
+  const int64_t* slots;
+  const void* k_new;
+  const void* v_new;
+  int64_t n;
+  int32_t log2P;
+  int32_t head_dim;
+  int32_t kv_heads;
+};
+
+struct CopyArgs {
+  void* k;
+  void* v;
+  int64_t k_sb, k_sh, v_sb, v_sh;
+  const int32_t* src;
+  const int32_t* dst;
+  int64_t tile_bytes;  // P * head_dim * scalar bytes
+  int32_t esize;
+};
+
+// Decode: one work-group per (partition, kv head, request).
+struct DecodeArgs {
+  const void* k;
+  const void* v;
+  int64_t k_sb, k_sh, v_sb, v_sh;
+  const void* q;
+  const int32_t* tables;
+  const int32_t* seq_lens;
+  float* out;
+  float* lse;
+  float* ws_ml;  // [B][H_q][n_parts][2]: running max (log2 domain), sum
+  float* ws_u;   // [B][H_q][n_parts][D]: unnormalised output
+  int32_t max_blocks;
+  int32_t log2P;
+  int32_t G;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t batch;
+  int32_t part_tokens;
+  int32_t n_parts;
+  float scale_log2;  // scale * log2(e): scores live in the log2 domain
+};
+
+hipError_t launch_kv_append(const AppendArgs& a, int esize, hipStream_t stream);
+hipError_t launch_block_copy(const CopyArgs& a, int64_t n_pairs, int kv_heads, hipStream_t stream);
+hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+
+}  // namespace pba

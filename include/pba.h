@@ -1,0 +1,190 @@
+/*
+ * pba.h -- paged block-table attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpba.so: the data-plane calls of decode-time attention over a
+ * paged KV cache.  A request keeps one logical token order; its block table
+ * maps logical block j (tokens [j*P, (j+1)*P)) to a physical block of a shared
+ * pool, and the last block holds T mod P rows (P when that is 0).
+ * ("M5.3 - KV Memory Layout and Exact Reuse", sections 0x00A, 0x03A-0x03D,
+ * 0x0A; "7. Memory Management and Local Model State", "Logical tokens,
+ * physical blocks".)
+ *
+ * Allocation of blocks (free FIFO, reference counts, fork, copy-on-write
+ * decisions) belongs to the caller; the library only moves and reads bytes.
+ *
+ * Conventions for every call
+ *   - All buffers are device memory owned by the caller; the library never
+ *     allocates, frees or retains them past the call.  Every call is
+ *     asynchronous on `stream` (a hipStream_t; NULL = the null stream) and is
+ *     ordered against other work only by that stream.
+ *   - Return value: PBA_OK (0) or a negative pba_status.  Arguments the host
+ *     can check (pointers, sizes, shapes, strides, dtypes, workspace size) are
+ *     checked before any launch, so a rejected call changes no device byte.
+ *     Values that live on the device (block ids, slots, sequence lengths) are
+ *     checked only in validate mode (pba_set_validate); outside it,
+ *     out-of-range device values are undefined behaviour.
+ *   - n == 0 (tokens, pairs, batch) is a successful no-op.
+ *   - Thread safety: calls may be made from several host threads; they share
+ *     no mutable state except the process-wide validate flag.
+ */
+#ifndef PBA_H_
+#define PBA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pba_status {
+  PBA_OK = 0,
+  PBA_ERR_NULL_ARG = -1,            /* a required pointer is NULL              */
+  PBA_ERR_BAD_DTYPE = -2,           /* dtype not PBA_F32 / PBA_BF16            */
+  PBA_ERR_BAD_SHAPE = -3,           /* negative size, head counts, strides     */
+  PBA_ERR_UNSUPPORTED = -4,         /* valid but not built: P, head_dim, G     */
+  PBA_ERR_WORKSPACE_TOO_SMALL = -5, /* workspace NULL or smaller than needed   */
+  PBA_ERR_OUT_OF_RANGE = -6,        /* validate mode: bad id, slot or length   */
+  PBA_ERR_OVERLAP = -7,             /* validate mode: duplicate slot / pair    */
+  PBA_ERR_HIP = -8                  /* a HIP runtime call failed               */
+} pba_status;
+
+typedef enum pba_dtype { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
+
+/*
+ * The K/V pool of one layer (one cache group): a fixed set of physical blocks
+ * of P token rows each.  Element (block b, kv head h, in-block token o, dim c):
+ *
+ *   K: k[b * k_stride_block + h * k_stride_head + o * head_dim + c]
+ *   V: v[b * v_stride_block + h * v_stride_head + c * block_size + o]
+ *
+ * i.e. inside one (block, head) tile K is [P][head_dim] (token major) and V is
+ * [head_dim][P] (dim major).  The default dense pool is
+ *   K [num_blocks, num_kv_heads, P, head_dim],  V [num_blocks, num_kv_heads, head_dim, P]
+ * with k_stride_head = v_stride_head = P * head_dim and
+ * k_stride_block = v_stride_block = num_kv_heads * P * head_dim.
+ * Strides are in elements; block ids are widened to int64 before they are
+ * multiplied by a stride ("Cache Concepts: Prefix Matching vs. Storage",
+ * int64 widening of page ids).  Axis order -> strides -> address follows
+ * "M5.3", section 0x03E.
+ *
+ * Requirements: block_size (P) in {16, 32, 64, 128, 256}; head_dim in
+ * {64, 128}; k, v and every tile 16-byte aligned; a (block, head) tile of
+ * P * head_dim elements must fit inside its stride.
+ */
+typedef struct pba_kv_pool {
+  void* k;
+  void* v;
+  int32_t dtype;         /* pba_dtype of every stored K/V scalar            */
+  int32_t num_blocks;    /* physical blocks in the pool                      */
+  int32_t block_size;    /* P: tokens per block (block_granularity)          */
+  int32_t num_kv_heads;  /* H_kv                                             */
+  int32_t head_dim;      /* d                                                */
+  int32_t reserved0;     /* must be 0                                        */
+  int64_t k_stride_block, k_stride_head;
+  int64_t v_stride_block, v_stride_head;
+} pba_kv_pool;
+
+/*
+ * pba_kv_append -- scatter new tokens' K/V rows into their physical slots.
+ *
+ * For each i < n_tokens with s = slot_mapping[i] >= 0: block = s div P,
+ * offset = s mod P, and for every kv head h the row k_new[i, h, :] becomes
+ * K(block, h, offset, :) and v_new[i, h, :] becomes V(block, h, offset, :).
+ * A negative slot skips the token.  ("M5.3", 0x03C-0x03D slot = block * P +
+ * offset; 0x04E the appended row o; "Cache Concepts", backend-owned write
+ * locations.)  The copy is bit exact: NaN payloads and signed zeros survive.
+ *
+ *   slot_mapping  device int64 [n_tokens]
+ *   k_new, v_new  device [n_tokens, num_kv_heads, head_dim], pool dtype,
+ *                 contiguous, 16-byte aligned
+ * Slots must be distinct within one call (validate mode: PBA_ERR_OVERLAP) and
+ * below num_blocks * P (validate mode: PBA_ERR_OUT_OF_RANGE).
+ */
+int pba_kv_append(const pba_kv_pool* pool, const int64_t* slot_mapping, int64_t n_tokens,
+                  const void* k_new, const void* v_new, void* stream);
+
+/*
+ * pba_block_copy -- copy-on-write before divergence: for each pair k the whole
+ * physical block src[k] (every row, every kv head, K and V) is copied bit for
+ * bit onto block dst[k].  ("M5.3", 0x04C a fused block-copy launch for COW,
+ * 0x05A-0x05D; "7. Memory Management and Local Model State", "Sharing and
+ * copy-on-write".)
+ *
+ *   src, dst  device int32 [n_pairs], ids in [0, num_blocks)
+ * No block may appear twice as a destination, nor as both a source and a
+ * destination, within one call (validate mode: PBA_ERR_OVERLAP).
+ */
+int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* dst,
+                   int64_t n_pairs, void* stream);
+
+/*
+ * pba_paged_decode -- one decode query row per request over its logical
+ * history ("M5.3", 0x0A the paged decode loop, 0x0BA partial states and their
+ * merge).
+ *
+ * For request r with T = seq_lens[r] and q-head i (kv head h = i / G,
+ * G = num_q_heads / num_kv_heads), over the visible tokens t < T read through
+ * block_tables[r, t div P] at offset t mod P:
+ *   s_t = scale * <q[r, i, :], K_t>
+ *   out[r, i, :] = sum_t exp(s_t - m) V_t / sum_t exp(s_t - m),  m = max_t s_t
+ *   lse[r, i]    = m + ln sum_t exp(s_t - m)
+ * Rows at positions >= T (tail padding, rows another request materialised in
+ * a shared block, stale rows of a recycled block) are never used, even if
+ * they hold NaN.
+ *
+ *   q             device [batch, num_q_heads, head_dim], pool dtype, contiguous
+ *   block_tables  device int32 [batch, max_blocks_per_seq], row major; entries
+ *                 at j >= ceil(T/P) are never read (any value)
+ *   seq_lens      device int32 [batch]; 1 <= T <= max_blocks_per_seq * P
+ *                 (validate mode: PBA_ERR_OUT_OF_RANGE)
+ *   scale         score scale, normally 1/sqrt(head_dim)
+ *   out           device float32 [batch, num_q_heads, head_dim]
+ *   lse           device float32 [batch, num_q_heads], or NULL
+ *   partition_tokens  0: the library splits each row into partitions of its
+ *                 choice; otherwise the partition length in tokens, a positive
+ *                 multiple of 256.  Partitions are reduced by the
+ *                 log-sum-exp merge; an empty partition is the identity.
+ *   workspace     device scratch of at least
+ *                 pba_paged_decode_workspace_bytes(...) bytes (NULL allowed
+ *                 when that is 0); contents need no initialisation and are
+ *                 undefined afterwards.
+ * Supported: num_q_heads a multiple of num_kv_heads with G <= 16.
+ * The result is deterministic for fixed arguments and does not depend on where
+ * the blocks lie physically.
+ */
+int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t batch, float scale, float* out, float* lse,
+                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Workspace bytes pba_paged_decode needs for these arguments (0 when one
+ * partition per row suffices); returns 0 for arguments it would reject. */
+size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_heads,
+                                        int32_t batch, int32_t max_blocks_per_seq,
+                                        int32_t partition_tokens);
+
+/* The partition length (tokens) and count pba_paged_decode would use; returns
+ * a pba_status.  Either output pointer may be NULL. */
+int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
+                          int32_t max_blocks_per_seq, int32_t partition_tokens,
+                          int32_t* partition_tokens_out, int32_t* num_partitions_out);
+
+/* Static description of a status code. */
+const char* pba_status_string(int status);
+
+/* Validate mode (process wide, default off).  When on, every call first copies
+ * its device-resident ids, slots and lengths to the host (synchronising the
+ * stream), checks them, and returns PBA_ERR_OUT_OF_RANGE / PBA_ERR_OVERLAP
+ * without launching anything if one is bad.  Returns the previous setting. */
+int pba_set_validate(int on);
+
+/* ABI version: major * 10000 + minor * 100 + patch. */
+int pba_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PBA_H_ */

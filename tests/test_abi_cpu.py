@@ -1,0 +1,157 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad host-visible arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "pba.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"\b(pba_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    import block_table_attention_amd as pba
+
+    lib = ctypes.CDLL(pba.lib_path())
+    declared = _header_functions()
+    assert declared == sorted(pba.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert pba.version() == 100
+
+
+def _desc(**kw):
+    import block_table_attention_amd as pba
+
+    d = dict(k=0x10000, v=0x20000, dtype=1, num_blocks=8, block_size=16, num_kv_heads=2,
+             head_dim=128, reserved0=0, k_stride_block=2 * 16 * 128, k_stride_head=16 * 128,
+             v_stride_block=2 * 16 * 128, v_stride_head=16 * 128)
+    d.update(kw)
+    return pba.PoolDesc(**d)
+
+
+def _lib():
+    import block_table_attention_amd as pba
+    return pba._lib
+
+
+NULL = None
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=7), -2),
+    (dict(block_size=48), -4),
+    (dict(block_size=8), -4),
+    (dict(block_size=512), -4),
+    (dict(head_dim=96), -4),
+    (dict(num_blocks=0), -3),
+    (dict(num_kv_heads=0), -3),
+    (dict(reserved0=1), -3),
+    (dict(k=0), -1),
+    (dict(k=0x10008), -4),
+    (dict(k_stride_head=1024), -3),
+    (dict(k_stride_head=16 * 128 + 4), -4),
+    (dict(v_stride_block=-16), -3),
+])
+def test_pool_descriptor_rejections(kw, status):
+    lib = _lib()
+    d = _desc(**kw)
+    assert lib.pba_kv_append(ctypes.byref(d), 0x30000, 4, 0x40000, 0x50000, NULL) == status
+    assert lib.pba_block_copy(ctypes.byref(d), 0x30000, 0x30010, 4, NULL) == status
+    assert lib.pba_paged_decode(ctypes.byref(d), 0x30000, 8, 0x40000, 4, 0x50000, 2,
+                                ctypes.c_float(0.1), 0x60000, NULL, 0, 0x70000, 1 << 30, NULL) == status
+
+
+def test_null_pool_and_pointers():
+    lib = _lib()
+    assert lib.pba_kv_append(NULL, 0x30000, 4, 0x40000, 0x50000, NULL) == -1
+    d = _desc()
+    assert lib.pba_kv_append(ctypes.byref(d), NULL, 4, 0x40000, 0x50000, NULL) == -1
+    assert lib.pba_block_copy(ctypes.byref(d), NULL, 0x30000, 1, NULL) == -1
+    assert lib.pba_paged_decode(ctypes.byref(d), NULL, 8, 0x40000, 4, 0x50000, 2,
+                                ctypes.c_float(0.1), 0x60000, NULL, 0, NULL, 0, NULL) == -1
+
+
+def test_empty_calls_are_noops():
+    lib = _lib()
+    d = _desc()
+    assert lib.pba_kv_append(ctypes.byref(d), NULL, 0, NULL, NULL, NULL) == 0
+    assert lib.pba_block_copy(ctypes.byref(d), NULL, NULL, 0, NULL) == 0
+    assert lib.pba_paged_decode(ctypes.byref(d), NULL, 8, NULL, 4, NULL, 0,
+                                ctypes.c_float(0.1), NULL, NULL, 0, NULL, 0, NULL) == 0
+    assert lib.pba_kv_append(ctypes.byref(d), NULL, -1, NULL, NULL, NULL) == -3
+
+
+def test_decode_shape_rejections():
+    lib = _lib()
+    d = _desc()
+    call = lambda hq, mb, pt, ws, wsb: lib.pba_paged_decode(
+        ctypes.byref(d), 0x30000, hq, 0x40000, mb, 0x50000, 2, ctypes.c_float(0.1), 0x60000,
+        NULL, pt, ws, wsb, NULL)
+    assert call(7, 4, 0, NULL, 0) == -3          # H_q not a multiple of H_kv
+    assert call(34, 4, 0, NULL, 0) == -4         # G = 17 > 16
+    assert call(8, 0, 0, NULL, 0) == -3          # no table width
+    assert call(8, 64, 100, NULL, 0) == -4       # partition not a multiple of 256
+    assert call(8, 64, -256, NULL, 0) == -3
+    # 64 blocks * 16 = 1024 tokens in 256-token partitions -> 4 partitions need a workspace.
+    assert call(8, 64, 256, NULL, 0) == -5
+    need = lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, 2, 64, 256)
+    assert call(8, 64, 256, 0x80000, need - 1) == -5
+    assert call(8, 64, 256, 0x80008, need) == -5  # misaligned workspace
+
+
+def test_workspace_and_plan():
+    import block_table_attention_amd as pba
+
+    lib = _lib()
+    d = _desc()
+    pt, npart = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, 2, 64, 256, ctypes.byref(pt), ctypes.byref(npart)) == 0
+    assert (pt.value, npart.value) == (256, 4)
+    rows = 2 * 8
+    ml = rows * 4 * 2 * 4
+    expect = (ml + 255) // 256 * 256 + rows * 4 * 128 * 4
+    assert lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, 2, 64, 256) == expect
+    # A single partition needs no workspace.
+    assert lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, 2, 64, 1024) == 0
+    # T = 2049 in 512-token partitions -> 5 (the pages' fixture), P = 16 -> 129 blocks.
+    assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, 1, 129, 512, ctypes.byref(pt), ctypes.byref(npart)) == 0
+    assert npart.value == 5
+    # Automatic plans: partitions are multiples of 256 and cover the table.
+    for B, mb in [(1, 1), (8, 256), (32, 129), (1, 4096), (128, 512)]:
+        assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, B, mb, 0, ctypes.byref(pt), ctypes.byref(npart)) == 0
+        assert pt.value % 256 == 0 and pt.value * npart.value >= mb * 16
+        assert pt.value * (npart.value - 1) < mb * 16
+    assert lib.pba_status_string(-5).decode().startswith("workspace")
+    assert pba.STATUS[-6] == "PBA_ERR_OUT_OF_RANGE"
+
+
+def test_validate_flag_roundtrip():
+    import block_table_attention_amd as pba
+
+    assert pba.set_validate(True) is False
+    assert pba.set_validate(False) is True
+
+
+def test_bench_fresh_layout_matches_oracle_allocator():
+    """bench.py builds tables itself (the caller's allocator for a fresh pool);
+    they must equal what the oracle allocator hands out for the same script."""
+    import numpy as np
+
+    import bench
+    import workloads as wl
+    from harness import execute
+
+    w = wl.long_context(3, 1000, num_blocks=64, block_size=64)
+    ex = execute(w)
+    prefill = [a[2] for a in w.actions if a[0] == "prefill"]
+    tables = bench.fresh_pool_layout(wl.fifo_order(w), [T + 1 for T in prefill], 64)
+    assert np.array_equal(tables, ex.tables)
+    slots = bench.slots_for(tables, 1, np.arange(5), 64)
+    assert slots.tolist() == [int(ex.tables[1, 0]) * 64 + i for i in range(5)]
