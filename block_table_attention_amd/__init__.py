@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_plan",
-           "paged_decode_workspace_bytes", "set_validate", "PBAError", "lib_path", "STATUS"]
+           "paged_decode_workspace_bytes", "decode_workspace", "set_validate", "PBAError", "lib_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -93,13 +93,27 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-@dataclass
+@dataclass(frozen=True)
 class KVPool:
     """One layer's K/V pool: K [NB, H_kv, P, d] (token-major tiles) and
     V [NB, H_kv, d, P] (dim-major tiles), both of the pool dtype."""
 
     k: torch.Tensor
     v: torch.Tensor
+
+    def __post_init__(self):
+        k, v = self.k, self.v
+        nb, h, p, d = k.shape
+        if v.shape != (nb, h, d, p) or v.dtype != k.dtype or v.device != k.device:
+            raise ValueError("V pool must be [num_blocks, H_kv, head_dim, block_size] of K's dtype")
+        if k.dtype not in _DTYPES:
+            raise TypeError(f"pool dtype {k.dtype} not supported")
+        if k.stride(2) != d or k.stride(3) != 1 or v.stride(2) != p or v.stride(3) != 1:
+            raise ValueError("pool tiles must be dense ([P][d] for K, [d][P] for V)")
+        desc = PoolDesc(k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], nb, p, h, d, 0,
+                        k.stride(0), k.stride(1), v.stride(0), v.stride(1))
+        object.__setattr__(self, "_desc", desc)
+        object.__setattr__(self, "_ref", ctypes.byref(desc))
 
     @classmethod
     def empty(cls, num_blocks: int, block_size: int, num_kv_heads: int, head_dim: int,
@@ -129,16 +143,7 @@ class KVPool:
         return self.k.dtype
 
     def desc(self) -> PoolDesc:
-        k, v = self.k, self.v
-        nb, h, p, d = k.shape
-        if v.shape != (nb, h, d, p) or v.dtype != k.dtype or v.device != k.device:
-            raise ValueError("V pool must be [num_blocks, H_kv, head_dim, block_size] of K's dtype")
-        if k.dtype not in _DTYPES:
-            raise TypeError(f"pool dtype {k.dtype} not supported")
-        if k.stride(2) != d or k.stride(3) != 1 or v.stride(2) != p or v.stride(3) != 1:
-            raise ValueError("pool tiles must be dense ([P][d] for K, [d][P] for V)")
-        return PoolDesc(k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], nb, p, h, d, 0,
-                        k.stride(0), k.stride(1), v.stride(0), v.stride(1))
+        return self._desc
 
 
 def _require(t: torch.Tensor, name: str, dtype, device, ndim: int):
@@ -160,9 +165,8 @@ def kv_append(pool: KVPool, slot_mapping: torch.Tensor, k_new: torch.Tensor,
     n = slot_mapping.shape[0]
     if k_new.shape != (n, pool.num_kv_heads, pool.head_dim) or v_new.shape != k_new.shape:
         raise ValueError("k_new/v_new must be [n_tokens, H_kv, head_dim]")
-    d = pool.desc()
-    _check("pba_kv_append", _lib.pba_kv_append(ctypes.byref(d), _ptr(slot_mapping), n,
-                                               _ptr(k_new), _ptr(v_new), _stream(stream)))
+    _check("pba_kv_append", _lib.pba_kv_append(pool._ref, slot_mapping.data_ptr(), n,
+                                               k_new.data_ptr(), v_new.data_ptr(), _stream(stream)))
 
 
 def block_copy(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
@@ -172,26 +176,43 @@ def block_copy(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=None) 
     _require(dst, "dst", torch.int32, dev, 1)
     if src.shape != dst.shape:
         raise ValueError("src and dst must have the same length")
-    d = pool.desc()
-    _check("pba_block_copy", _lib.pba_block_copy(ctypes.byref(d), _ptr(src), _ptr(dst),
+    _check("pba_block_copy", _lib.pba_block_copy(pool._ref, src.data_ptr(), dst.data_ptr(),
                                                  src.shape[0], _stream(stream)))
 
 
 def paged_decode_plan(pool: KVPool, num_q_heads: int, batch: int, max_blocks_per_seq: int,
                       partition_tokens: int = 0) -> Tuple[int, int]:
-    d = pool.desc()
     pt, npart = ctypes.c_int32(0), ctypes.c_int32(0)
     _check("pba_paged_decode_plan", _lib.pba_paged_decode_plan(
-        ctypes.byref(d), num_q_heads, batch, max_blocks_per_seq, partition_tokens,
+        pool._ref, num_q_heads, batch, max_blocks_per_seq, partition_tokens,
         ctypes.byref(pt), ctypes.byref(npart)))
     return pt.value, npart.value
 
 
 def paged_decode_workspace_bytes(pool: KVPool, num_q_heads: int, batch: int,
                                  max_blocks_per_seq: int, partition_tokens: int = 0) -> int:
-    d = pool.desc()
-    return int(_lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), num_q_heads, batch,
+    return int(_lib.pba_paged_decode_workspace_bytes(pool._ref, num_q_heads, batch,
                                                      max_blocks_per_seq, partition_tokens))
+
+
+_WORKSPACES = {}
+
+
+def decode_workspace(pool: KVPool, num_q_heads: int, batch: int, max_blocks_per_seq: int,
+                     partition_tokens: int = 0, stream=None) -> Optional[torch.Tensor]:
+    """A zero-initialised workspace for paged_decode, cached per (device,
+    stream, size).  The library leaves its counters at zero after every call,
+    so one workspace serves every call ordered on that stream."""
+    need = paged_decode_workspace_bytes(pool, num_q_heads, batch, max_blocks_per_seq,
+                                        partition_tokens)
+    if need == 0:
+        return None
+    key = (pool.k.device, _stream(stream), need)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        ws = torch.zeros(need, dtype=torch.uint8, device=pool.k.device)
+        _WORKSPACES[key] = ws
+    return ws
 
 
 def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
@@ -201,7 +222,9 @@ def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
                  workspace: Optional[torch.Tensor] = None, stream=None):
     """q [B, H_q, d] (pool dtype), block_tables int32 [B, max_blocks], seq_lens int32 [B].
 
-    Returns (out float32 [B, H_q, d], lse float32 [B, H_q] or None).
+    Returns (out float32 [B, H_q, d], lse float32 [B, H_q] or None).  A caller
+    supplied workspace must be zero-filled before its first use (the library
+    keeps it zeroed afterwards); without one, a cached zeroed workspace is used.
     """
     dev = pool.k.device
     _require(q, "q", pool.dtype, dev, 3)
@@ -215,20 +238,20 @@ def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
         scale = 1.0 / math.sqrt(D)
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
-    _require(out, "out", torch.float32, dev, 3)
+    else:
+        _require(out, "out", torch.float32, dev, 3)
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    if lse is not None:
+    elif lse is not None:
         _require(lse, "lse", torch.float32, dev, 2)
-    d = pool.desc()
-    need = _lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), Hq, B, max_blocks, partition_tokens)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None and B > 0:
+        workspace = decode_workspace(pool, Hq, B, max_blocks, partition_tokens, stream)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pba_paged_decode", _lib.pba_paged_decode(
-        ctypes.byref(d), _ptr(q), Hq, _ptr(block_tables), max_blocks, _ptr(seq_lens), B,
-        ctypes.c_float(scale), _ptr(out), _ptr(lse), partition_tokens, _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        pool._ref, q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks, seq_lens.data_ptr(), B,
+        ctypes.c_float(scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
     return out, lse
 
 

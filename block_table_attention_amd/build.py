@@ -22,6 +22,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["pba_api.hip", "kv_append.hip", "block_copy.hip", "paged_decode.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in arch VGPRs: the online-softmax rescale is VALU
+         # work on them, and AGPR homes cost two copies per chunk.
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

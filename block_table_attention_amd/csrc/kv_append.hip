@@ -2,73 +2,70 @@
 //
 // slot s -> (block s div P, offset s mod P) ("M5.3 - KV Memory Layout and
 // Exact Reuse", 0x03C-0x03D); the rows are bit copies, so NaN payloads and
-// signed zeros survive.  One 64-lane wave handles 64 consecutive tokens of one
-// kv head:
-//   K: the tile is token major, so a row is one contiguous run of d scalars;
-//      lanes walk (token, 16-byte chunk) pairs, which keeps both the reads of
-//      k_new and the writes into the pool coalesced.
-//   V: the tile is dim major ([d][P]), so a row becomes d scalars P apart.
-//      Lane i owns token i: it reads its row 16 bytes at a time and writes each
-//      scalar into its dim's run; for a prefill whose slots are consecutive the
-//      64 lanes of one store fill 64 neighbouring positions of that run.
+// signed zeros survive.  One thread moves one 16-byte piece of one token's row
+// of one kv head, so every load is independent of every store:
+//   K tasks (piece fastest): the K tile is token major, a row is one run of d
+//      scalars, and neighbouring lanes read and write neighbouring pieces;
+//   V tasks (token fastest): the V tile is dim major ([d][P]), a row becomes d
+//      scalars P apart; neighbouring lanes hold neighbouring tokens, so when a
+//      prefill's slots are consecutive, the lanes of one store fill
+//      neighbouring positions of the same dim run.
 #include "pba_internal.h"
 
 namespace pba {
 
 template <typename E>
-__global__ __launch_bounds__(64) void kv_append_kernel(AppendArgs a) {
-  const int lane = threadIdx.x;
-  const int h = blockIdx.y;
-  const int64_t i0 = (int64_t)blockIdx.x * 64;
+__global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
+  constexpr int EPC = 16 / sizeof(E);  // scalars per 16-byte piece
   const int D = a.head_dim;
+  const int H = a.kv_heads;
+  const int pieces = D / EPC;
+  const int64_t per_kind = a.n * H * pieces;
+  int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= 2 * per_kind) return;
   const int P = 1 << a.log2P;
-  const int chunks = D * (int)sizeof(E) / 16;  // 16-byte pieces per row
-  constexpr int EPC = 16 / sizeof(E);           // scalars per piece
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-  // K rows.
-  const char* knew = static_cast<const char*>(a.k_new);
-  char* kpool = static_cast<char*>(a.k);
-  for (int idx = lane; idx < 64 * chunks; idx += 64) {
-    const int64_t i = i0 + idx / chunks;
-    const int c = idx % chunks;
-    if (i >= a.n) break;
+  if (t < per_kind) {
+    const int c = (int)(t % pieces);
+    const int64_t rest = t / pieces;
+    const int h = (int)(rest % H);
+    const int64_t i = rest / H;
     const int64_t s = a.slots[i];
-    if (s < 0) continue;
-    const int64_t blk = s >> a.log2P;
-    const int64_t off = s & (P - 1);
-    const uint4 val = *reinterpret_cast<const uint4*>(
-        knew + ((i * a.kv_heads + h) * D) * (int64_t)sizeof(E) + c * 16);
-    *reinterpret_cast<uint4*>(kpool + (blk * a.k_sb + h * a.k_sh + off * D) * (int64_t)sizeof(E) +
-                              c * 16) = val;
-  }
-
-  // V rows, transposed into the dim-major tile.
-  const int64_t i = i0 + lane;
-  if (i >= a.n) return;
-  const int64_t s = a.slots[i];
-  if (s < 0) return;
-  const int64_t blk = s >> a.log2P;
-  const int64_t off = s & (P - 1);
-  const char* vrow = static_cast<const char*>(a.v_new) + ((i * a.kv_heads + h) * D) * (int64_t)sizeof(E);
-  E* vdst = static_cast<E*>(a.v) + blk * a.v_sb + h * a.v_sh + off;
-  for (int c = 0; c < chunks; ++c) {
+    if (s < 0) return;
+    const int64_t blk = s >> a.log2P, off = s & (P - 1);
+    const u32x4 val = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k_new) +
+                                                      (i * H + h) * D + c * EPC);
+    *reinterpret_cast<u32x4*>(static_cast<E*>(a.k) + blk * a.k_sb + h * a.k_sh + off * D +
+                              c * EPC) = val;
+  } else {
+    t -= per_kind;
+    const int64_t i = t % a.n;
+    const int64_t rest = t / a.n;
+    const int h = (int)(rest % H);
+    const int c = (int)(rest / H);
+    const int64_t s = a.slots[i];
+    if (s < 0) return;
+    const int64_t blk = s >> a.log2P, off = s & (P - 1);
     union {
-      uint4 u;
+      u32x4 u;
       E e[EPC];
     } piece;
-    piece.u = *reinterpret_cast<const uint4*>(vrow + c * 16);
+    piece.u = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v_new) + (i * H + h) * D +
+                                              c * EPC);
+    E* dst = static_cast<E*>(a.v) + blk * a.v_sb + h * a.v_sh + (int64_t)(c * EPC) * P + off;
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) vdst[(int64_t)(c * EPC + e) * P] = piece.e[e];
+    for (int e = 0; e < EPC; ++e) dst[(int64_t)e * P] = piece.e[e];
   }
 }
 
 hipError_t launch_kv_append(const AppendArgs& a, int esize, hipStream_t stream) {
-  const int64_t tiles = (a.n + 63) / 64;
-  dim3 grid((unsigned)tiles, (unsigned)a.kv_heads);
+  const int64_t tasks = 2 * a.n * a.kv_heads * (a.head_dim * esize / 16);
+  const dim3 grid((unsigned)((tasks + 255) / 256));
   if (esize == 2)
-    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(kv_append_kernel<uint16_t>, grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(64), 0, stream, a);
+    hipLaunchKernelGGL(kv_append_kernel<uint32_t>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

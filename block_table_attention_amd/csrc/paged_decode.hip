@@ -10,25 +10,32 @@
 //
 // Work decomposition on gfx950 (256 CUs, 64-lane waves):
 //   work-group = (partition, kv head h, request r), 4 waves.  Wave w walks
-//   the partition's 32-token chunks w, w+4, w+8, ...; the four waves merge
-//   their states through LDS at the end, and the work-group writes either the
-//   final row (single partition) or its partition state (merged by
-//   pba_decode_merge_kernel).
+//   the partition's chunks w, w+4, w+8, ...; the four waves merge their states
+//   through LDS.  A row with one partition is written directly.  Otherwise
+//   each work-group stores its partition state, and the last work-group of the
+//   (request, kv head) to finish -- found with one atomic counter per pair --
+//   merges the partitions in index order (deterministic) and resets the
+//   counter, so no second kernel is launched.
 //
 // bf16 path: the G query heads of kv head h are processed together, so the
-// scores of a chunk are the small dense product S^T[32 tokens x G] =
+// scores of a 32-token chunk are the small dense product S^T[32 x G] =
 // K[32 x d] Q^T[d x G] and the value update is O^T[d x G] += V^T[d x 32]
 // P^T[32 x G].  Both run on v_mfma_f32_16x16x32_bf16 (G padded to 16 columns):
-//   * K tile is token major, so each lane's A-operand fragment (one token row,
-//     8 consecutive dims) is one 16-byte load straight from HBM;
-//   * V tile is dim major ([d][P]), so each lane's A-operand fragment for the
-//     value product (one dim, 8 consecutive tokens) is again one 16-byte load;
+//   * the K tile is token major, so each lane's A-operand fragment (one token
+//     row, 8 consecutive dims) is one 16-byte load straight from HBM;
+//   * the V tile is dim major ([d][P]), so each lane's A-operand fragment for
+//     the value product (one dim, 8 consecutive tokens) is again one 16-byte
+//     load;
 //   * the token order inside a chunk is permuted so that the score fragment a
-//     lane receives (tokens 8g..8g+7 for its head) is exactly the B-operand
+//     lane receives (tokens 8g..8g+7 of its head) is exactly the B-operand
 //     fragment it needs for the value product: no cross-lane traffic.
 // No LDS staging: every loaded byte feeds exactly one MFMA of the wave that
-// loaded it.  Probabilities enter the value MFMA as a bf16 pair p = hi + lo
-// (hi = bf16(p), lo = bf16(p - hi)), which keeps ~16 significant bits.
+// loaded it.  Loads are software pipelined: the next chunk's K is requested as
+// soon as the score MFMAs have consumed the current K, and the next V as soon
+// as the value MFMAs have consumed the current V, so each wave keeps a chunk
+// of loads in flight while it computes.  Probabilities enter the value MFMA as
+// a bf16 pair p = hi + lo (hi = bf16(p), lo = bf16(p - hi)), ~16 significant
+// bits.  The running output is rescaled only when some head's maximum moved.
 //
 // Visibility: positions t >= T (tail padding, rows materialised in a shared
 // block by a longer request, stale rows) are removed by selects -- scores to
@@ -41,32 +48,31 @@ namespace pba {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWaves = kDecodeThreads / 64;
+// s_waitcnt encoding (gfx9 family): vmcnt(0), expcnt and lgkmcnt unconstrained.
+constexpr int kWaitVmcnt0 = 0x0F70;
 constexpr float kLn2 = 0.69314718055994530942f;
-
-__device__ __forceinline__ float wave_max_xor(float x, int mask) {
-  return fmaxf(x, __shfl_xor(x, mask, 64));
-}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Per-wave partial state, staged in LDS for the work-group merge.
+// Per-wave partial states, staged in LDS for the work-group merge.
 template <int D>
 struct WaveStates {
   float m[kWaves][16];
   float l[kWaves][16];
   float o[kWaves][D][17];  // [dim][head], padded against bank conflicts
+  int last;
 };
 
-// Merge the 4 wave states of one work-group and write the final row or the
-// partition state.  Every thread participates.
+// Merge the wave states of one work-group; write the row (one partition) or
+// the partition state; the last partition of a (request, kv head) merges all.
 template <int D>
-__device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, int h, int part) {
+__device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, int h, int part,
+                                 int T) {
   const int G = a.G;
-  for (int idx = threadIdx.x; idx < G * D; idx += kThreads) {
+  const int np_r = (T + a.part_tokens - 1) / a.part_tokens;
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
     const int n = idx / D;
     const int c = idx - n * D;
     float M = -INFINITY;
@@ -84,7 +90,7 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
       }
     }
     const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
-    if (a.n_parts == 1) {
+    if (np_r == 1) {
       a.out[row * D + c] = (L > 0.f) ? O / L : 0.f;
       if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     } else {
@@ -96,13 +102,93 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
       }
     }
   }
+  if (np_r == 1) return;
+
+  // Publish this partition, then count it.  The fences make every thread's
+  // partition-state stores visible at device scope before the count moves.
+  __threadfence();
+  __syncthreads();
+  int32_t* counter = a.counters + (int64_t)r * a.num_kv_heads + h;
+  if (threadIdx.x == 0) st.last = (atomicAdd(counter, 1) == np_r - 1);
+  __syncthreads();
+  if (!st.last) return;
+  __threadfence();  // acquire: observe every other partition's state
+
+  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+    const int n = idx / D;
+    const int c = idx - n * D;
+    const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
+    const float* ml = a.ws_ml + row * a.n_parts * 2;
+    const float* uu = a.ws_u + row * a.n_parts * D + c;
+    float M = -INFINITY;
+    for (int p = 0; p < np_r; ++p) M = fmaxf(M, ml[2 * p]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int p = 0; p < np_r; ++p) {
+        const float mp = ml[2 * p];
+        if (mp == -INFINITY) continue;
+        const float w = fast_exp2(mp - M);
+        L += w * ml[2 * p + 1];
+        O += w * uu[(int64_t)p * D];
+      }
+    }
+    a.out[row * D + c] = (L > 0.f) ? O / L : 0.f;
+    if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  }
+  if (threadIdx.x == 0) *counter = 0;  // ready for the next call on this workspace
 }
 
 // ---------------------------------------------------------------------------
 // bf16 K/V, MFMA path
 // ---------------------------------------------------------------------------
+// Block tables are read-only for the whole launch: reading them through the
+// constant address space lets wave-uniform lookups use scalar loads, which do
+// not queue behind the vector K/V loads.
+typedef const int32_t __attribute__((address_space(4))) table_t;
+
+// Physical block ids of the chunk starting at t0 (one when P >= 32, two when
+// P == 16; the second is never read past the request's last block).
+__device__ __forceinline__ void chunk_blocks(table_t* trow, int t0, int log2P, int nblk,
+                                             int64_t& pb0, int64_t& pb1) {
+  const int j0 = t0 >> log2P;
+  pb0 = trow[j0];
+  pb1 = pb0;
+  if (log2P == 4 && j0 + 1 < nblk) pb1 = trow[j0 + 1];
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
+__device__ __forceinline__ void load_k(u32x4 (&kf)[2][D / 32], const uint16_t* kpool,
+                                       const DecodeArgs& a, int h, int t0, int64_t pb0,
+                                       int64_t pb1, int n, int g) {
+  const int P = 1 << a.log2P;
+#pragma unroll
+  for (int at = 0; at < 2; ++at) {
+    // A-operand row n of tile `at` holds chunk token 8(n>>2) + 4at + (n&3).
+    const int tk = 8 * (n >> 2) + 4 * at + (n & 3);
+    const int64_t pb = (tk >= 16 && a.log2P == 4) ? pb1 : pb0;
+    const int off = (t0 + tk) & (P - 1);
+    const uint16_t* kp = kpool + pb * a.k_sb + (int64_t)h * a.k_sh + (int64_t)off * D + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) kf[at][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const uint16_t* vpool,
+                                       const DecodeArgs& a, int h, int t0, int64_t pb0,
+                                       int64_t pb1, int n, int g) {
+  const int P = 1 << a.log2P;
+  // A-operand row n of tile mt is dim 16mt + n; its k-slots are tokens 8g..8g+7.
+  const int tv = 8 * g;
+  const int64_t pb = (tv >= 16 && a.log2P == 4) ? pb1 : pb0;
+  const int off = (t0 + tv) & (P - 1);
+  const uint16_t* vp = vpool + pb * a.v_sb + (int64_t)h * a.v_sh + (int64_t)n * P + off;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KK = D / 32;  // k-steps of the score product
   constexpr int MT = D / 16;  // 16-dim tiles of the value product
@@ -118,11 +204,12 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
 
   const int T = a.seq_lens[r];
   const int p_begin = part * a.part_tokens;
-  if (p_begin >= T) return;  // empty partition: the merge never reads it
+  if (p_begin >= T) return;  // empty partition: never counted, never read
   const int p_end = min(T, p_begin + a.part_tokens);
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Wave-uniform (SGPR): chunk positions and block-table reads become scalar.
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;  // head column of this lane
   const int g = lane >> 4;  // k-group of this lane
   const int G = a.G;
@@ -143,10 +230,14 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
       qf[kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
+  // Drain the q loads here, so that inside the chunk loop the only vector
+  // loads in flight are K (older) and V (younger) and the loop waits for K
+  // alone before the score MFMAs.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
   const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
   const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
-  const int32_t* trow = a.tables + (int64_t)r * a.max_blocks;
+  table_t* trow = (table_t*)(a.tables + (int64_t)r * a.max_blocks);
 
   float m_run = -INFINITY;  // running max (log2 domain) of head n
   float l_run = 0.f;        // this lane's share of the running sum
@@ -154,37 +245,25 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int t0 = p_begin + wave * CH; t0 < p_end; t0 += kWaves * CH) {
-    // Physical blocks of the chunk: one when P >= 32, two when P == 16.
-    const int j0 = t0 >> log2P;
-    const int64_t pb0 = trow[j0];
-    int64_t pb1 = pb0;
-    if (log2P == 4 && j0 + 1 < nblk) pb1 = trow[j0 + 1];
+  int t0 = p_begin + wave * CH;
+  u32x4 kf[2][KK];
+  u32x4 vf[MT];
+  if (t0 < p_end) {
+    int64_t pb0, pb1;
+    chunk_blocks(trow, t0, log2P, nblk, pb0, pb1);
+    load_k<D>(kf, kpool, a, h, t0, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);  // K strictly before V
+    load_v<D>(vf, vpool, a, h, t0, pb0, pb1, n, g);
+  }
 
-    // K fragments.  Tile a, A-operand row m = lane & 15 holds chunk token
-    // 8(m>>2) + 4a + (m&3); dims 32kk + 8g .. +8.
-    u32x4 kf[2][KK];
-#pragma unroll
-    for (int at = 0; at < 2; ++at) {
-      const int tk = 8 * (n >> 2) + 4 * at + (n & 3);
-      const int64_t pb = (tk >= 16 && log2P == 4) ? pb1 : pb0;
-      const int off = (t0 + tk) & (P - 1);
-      const uint16_t* kp = kpool + pb * a.k_sb + (int64_t)h * a.k_sh + (int64_t)off * D + 8 * g;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) kf[at][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
-    }
-    // V^T fragments.  Tile mt, A-operand row = dim 16mt + (lane & 15), k-slots
-    // = chunk tokens 8g .. 8g+7.
-    u32x4 vf[MT];
-    {
-      const int tv = 8 * g;
-      const int64_t pb = (tv >= 16 && log2P == 4) ? pb1 : pb0;
-      const int off = (t0 + tv) & (P - 1);
-      const uint16_t* vp = vpool + pb * a.v_sb + (int64_t)h * a.v_sh + (int64_t)n * P + off;
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
-    }
+  for (; t0 < p_end; t0 += kWaves * CH) {
+    // Next chunk of this wave; on the last iteration the current chunk is
+    // requested again (in bounds, served from L2), which keeps the number of
+    // loads in flight the same on every iteration.
+    const int tn_raw = t0 + kWaves * CH;
+    const int tn = tn_raw < p_end ? tn_raw : t0;
+    int64_t nb0, nb1;
+    chunk_blocks(trow, tn, log2P, nblk, nb0, nb1);
 
     // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
     f32x4 s[2];
@@ -196,8 +275,9 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
         s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[at][kk]),
                                                          qf[kk], s[at], 0, 0, 0);
     }
+    load_k<D>(kf, kpool, a, h, tn, nb0, nb1, n, g);
 
-    const int tbase = t0 + 8 * g;  // token of slot j = 0 of this lane
+    const int tbase = t0 + 8 * g;  // token of k-slot j = 0 of this lane
     float x[8];
 #pragma unroll
     for (int at = 0; at < 2; ++at)
@@ -210,8 +290,8 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
     float cmax = x[0];
 #pragma unroll
     for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
-    cmax = wave_max_xor(cmax, 16);
-    cmax = wave_max_xor(cmax, 32);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
     const float m_new = fmaxf(m_run, cmax);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
@@ -224,8 +304,10 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
       psum += p[j];
     }
     l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+    }
 
     bf16x8 phi, plo;
 #pragma unroll
@@ -252,6 +334,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[mt], 0, 0, 0);
     }
+    load_v<D>(vf, vpool, a, h, tn, nb0, nb1, n, g);
   }
 
   // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n].
@@ -266,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) st.o[wave][16 * mt + 4 * g + i][n] = acc[mt][i];
   __syncthreads();
-  finish_workgroup<D>(a, st, r, h, part);
+  finish_workgroup<D>(a, st, r, h, part, T);
 }
 
 // ---------------------------------------------------------------------------
@@ -274,7 +357,7 @@ __global__ __launch_bounds__(kThreads) void decode_bf16_kernel(DecodeArgs a) {
 // for the value update)
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int CH = 64;
   constexpr int DPL = D / 64;  // dims per lane in the value update
@@ -302,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
   const int nblk = (T + P - 1) >> log2P;
 
   const float* qsrc = static_cast<const float*>(a.q) + ((int64_t)r * a.num_q_heads + (int64_t)h * G) * D;
-  for (int i = threadIdx.x; i < 16 * D; i += kThreads) {
+  for (int i = threadIdx.x; i < 16 * D; i += kDecodeThreads) {
     const int gg = i / D;
     sq[gg][i - gg * D] = (gg < G) ? qsrc[i] : 0.f;
   }
@@ -331,7 +414,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
     for (int gg = 0; gg < 16; ++gg) s[gg] = 0.f;
     for (int c = 0; c < D; c += 4) {
-      const f32x4v kv = *reinterpret_cast<const f32x4v*>(krow + c);
+      const f32x4 kv = *reinterpret_cast<const f32x4*>(krow + c);
 #pragma unroll
       for (int gg = 0; gg < 16; ++gg)
         if (gg < G) s[gg] += sq[gg][c] * kv[0] + sq[gg][c + 1] * kv[1] + sq[gg][c + 2] * kv[2] +
@@ -344,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
       const float x = valid ? s[gg] * a.scale_log2 : -INFINITY;
       float cm = x;
 #pragma unroll
-      for (int msk = 32; msk >= 1; msk >>= 1) cm = wave_max_xor(cm, msk);
+      for (int msk = 32; msk >= 1; msk >>= 1) cm = fmaxf(cm, __shfl_xor(cm, msk, 64));
       const float m_new = fmaxf(m_run[gg], cm);
       alpha[gg] = fast_exp2(m_run[gg] - m_new);
       m_run[gg] = m_new;
@@ -370,8 +453,8 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         const int c = lane + 64 * e;
-        f32x4v vv = *reinterpret_cast<const f32x4v*>(vpool + pbv * a.v_sb + (int64_t)h * a.v_sh +
-                                                     (int64_t)c * P + off);
+        f32x4 vv = *reinterpret_cast<const f32x4*>(vpool + pbv * a.v_sb + (int64_t)h * a.v_sh +
+                                                   (int64_t)c * P + off);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (tt + q >= T) vv[q] = 0.f;
@@ -400,42 +483,36 @@ __global__ __launch_bounds__(kThreads) void decode_f32_kernel(DecodeArgs a) {
     for (int e = 0; e < DPL; ++e) st.o[wave][lane + 64 * e][gg] = u[gg][e];
   }
   __syncthreads();
-  finish_workgroup<D>(a, st, r, h, part);
+  finish_workgroup<D>(a, st, r, h, part, T);
 }
 
-// ---------------------------------------------------------------------------
-// Partition merge: O = sum_p w_p u_p / sum_p w_p l_p, w_p = 2^(m_p - M).
-// One work-group of D threads per (request, q head); partitions in index
-// order, so the result is deterministic.
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(D) void decode_merge_kernel(DecodeArgs a) {
-  const int64_t row = blockIdx.x;  // r * H_q + head
-  const int r = (int)(row / a.num_q_heads);
-  const int c = threadIdx.x;
-  const int T = a.seq_lens[r];
-  const int np = min(a.n_parts, (T + a.part_tokens - 1) / a.part_tokens);
-  const float* ml = a.ws_ml + row * a.n_parts * 2;
-  const float* uu = a.ws_u + row * a.n_parts * D;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-  float L = 0.f, O = 0.f;
-  if (M != -INFINITY) {
-    for (int p = 0; p < np; ++p) {
-      const float mp = ml[2 * p];
-      if (mp == -INFINITY) continue;
-      const float w = fast_exp2(mp - M);
-      L += w * ml[2 * p + 1];
-      O += w * uu[(int64_t)p * D + c];
-    }
+template <typename K>
+static int occupancy(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kDecodeThreads, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
   }
-  a.out[row * D + c] = (L > 0.f) ? O / L : 0.f;
-  if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  return n;
+}
+
+int decode_workgroups_per_cu(int dtype, int head_dim) {
+  static int cache[2][2] = {{-1, -1}, {-1, -1}};
+  const int i = dtype == PBA_BF16 ? 1 : 0, j = head_dim == 128 ? 1 : 0;
+  if (cache[i][j] < 0) {
+    int n;
+    if (dtype == PBA_BF16)
+      n = head_dim == 128 ? occupancy(decode_bf16_kernel<128>) : occupancy(decode_bf16_kernel<64>);
+    else
+      n = head_dim == 128 ? occupancy(decode_f32_kernel<128>) : occupancy(decode_f32_kernel<64>);
+    cache[i][j] = n;
+  }
+  return cache[i][j];
 }
 
 hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
   const int64_t wgs = (int64_t)a.n_parts * a.num_kv_heads * a.batch;
-  const dim3 grid((unsigned)wgs), block(kThreads);
+  const dim3 grid((unsigned)wgs), block(kDecodeThreads);
   if (dtype == PBA_BF16) {
     if (head_dim == 128)
       hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, block, 0, stream, a);
@@ -447,13 +524,6 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     else
       hipLaunchKernelGGL(decode_f32_kernel<64>, grid, block, 0, stream, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_parts == 1) return e;
-  const dim3 mgrid((unsigned)((int64_t)a.batch * a.num_q_heads));
-  if (head_dim == 128)
-    hipLaunchKernelGGL(decode_merge_kernel<128>, mgrid, dim3(128), 0, stream, a);
-  else
-    hipLaunchKernelGGL(decode_merge_kernel<64>, mgrid, dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

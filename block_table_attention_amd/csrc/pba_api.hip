@@ -74,14 +74,18 @@ int device_cu_count() {
   return cache[dev];
 }
 
-// Split planner.  Partitions are multiples of 256 tokens (so every block size
-// P <= 256 divides them and 32/64-token chunks never straddle one).  Without
-// an explicit length the planner aims at ~4 work-groups per CU over the
+// Split planner.  Partition lengths are multiples of the dtype's token granule
+// (128 tokens for bf16 = 4 waves x 32-token chunks, 256 for fp32), so chunks
+// never straddle a partition; an explicit length must be a multiple of 256.
+// Without one, the planner cuts every row into the largest number of equal
+// partitions for which all (request, kv head, partition) work-groups fit on
+// the GPU at once (CUs x resident work-groups per CU), measured over the
 // longest row the table can describe (the host does not see seq_lens).
 int plan_partitions(const pba_kv_pool* pool, int32_t batch, int32_t max_blocks, int32_t requested,
                     int32_t* part_tokens, int32_t* n_parts) {
   const int64_t max_T = (int64_t)max_blocks * pool->block_size;
   if (max_T <= 0) return PBA_ERR_BAD_SHAPE;
+  const int64_t granule = pba::decode_granule(pool->dtype);
   int64_t pt;
   if (requested > 0) {
     if (requested % kPartGranule) return PBA_ERR_UNSUPPORTED;
@@ -89,14 +93,16 @@ int plan_partitions(const pba_kv_pool* pool, int32_t batch, int32_t max_blocks, 
   } else if (requested < 0) {
     return PBA_ERR_BAD_SHAPE;
   } else {
+    int occ = pba::decode_workgroups_per_cu(pool->dtype, pool->head_dim);
+    if (occ <= 0) occ = 2;
+    const int64_t slots = (int64_t)occ * device_cu_count();
     const int64_t units = (int64_t)batch * pool->num_kv_heads;
-    const int64_t target = 4LL * device_cu_count();
-    const int64_t max_splits = (max_T + kPartGranule - 1) / kPartGranule;
-    int64_t splits = (target + units - 1) / units;
+    const int64_t max_splits = (max_T + granule - 1) / granule;
+    int64_t splits = slots / units;
     if (splits < 1) splits = 1;
     if (splits > max_splits) splits = max_splits;
     const int64_t per = (max_T + splits - 1) / splits;
-    pt = (per + kPartGranule - 1) / kPartGranule * kPartGranule;
+    pt = (per + granule - 1) / granule * granule;
   }
   const int64_t np = (max_T + pt - 1) / pt;
   if (pt > INT32_MAX || np > INT32_MAX) return PBA_ERR_UNSUPPORTED;
@@ -105,15 +111,23 @@ int plan_partitions(const pba_kv_pool* pool, int32_t batch, int32_t max_blocks, 
   return PBA_OK;
 }
 
-size_t workspace_layout(int64_t rows, int32_t n_parts, int head_dim, size_t* u_offset) {
-  if (n_parts <= 1) {
-    *u_offset = 0;
-    return 0;
-  }
-  const size_t ml = (size_t)rows * n_parts * 2 * sizeof(float);
-  const size_t off = (ml + 255) / 256 * 256;
-  *u_offset = off;
-  return off + (size_t)rows * n_parts * head_dim * sizeof(float);
+// Workspace: [counters int32 B*H_kv | pad to 256 B][m, l: B*H_q*n_parts*2 f32
+// | pad][u: B*H_q*n_parts*d f32].  Only rows with more than one partition use
+// it.  The counters must be zero before the first call; every call leaves them
+// zero again.
+struct WsLayout {
+  size_t ml_off, u_off, bytes;
+};
+
+WsLayout workspace_layout(int32_t batch, int32_t kv_heads, int64_t rows, int32_t n_parts,
+                          int head_dim) {
+  WsLayout w{0, 0, 0};
+  if (n_parts <= 1) return w;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  w.ml_off = up((size_t)batch * kv_heads * sizeof(int32_t));
+  w.u_off = w.ml_off + up((size_t)rows * n_parts * 2 * sizeof(float));
+  w.bytes = w.u_off + (size_t)rows * n_parts * head_dim * sizeof(float);
+  return w;
 }
 
 template <typename T>
@@ -157,7 +171,8 @@ int pba_kv_append(const pba_kv_pool* pool, const int64_t* slot_mapping, int64_t 
   if (n_tokens == 0) return PBA_OK;
   if (!slot_mapping || !k_new || !v_new) return PBA_ERR_NULL_ARG;
   if (!aligned16(k_new) || !aligned16(v_new)) return PBA_ERR_UNSUPPORTED;
-  if ((n_tokens + 63) / 64 > INT32_MAX || pool->num_kv_heads > 65535) return PBA_ERR_UNSUPPORTED;
+  const int64_t tasks = 2 * n_tokens * pool->num_kv_heads * (pool->head_dim * esize_of(pool->dtype) / 16);
+  if ((tasks + 255) / 256 > INT32_MAX) return PBA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g_validate.load()) {
     std::vector<int64_t> slots;
@@ -244,8 +259,8 @@ size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_h
   if (pba_paged_decode_plan(pool, num_q_heads, batch, max_blocks_per_seq, partition_tokens, &pt,
                             &np))
     return 0;
-  size_t off = 0;
-  return workspace_layout((int64_t)batch * num_q_heads, np, pool->head_dim, &off);
+  return workspace_layout(batch, pool->num_kv_heads, (int64_t)batch * num_q_heads, np,
+                          pool->head_dim).bytes;
 }
 
 int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
@@ -268,8 +283,8 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   const int64_t rows = (int64_t)batch * num_q_heads;
   const int64_t wgs = (int64_t)np * pool->num_kv_heads * batch;
   if (wgs > INT32_MAX || rows > INT32_MAX) return PBA_ERR_UNSUPPORTED;
-  size_t u_off = 0;
-  const size_t need = workspace_layout(rows, np, pool->head_dim, &u_off);
+  const WsLayout ws = workspace_layout(batch, pool->num_kv_heads, rows, np, pool->head_dim);
+  const size_t need = ws.bytes;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PBA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -300,8 +315,10 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   a.seq_lens = seq_lens;
   a.out = out;
   a.lse = lse;
-  a.ws_ml = need ? static_cast<float*>(workspace) : nullptr;
-  a.ws_u = need ? reinterpret_cast<float*>(static_cast<char*>(workspace) + u_off) : nullptr;
+  char* wsb = static_cast<char*>(workspace);
+  a.counters = need ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+  a.ws_ml = need ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
+  a.ws_u = need ? reinterpret_cast<float*>(wsb + ws.u_off) : nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.log2P = log2_exact(pool->block_size);
   a.G = G;

@@ -44,6 +44,7 @@ struct DecodeArgs {
   float* lse;
   float* ws_ml;  // [B][H_q][n_parts][2]: running max (log2 domain), sum
   float* ws_u;   // [B][H_q][n_parts][D]: unnormalised output
+  int32_t* counters;  // [B][H_kv]: partitions finished; zero between calls
   int32_t max_blocks;
   int32_t log2P;
   int32_t G;
@@ -58,5 +59,10 @@ struct DecodeArgs {
 hipError_t launch_kv_append(const AppendArgs& a, int esize, hipStream_t stream);
 hipError_t launch_block_copy(const CopyArgs& a, int64_t n_pairs, int kv_heads, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// Resident work-groups per CU of the decode kernel for (dtype, head_dim); 0 if unknown.
+int decode_workgroups_per_cu(int dtype, int head_dim);
+// Work-group size and the token granule partitions are cut at, per dtype.
+constexpr int kDecodeThreads = 256;
+inline int decode_granule(int dtype) { return dtype == PBA_BF16 ? 128 : 256; }
 
 }  // namespace pba

@@ -142,13 +142,19 @@ int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* d
  *   out           device float32 [batch, num_q_heads, head_dim]
  *   lse           device float32 [batch, num_q_heads], or NULL
  *   partition_tokens  0: the library splits each row into partitions of its
- *                 choice; otherwise the partition length in tokens, a positive
- *                 multiple of 256.  Partitions are reduced by the
- *                 log-sum-exp merge; an empty partition is the identity.
+ *                 choice (sized so that all work-groups are resident at once);
+ *                 otherwise the partition length in tokens, a positive
+ *                 multiple of 256.  Partitions are reduced by the log-sum-exp
+ *                 merge; an empty partition is the identity.
  *   workspace     device scratch of at least
- *                 pba_paged_decode_workspace_bytes(...) bytes (NULL allowed
- *                 when that is 0); contents need no initialisation and are
- *                 undefined afterwards.
+ *                 pba_paged_decode_workspace_bytes(...) bytes, 16-byte aligned
+ *                 (NULL allowed when that is 0).  Its first 4 * batch *
+ *                 num_kv_heads bytes are completion counters that must be zero
+ *                 before the first call that uses the workspace; every call
+ *                 leaves them zero again, so a workspace zero-filled once
+ *                 serves any number of calls ordered on one stream.  Calls
+ *                 that overlap in time must not share a workspace.  The rest
+ *                 needs no initialisation.
  * Supported: num_q_heads a multiple of num_kv_heads with G <= 16.
  * The result is deterministic for fixed arguments and does not depend on where
  * the blocks lie physically.

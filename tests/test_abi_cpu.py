@@ -115,8 +115,10 @@ def test_workspace_and_plan():
     assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, 2, 64, 256, ctypes.byref(pt), ctypes.byref(npart)) == 0
     assert (pt.value, npart.value) == (256, 4)
     rows = 2 * 8
-    ml = rows * 4 * 2 * 4
-    expect = (ml + 255) // 256 * 256 + rows * 4 * 128 * 4
+    up = lambda x: (x + 255) // 256 * 256
+    counters = 2 * 2 * 4                     # B * H_kv int32
+    ml = rows * 4 * 2 * 4                    # rows * n_parts * (m, l)
+    expect = up(counters) + up(ml) + rows * 4 * 128 * 4
     assert lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, 2, 64, 256) == expect
     # A single partition needs no workspace.
     assert lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, 2, 64, 1024) == 0
@@ -126,7 +128,7 @@ def test_workspace_and_plan():
     # Automatic plans: partitions are multiples of 256 and cover the table.
     for B, mb in [(1, 1), (8, 256), (32, 129), (1, 4096), (128, 512)]:
         assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, B, mb, 0, ctypes.byref(pt), ctypes.byref(npart)) == 0
-        assert pt.value % 256 == 0 and pt.value * npart.value >= mb * 16
+        assert pt.value % 128 == 0 and pt.value * npart.value >= mb * 16
         assert pt.value * (npart.value - 1) < mb * 16
     assert lib.pba_status_string(-5).decode().startswith("workspace")
     assert pba.STATUS[-6] == "PBA_ERR_OUT_OF_RANGE"

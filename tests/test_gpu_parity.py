@@ -241,3 +241,34 @@ def test_block_copy_bit_exact_nan_payloads(pba, gpu):
     pba.block_copy(pool, torch.from_numpy(src).to(gpu), torch.from_numpy(dst).to(gpu))
     torch.cuda.synchronize()
     assert np.array_equal(to_bits(pool.k), opool.k) and np.array_equal(to_bits(pool.v), opool.v)
+
+
+def test_workspace_counters_reset_between_calls(pba, gpu):
+    """One zeroed workspace, calls with different partition counts per row:
+    every call must leave the completion counters at zero for the next."""
+    base = small_workload("bf16", 64, 128, 2, 8, [3000, 700, 2048, 1], 20261202 + 4000)
+    say("workspace reuse", base.shape)
+    ex = execute(base)
+    k_rows, v_rows = wl.kv_rows(base, ex.n_writes)
+    opool = oracle_pool(ex, k_rows, v_rows)
+    pool = gpu_pool(ex, gpu)
+    gpu_replay(ex, pool, to_device(k_rows, "bf16", gpu), to_device(v_rows, "bf16", gpu))
+    qb = wl.q_bits(base)
+    q = to_device(qb, "bf16", gpu)
+    tables = torch.from_numpy(ex.tables).to(gpu)
+    B, Hq = qb.shape[0], qb.shape[1]
+    ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, ex.tables.shape[1], 256)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=gpu)
+    scale = 1 / math.sqrt(128)
+    outs = []
+    for lens in ([3000, 700, 2048, 1], [257, 700, 1, 1024], [3000, 700, 2048, 1], [1, 1, 1, 1],
+                 [3000, 700, 2048, 1]):
+        ld = torch.tensor(lens, dtype=torch.int32, device=gpu)
+        out, lse = pba.paged_decode(pool, q, tables, ld, scale, partition_tokens=256, workspace=ws)
+        torch.cuda.synchronize()
+        ref, _ = att.paged_decode(opool, qb, list(ex.tables), lens, scale)
+        assert np.max(np.abs(out.cpu().numpy() - ref)) <= TOL, lens
+        outs.append(out.clone())
+    assert torch.equal(outs[0], outs[2]) and torch.equal(outs[0], outs[4])
+    n_counters = B * base.shape.num_kv_heads
+    assert torch.count_nonzero(ws[:4 * n_counters]).item() == 0
