@@ -23,7 +23,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libpba.so")
+    """The in-tree library, or the file named by PBA_LIB (a build kept elsewhere)."""
+    return os.environ.get("PBA_LIB") or os.path.join(_HERE, "libpba.so")
 
 
 if not os.path.exists(lib_path()):

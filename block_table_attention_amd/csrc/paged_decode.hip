@@ -61,9 +61,94 @@ template <int D>
 struct WaveStates {
   float m[kWaves][16];
   float l[kWaves][16];
-  float o[kWaves][D][17];  // [dim][head], padded against bank conflicts
+  union {
+    float o[kWaves][D][17];   // [dim][head], padded against bank conflicts
+    float w[16 * 2 * 16];     // (m, l) of a tile of partitions, final merge
+  };
   int last;
 };
+
+// Partition states cross work-groups (and XCDs, whose L2s are not coherent
+// with each other) through memory: they are written and read with
+// system-coherent (write-through / uncached) accesses, so no device-wide
+// cache write-back or invalidate is needed.  The writer waits for its stores
+// to complete (vmcnt(0)) before it increments the completion counter; the
+// work-group that observes the final count reads the states from memory.
+__device__ __forceinline__ void st_state(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__device__ __forceinline__ float ld_state(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Final merge of the partition states of one (request, kv head):
+//   O = sum_p w_p u_p / L,  w_p = 2^(m_p - M),  M = max_p m_p,  L = sum_p w_p l_p,
+// partitions in index order.  Every load is issued before any result is
+// used: the (m, l) of all partitions go to LDS, each thread keeps the u of its
+// output elements in registers, so the merge costs one memory round trip.
+// Rows with more than kMergeFast partitions take the same path in tiles.
+constexpr int kMergeFast = 16;
+
+template <int D>
+__device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r, float* s_ml) {
+  constexpr int KO = 16 * D / kDecodeThreads;  // output elements per thread (G <= 16)
+  const int G = a.G;
+  const int64_t row0 = (int64_t)r * a.num_q_heads + (int64_t)h * G;
+  float O[KO], L[KO], M[KO];
+#pragma unroll
+  for (int k = 0; k < KO; ++k) O[k] = 0.f, L[k] = 0.f, M[k] = -INFINITY;
+  for (int p0 = 0; p0 < np_r; p0 += kMergeFast) {
+    const int pn = min(kMergeFast, np_r - p0);
+    // (m, l) of this tile of partitions, every head, into LDS.
+    for (int i = threadIdx.x; i < G * pn * 2; i += kDecodeThreads) {
+      const int n = i / (2 * pn), rem = i - n * 2 * pn;
+      s_ml[n * 2 * kMergeFast + rem] = ld_state(a.ws_ml + ((row0 + n) * a.n_parts + p0) * 2 + rem);
+    }
+    float u[KO][kMergeFast];
+#pragma unroll
+    for (int k = 0; k < KO; ++k) {
+      const int idx = threadIdx.x + k * kDecodeThreads;
+      const int n = idx / D, c = idx - (idx / D) * D;
+      const float* uu = a.ws_u + ((row0 + n) * a.n_parts + p0) * D + c;
+#pragma unroll
+      for (int p = 0; p < kMergeFast; ++p) u[k][p] = (n < G && p < pn) ? ld_state(uu + (int64_t)p * D) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < KO; ++k) {
+      const int idx = threadIdx.x + k * kDecodeThreads;
+      const int n = idx / D;
+      if (n >= G) continue;
+      const float* ml = s_ml + n * 2 * kMergeFast;
+      float Mt = M[k];
+      for (int p = 0; p < pn; ++p) Mt = fmaxf(Mt, ml[2 * p]);
+      if (Mt == -INFINITY) continue;
+      const float sc = (M[k] == -INFINITY) ? 0.f : fast_exp2(M[k] - Mt);
+      float Lt = L[k] * sc, Ot = O[k] * sc;
+#pragma unroll
+      for (int p = 0; p < kMergeFast; ++p) {
+        if (p >= pn) break;
+        const float mp = ml[2 * p];
+        if (mp == -INFINITY) continue;
+        const float w = fast_exp2(mp - Mt);
+        Lt += w * ml[2 * p + 1];
+        Ot += w * u[k][p];
+      }
+      M[k] = Mt, L[k] = Lt, O[k] = Ot;
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < KO; ++k) {
+    const int idx = threadIdx.x + k * kDecodeThreads;
+    const int n = idx / D, c = idx - (idx / D) * D;
+    if (n >= G) continue;
+    const int64_t row = row0 + n;
+    a.out[row * D + c] = (L[k] > 0.f) ? O[k] / L[k] : 0.f;
+    if (a.lse && c == 0) a.lse[row] = (L[k] > 0.f) ? (M[k] + __log2f(L[k])) * kLn2 : -INFINITY;
+  }
+}
 
 // Merge the wave states of one work-group; write the row (one partition) or
 // the partition state; the last partition of a (request, kv head) merges all.
@@ -95,46 +180,23 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
       if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = row * a.n_parts + part;
-      a.ws_u[prow * D + c] = O;
+      st_state(a.ws_u + prow * D + c, O);
       if (c == 0) {
-        a.ws_ml[prow * 2 + 0] = M;
-        a.ws_ml[prow * 2 + 1] = L;
+        st_state(a.ws_ml + prow * 2 + 0, M);
+        st_state(a.ws_ml + prow * 2 + 1, L);
       }
     }
   }
   if (np_r == 1) return;
-
-  // Publish this partition, then count it.  The fences make every thread's
-  // partition-state stores visible at device scope before the count moves.
-  __threadfence();
-  __syncthreads();
   int32_t* counter = a.counters + (int64_t)r * a.num_kv_heads + h;
-  if (threadIdx.x == 0) st.last = (atomicAdd(counter, 1) == np_r - 1);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's state stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0)
+    st.last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               np_r - 1);
   __syncthreads();
   if (!st.last) return;
-  __threadfence();  // acquire: observe every other partition's state
-
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-    const int n = idx / D;
-    const int c = idx - n * D;
-    const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
-    const float* ml = a.ws_ml + row * a.n_parts * 2;
-    const float* uu = a.ws_u + row * a.n_parts * D + c;
-    float M = -INFINITY;
-    for (int p = 0; p < np_r; ++p) M = fmaxf(M, ml[2 * p]);
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int p = 0; p < np_r; ++p) {
-        const float mp = ml[2 * p];
-        if (mp == -INFINITY) continue;
-        const float w = fast_exp2(mp - M);
-        L += w * ml[2 * p + 1];
-        O += w * uu[(int64_t)p * D];
-      }
-    }
-    a.out[row * D + c] = (L > 0.f) ? O / L : 0.f;
-    if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
-  }
+  merge_partitions<D>(a, r, h, np_r, st.w);
   if (threadIdx.x == 0) *counter = 0;  // ready for the next call on this workspace
 }
 
@@ -147,13 +209,16 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
 typedef const int32_t __attribute__((address_space(4))) table_t;
 
 // Physical block ids of the chunk starting at t0 (one when P >= 32, two when
-// P == 16; the second is never read past the request's last block).
-__device__ __forceinline__ void chunk_blocks(table_t* trow, int t0, int log2P, int nblk,
+// P == 16).  Ids are clamped into the pool so that a lookup made before the
+// request length is known (or past it) only ever addresses pool memory; rows
+// past the length are masked out of the result regardless.
+__device__ __forceinline__ void chunk_blocks(const DecodeArgs& a, table_t* trow, int t0,
                                              int64_t& pb0, int64_t& pb1) {
-  const int j0 = t0 >> log2P;
-  pb0 = trow[j0];
+  const int j0 = min(t0 >> a.log2P, a.max_blocks - 1);
+  const int last = a.num_blocks - 1;
+  pb0 = min(max(trow[j0], 0), last);
   pb1 = pb0;
-  if (log2P == 4 && j0 + 1 < nblk) pb1 = trow[j0 + 1];
+  if (a.log2P == 4) pb1 = min(max(trow[min(j0 + 1, a.max_blocks - 1)], 0), last);
 }
 
 template <int D>
@@ -184,7 +249,8 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const uint16_t* vpoo
   const int off = (t0 + tv) & (P - 1);
   const uint16_t* vp = vpool + pb * a.v_sb + (int64_t)h * a.v_sh + (int64_t)n * P + off;
 #pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
+  for (int mt = 0; mt < D / 16; ++mt)
+    vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
 }
 
 template <int D>
@@ -201,26 +267,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
   const int rest = wg / a.n_parts;
   const int h = rest % a.num_kv_heads;
   const int r = rest / a.num_kv_heads;
-
-  const int T = a.seq_lens[r];
-  const int p_begin = part * a.part_tokens;
-  if (p_begin >= T) return;  // empty partition: never counted, never read
-  const int p_end = min(T, p_begin + a.part_tokens);
-
   const int lane = threadIdx.x & 63;
   // Wave-uniform (SGPR): chunk positions and block-table reads become scalar.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;  // head column of this lane
   const int g = lane >> 4;  // k-group of this lane
   const int G = a.G;
-  const int log2P = a.log2P;
-  const int P = 1 << log2P;
-  const int nblk = (T + P - 1) >> log2P;
+  const int p_begin = part * a.part_tokens;
+  const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
+  const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
+  table_t* trow = (table_t*)(a.tables + (int64_t)r * a.max_blocks);
 
-  // Q^T fragments (B operand of the score product): lane holds dims
-  // 32kk + 8g .. +8 of query head n; padding heads are zero.
+  // Start-up, without waiting for the request length: the length, this wave's
+  // first block-table entry, q, and the first chunk's K and V are all
+  // requested at once.  Nothing is read out of bounds whatever the length
+  // turns out to be (see chunk_blocks); the loads are simply unused when the
+  // wave has no chunk.  Issue order q, K, V keeps the in-loop waits exact.
+  const int T = a.seq_lens[r];
+  int t0 = p_begin + wave * CH;
+  int64_t pb0, pb1;
+  chunk_blocks(a, trow, t0, pb0, pb1);
   bf16x8 qf[KK];
   {
+    // Q^T fragments (B operand of the score product): lane holds dims
+    // 32kk + 8g .. +8 of query head n; padding heads are zero.
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            ((int64_t)r * a.num_q_heads + (int64_t)h * G + (n < G ? n : 0)) * D;
 #pragma unroll
@@ -230,14 +300,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
       qf[kk] = __builtin_bit_cast(bf16x8, raw);
     }
   }
-  // Drain the q loads here, so that inside the chunk loop the only vector
-  // loads in flight are K (older) and V (younger) and the loop waits for K
-  // alone before the score MFMAs.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __builtin_amdgcn_sched_barrier(0);
+  u32x4 kf[2][KK];
+  u32x4 vf[MT];
+  load_k<D>(kf, kpool, a, h, t0, pb0, pb1, n, g);
+  __builtin_amdgcn_sched_barrier(0);
+  load_v<D>(vf, vpool, a, h, t0, pb0, pb1, n, g);
+  __builtin_amdgcn_sched_barrier(0);
 
-  const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
-  table_t* trow = (table_t*)(a.tables + (int64_t)r * a.max_blocks);
+  if (p_begin >= T) return;  // empty partition: never counted, never read
+  const int p_end = min(T, p_begin + a.part_tokens);
+  // This wave's chunks: p_begin + wave*CH + k*kWaves*CH for k < n_w.
+  const int span = p_end - p_begin - wave * CH;
+  const int n_w = span > 0 ? (span + kWaves * CH - 1) / (kWaves * CH) : 0;
 
   float m_run = -INFINITY;  // running max (log2 domain) of head n
   float l_run = 0.f;        // this lane's share of the running sum
@@ -245,25 +320,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  int t0 = p_begin + wave * CH;
-  u32x4 kf[2][KK];
-  u32x4 vf[MT];
-  if (t0 < p_end) {
-    int64_t pb0, pb1;
-    chunk_blocks(trow, t0, log2P, nblk, pb0, pb1);
-    load_k<D>(kf, kpool, a, h, t0, pb0, pb1, n, g);
-    __builtin_amdgcn_sched_barrier(0);  // K strictly before V
-    load_v<D>(vf, vpool, a, h, t0, pb0, pb1, n, g);
-  }
-
-  for (; t0 < p_end; t0 += kWaves * CH) {
+  for (int it = 0; it < n_w; ++it, t0 += kWaves * CH) {
     // Next chunk of this wave; on the last iteration the current chunk is
     // requested again (in bounds, served from L2), which keeps the number of
     // loads in flight the same on every iteration.
-    const int tn_raw = t0 + kWaves * CH;
-    const int tn = tn_raw < p_end ? tn_raw : t0;
+    const int tn = it + 1 < n_w ? t0 + kWaves * CH : t0;
     int64_t nb0, nb1;
-    chunk_blocks(trow, tn, log2P, nblk, nb0, nb1);
+    chunk_blocks(a, trow, tn, nb0, nb1);
 
     // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
     f32x4 s[2];

@@ -78,9 +78,12 @@ int device_cu_count() {
 // (128 tokens for bf16 = 4 waves x 32-token chunks, 256 for fp32), so chunks
 // never straddle a partition; an explicit length must be a multiple of 256.
 // Without one, the planner cuts every row into the largest number of equal
-// partitions for which all (request, kv head, partition) work-groups fit on
-// the GPU at once (CUs x resident work-groups per CU), measured over the
-// longest row the table can describe (the host does not see seq_lens).
+// partitions for which the (request, kv head, partition) work-groups number
+// at most one per CU, measured over the longest row the table can describe
+// (the host does not see seq_lens).  More resident work-groups per CU only
+// add bytes in flight: measured on MI355X, one 4-wave work-group per CU
+// already keeps the HBM stream at its chunked-access ceiling, while three
+// per CU lose ~10% and lengthen the final merges.
 int plan_partitions(const pba_kv_pool* pool, int32_t batch, int32_t max_blocks, int32_t requested,
                     int32_t* part_tokens, int32_t* n_parts) {
   const int64_t max_T = (int64_t)max_blocks * pool->block_size;
@@ -93,9 +96,7 @@ int plan_partitions(const pba_kv_pool* pool, int32_t batch, int32_t max_blocks, 
   } else if (requested < 0) {
     return PBA_ERR_BAD_SHAPE;
   } else {
-    int occ = pba::decode_workgroups_per_cu(pool->dtype, pool->head_dim);
-    if (occ <= 0) occ = 2;
-    const int64_t slots = (int64_t)occ * device_cu_count();
+    const int64_t slots = device_cu_count();
     const int64_t units = (int64_t)batch * pool->num_kv_heads;
     const int64_t max_splits = (max_T + granule - 1) / granule;
     int64_t splits = slots / units;
@@ -320,6 +321,7 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   a.ws_ml = need ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
   a.ws_u = need ? reinterpret_cast<float*>(wsb + ws.u_off) : nullptr;
   a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = pool->num_blocks;
   a.log2P = log2_exact(pool->block_size);
   a.G = G;
   a.num_q_heads = num_q_heads;

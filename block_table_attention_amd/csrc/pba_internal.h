@@ -46,6 +46,7 @@ struct DecodeArgs {
   float* ws_u;   // [B][H_q][n_parts][D]: unnormalised output
   int32_t* counters;  // [B][H_kv]: partitions finished; zero between calls
   int32_t max_blocks;
+  int32_t num_blocks;  // pool size: clamp for block ids read ahead of the length
   int32_t log2P;
   int32_t G;
   int32_t num_q_heads;
