@@ -63,7 +63,7 @@ struct WaveStates {
   float l[kWaves][16];
   union {
     float o[kWaves][D][17];   // [dim][head], padded against bank conflicts
-    float w[16 * 2 * 16];     // (m, l) of a tile of partitions, final merge
+    float w[16 * 2 * 4];      // (m, l) of a tile of partitions, final merge
   };
   int last;
 };
@@ -84,66 +84,70 @@ __device__ __forceinline__ float ld_state(const float* p) {
 
 // Final merge of the partition states of one (request, kv head):
 //   O = sum_p w_p u_p / L,  w_p = 2^(m_p - M),  M = max_p m_p,  L = sum_p w_p l_p,
-// partitions in index order.  Every load is issued before any result is
-// used: the (m, l) of all partitions go to LDS, each thread keeps the u of its
-// output elements in registers, so the merge costs one memory round trip.
-// Rows with more than kMergeFast partitions take the same path in tiles.
-constexpr int kMergeFast = 16;
+// partitions in index order, kMergeTile at a time with a running (M, L, O).
+// Within a tile every load is issued before any is used -- the (m, l) of all
+// heads go to LDS, the u of this thread's output elements to registers -- and
+// no load sits under a lane-dependent branch (indices are clamped in bounds
+// and the surplus ignored), so a tile costs one memory round trip.
+constexpr int kMergeTile = 4;
 
 template <int D>
 __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r, float* s_ml) {
   constexpr int KO = 16 * D / kDecodeThreads;  // output elements per thread (G <= 16)
   const int G = a.G;
+  const int nout = G * D;
   const int64_t row0 = (int64_t)r * a.num_q_heads + (int64_t)h * G;
   float O[KO], L[KO], M[KO];
 #pragma unroll
   for (int k = 0; k < KO; ++k) O[k] = 0.f, L[k] = 0.f, M[k] = -INFINITY;
-  for (int p0 = 0; p0 < np_r; p0 += kMergeFast) {
-    const int pn = min(kMergeFast, np_r - p0);
-    // (m, l) of this tile of partitions, every head, into LDS.
-    for (int i = threadIdx.x; i < G * pn * 2; i += kDecodeThreads) {
-      const int n = i / (2 * pn), rem = i - n * 2 * pn;
-      s_ml[n * 2 * kMergeFast + rem] = ld_state(a.ws_ml + ((row0 + n) * a.n_parts + p0) * 2 + rem);
-    }
-    float u[KO][kMergeFast];
+  for (int p0 = 0; p0 < np_r; p0 += kMergeTile) {
+    float u[KO][kMergeTile];
 #pragma unroll
     for (int k = 0; k < KO; ++k) {
-      const int idx = threadIdx.x + k * kDecodeThreads;
+      const int idx = min((int)threadIdx.x + k * kDecodeThreads, nout - 1);
       const int n = idx / D, c = idx - (idx / D) * D;
-      const float* uu = a.ws_u + ((row0 + n) * a.n_parts + p0) * D + c;
+      const float* uu = a.ws_u + (row0 + n) * a.n_parts * D + c;
 #pragma unroll
-      for (int p = 0; p < kMergeFast; ++p) u[k][p] = (n < G && p < pn) ? ld_state(uu + (int64_t)p * D) : 0.f;
+      for (int j = 0; j < kMergeTile; ++j) u[k][j] = ld_state(uu + (int64_t)min(p0 + j, np_r - 1) * D);
+    }
+    // (m, l) of partitions p0 .. p0+3 of every head: thread i < G*8 loads one.
+    {
+      const int i = min((int)threadIdx.x, G * 2 * kMergeTile - 1);
+      const int n = i / (2 * kMergeTile), j = (i >> 1) & (kMergeTile - 1), e = i & 1;
+      const int p = min(p0 + j, np_r - 1);
+      const float v = ld_state(a.ws_ml + ((row0 + n) * a.n_parts + p) * 2 + e);
+      if ((int)threadIdx.x < G * 2 * kMergeTile) s_ml[i] = v;
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < KO; ++k) {
       const int idx = threadIdx.x + k * kDecodeThreads;
-      const int n = idx / D;
-      if (n >= G) continue;
-      const float* ml = s_ml + n * 2 * kMergeFast;
+      const int n = min(idx / D, G - 1);
+      const float* ml = s_ml + n * 2 * kMergeTile;
       float Mt = M[k];
-      for (int p = 0; p < pn; ++p) Mt = fmaxf(Mt, ml[2 * p]);
-      if (Mt == -INFINITY) continue;
+#pragma unroll
+      for (int j = 0; j < kMergeTile; ++j)
+        if (p0 + j < np_r) Mt = fmaxf(Mt, ml[2 * j]);
       const float sc = (M[k] == -INFINITY) ? 0.f : fast_exp2(M[k] - Mt);
       float Lt = L[k] * sc, Ot = O[k] * sc;
 #pragma unroll
-      for (int p = 0; p < kMergeFast; ++p) {
-        if (p >= pn) break;
-        const float mp = ml[2 * p];
-        if (mp == -INFINITY) continue;
-        const float w = fast_exp2(mp - Mt);
-        Lt += w * ml[2 * p + 1];
-        Ot += w * u[k][p];
+      for (int j = 0; j < kMergeTile; ++j) {
+        const float mp = ml[2 * j];
+        if (p0 + j < np_r && mp != -INFINITY) {
+          const float w = fast_exp2(mp - Mt);
+          Lt += w * ml[2 * j + 1];
+          Ot += w * u[k][j];
+        }
       }
-      M[k] = Mt, L[k] = Lt, O[k] = Ot;
+      if (Mt != -INFINITY) M[k] = Mt, L[k] = Lt, O[k] = Ot;
     }
     __syncthreads();
   }
 #pragma unroll
   for (int k = 0; k < KO; ++k) {
     const int idx = threadIdx.x + k * kDecodeThreads;
+    if (idx >= nout) break;
     const int n = idx / D, c = idx - (idx / D) * D;
-    if (n >= G) continue;
     const int64_t row = row0 + n;
     a.out[row * D + c] = (L[k] > 0.f) ? O[k] / L[k] : 0.f;
     if (a.lse && c == 0) a.lse[row] = (L[k] > 0.f) ? (M[k] + __log2f(L[k])) * kLn2 : -INFINITY;

@@ -63,7 +63,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
 // Resident work-groups per CU of the decode kernel for (dtype, head_dim); 0 if unknown.
 int decode_workgroups_per_cu(int dtype, int head_dim);
 // Work-group size and the token granule partitions are cut at, per dtype.
-constexpr int kDecodeThreads = 256;
-inline int decode_granule(int dtype) { return dtype == PBA_BF16 ? 128 : 256; }
+#ifndef PBA_DECODE_WAVES
+#define PBA_DECODE_WAVES 4
+#endif
+constexpr int kDecodeThreads = 64 * PBA_DECODE_WAVES;
+inline int decode_granule(int dtype) { return (dtype == PBA_BF16 ? 32 : 64) * PBA_DECODE_WAVES; }
 
 }  // namespace pba
