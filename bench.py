@@ -10,10 +10,11 @@ Default workload: long16k -- 8 requests x 16,384 tokens of context at decode
 kv-heads (GQA 8), head_dim 128, bf16 K/V, pool of 4096 blocks (1 GiB).  All
 inputs are seeded synthetic data and resident in HBM before timing starts.
 
-Prints one JSON line (see the field list in the design doc).  The decode call is
-also timed per launch with HIP events on the stream it runs on; that average
-is the roofline figure.  The cpu_baseline leg times the CPU oracle on a
-bounded sample of the same workload.
+Prints one JSON line: metric, value (K/V GB/s of a whole step), step time,
+query rows/s, the roofline of the decode kernel (its average launch time over
+a back-to-back burst, timed with HIP events on its stream, against HBM peak),
+and cpu_baseline (the CPU oracle timed on a bounded sample of the same
+workload).
 """
 from __future__ import annotations
 
@@ -76,11 +77,34 @@ def decode_bytes(lengths, P, Hq, Hkv, d, esize):
     return kv, kv + q + out + tbl
 
 
+def profiled_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 summary, or None
+    when there is none for this workload or the decode source changed since."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", f"decode_bf16_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    m_h = re.search(r"decode_source_sha256: ([0-9a-f]{64})", text)
+    if not (m_t and m_h):
+        return None
+    csrc = os.path.join(ROOT, "block_table_attention_amd", "csrc")
+    blob = b"".join(open(os.path.join(csrc, f), "rb").read()
+                    for f in ("paged_decode.hip", "pba_internal.h"))
+    if hashlib.sha256(blob).hexdigest() != m_h.group(1):
+        return None
+    return int(m_t.group(1))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding plan is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: this implementation runs on one GPU; --gpus {args.gpus} is not "
+              "supported (requests and kv heads shard without exchange, one long request "
+              "would need an all-gather of partition states)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -183,6 +207,7 @@ def main():
           file=sys.stderr, flush=True)
 
     kv_bytes, alg_bytes = decode_bytes(ctx, P, Hq, Hkv, d, esize)
+    traffic = profiled_traffic(w.name) if args.partition_tokens == 0 else None
     step_kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg_ms * 1e-3) / 1e9
     result = {
@@ -210,7 +235,8 @@ def main():
         "decode_us": round(dec_avg_ms * 1e3, 2),
         "decode_us_in_step": round(dec_step_ms * 1e3, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
                      "kernel": "decode_bf16_kernel<128> (partition merge fused in)",
                      "algorithmic_bytes_per_launch": alg_bytes},
     }
