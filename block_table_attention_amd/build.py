@@ -25,6 +25,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          # MFMA accumulators in arch VGPRs: the online-softmax rescale is VALU
          # work on them, and AGPR homes cost two copies per chunk.
          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+         # The decode kernel's leading scalar arguments (10 of them, 14 dwords,
+         # the hardware maximum) arrive preloaded in SGPRs.
+         "-mllvm", "-amdgpu-kernarg-preload-count=10",
          "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

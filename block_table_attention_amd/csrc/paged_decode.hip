@@ -61,96 +61,79 @@ template <int D>
 struct WaveStates {
   float m[kWaves][16];
   float l[kWaves][16];
-  union {
-    float o[kWaves][D][17];   // [dim][head], padded against bank conflicts
-    float w[16 * 2 * 4];      // (m, l) of a tile of partitions, final merge
-  };
+  float o[kWaves][16][D + 4];  // [head][dim]; rows padded against bank conflicts
   int last;
 };
 
 // Partition states cross work-groups (and XCDs, whose L2s are not coherent
 // with each other) through memory: they are written and read with
-// system-coherent (write-through / uncached) accesses, so no device-wide
+// device-coherent (write-through / L2-bypassing) accesses, so no device-wide
 // cache write-back or invalidate is needed.  The writer waits for its stores
 // to complete (vmcnt(0)) before it increments the completion counter; the
 // work-group that observes the final count reads the states from memory.
 __device__ __forceinline__ void st_state(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ float ld_state(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Final merge of the partition states of one (request, kv head):
 //   O = sum_p w_p u_p / L,  w_p = 2^(m_p - M),  M = max_p m_p,  L = sum_p w_p l_p,
 // partitions in index order, kMergeTile at a time with a running (M, L, O).
-// Within a tile every load is issued before any is used -- the (m, l) of all
-// heads go to LDS, the u of this thread's output elements to registers -- and
-// no load sits under a lane-dependent branch (indices are clamped in bounds
-// and the surplus ignored), so a tile costs one memory round trip.
-constexpr int kMergeTile = 4;
+// A thread owns four consecutive dims of one head, so it needs only that
+// head's (m, l): every load of a tile is issued before any is used and none
+// sits under a lane-dependent branch (partition indices are clamped in bounds
+// and the surplus ignored), so a tile costs one memory round trip and the
+// merge needs no LDS and no barrier.
+constexpr int kMergeTile = 8;
 
 template <int D>
-__device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r, float* s_ml) {
-  constexpr int KO = 16 * D / kDecodeThreads;  // output elements per thread (G <= 16)
+__device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
+  constexpr int C4 = D / 4;
   const int G = a.G;
-  const int nout = G * D;
   const int64_t row0 = (int64_t)r * a.num_q_heads + (int64_t)h * G;
-  float O[KO], L[KO], M[KO];
-#pragma unroll
-  for (int k = 0; k < KO; ++k) O[k] = 0.f, L[k] = 0.f, M[k] = -INFINITY;
-  for (int p0 = 0; p0 < np_r; p0 += kMergeTile) {
-    float u[KO][kMergeTile];
-#pragma unroll
-    for (int k = 0; k < KO; ++k) {
-      const int idx = min((int)threadIdx.x + k * kDecodeThreads, nout - 1);
-      const int n = idx / D, c = idx - (idx / D) * D;
-      const float* uu = a.ws_u + (row0 + n) * a.n_parts * D + c;
-#pragma unroll
-      for (int j = 0; j < kMergeTile; ++j) u[k][j] = ld_state(uu + (int64_t)min(p0 + j, np_r - 1) * D);
-    }
-    // (m, l) of partitions p0 .. p0+3 of every head: thread i < G*8 loads one.
-    {
-      const int i = min((int)threadIdx.x, G * 2 * kMergeTile - 1);
-      const int n = i / (2 * kMergeTile), j = (i >> 1) & (kMergeTile - 1), e = i & 1;
-      const int p = min(p0 + j, np_r - 1);
-      const float v = ld_state(a.ws_ml + ((row0 + n) * a.n_parts + p) * 2 + e);
-      if ((int)threadIdx.x < G * 2 * kMergeTile) s_ml[i] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < KO; ++k) {
-      const int idx = threadIdx.x + k * kDecodeThreads;
-      const int n = min(idx / D, G - 1);
-      const float* ml = s_ml + n * 2 * kMergeTile;
-      float Mt = M[k];
-#pragma unroll
-      for (int j = 0; j < kMergeTile; ++j)
-        if (p0 + j < np_r) Mt = fmaxf(Mt, ml[2 * j]);
-      const float sc = (M[k] == -INFINITY) ? 0.f : fast_exp2(M[k] - Mt);
-      float Lt = L[k] * sc, Ot = O[k] * sc;
+  for (int idx = threadIdx.x; idx < G * C4; idx += kDecodeThreads) {
+    const int n = idx / C4;
+    const int c = 4 * (idx - n * C4);
+    const int64_t row = row0 + n;
+    const float* ml = a.ws_ml + row * a.n_parts * 2;
+    const float* uu = a.ws_u + row * a.n_parts * D + c;
+    float M = -INFINITY, L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int p0 = 0; p0 < np_r; p0 += kMergeTile) {
+      float mt[kMergeTile], lt[kMergeTile];
+      f32x4 ut[kMergeTile];
 #pragma unroll
       for (int j = 0; j < kMergeTile; ++j) {
-        const float mp = ml[2 * j];
-        if (p0 + j < np_r && mp != -INFINITY) {
-          const float w = fast_exp2(mp - Mt);
-          Lt += w * ml[2 * j + 1];
-          Ot += w * u[k][j];
+        const int64_t pp = min(p0 + j, np_r - 1);
+        mt[j] = ld_state(ml + 2 * pp);
+        lt[j] = ld_state(ml + 2 * pp + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(uu + pp * D + e);
+      }
+      float Mt = M;
+#pragma unroll
+      for (int j = 0; j < kMergeTile; ++j)
+        if (p0 + j < np_r) Mt = fmaxf(Mt, mt[j]);
+      if (Mt == -INFINITY) continue;  // only empty states so far: identity
+      const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mt);
+      L *= sc;
+      O *= sc;
+#pragma unroll
+      for (int j = 0; j < kMergeTile; ++j) {
+        if (p0 + j < np_r && mt[j] != -INFINITY) {
+          const float w = fast_exp2(mt[j] - Mt);
+          L += w * lt[j];
+          O += w * ut[j];
         }
       }
-      if (Mt != -INFINITY) M[k] = Mt, L[k] = Lt, O[k] = Ot;
+      M = Mt;
     }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < KO; ++k) {
-    const int idx = threadIdx.x + k * kDecodeThreads;
-    if (idx >= nout) break;
-    const int n = idx / D, c = idx - (idx / D) * D;
-    const int64_t row = row0 + n;
-    a.out[row * D + c] = (L[k] > 0.f) ? O[k] / L[k] : 0.f;
-    if (a.lse && c == 0) a.lse[row] = (L[k] > 0.f) ? (M[k] + __log2f(L[k])) * kLn2 : -INFINITY;
+    const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(a.out + row * D + c) = res;
+    if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
   }
 }
 
@@ -159,15 +142,17 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r, fl
 template <int D>
 __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, int h, int part,
                                  int T) {
+  constexpr int C4 = D / 4;
   const int G = a.G;
   const int np_r = (T + a.part_tokens - 1) / a.part_tokens;
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-    const int n = idx / D;
-    const int c = idx - n * D;
+  for (int idx = threadIdx.x; idx < G * C4; idx += kDecodeThreads) {
+    const int n = idx / C4;
+    const int c = 4 * (idx - n * C4);
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st.m[w][n]);
-    float L = 0.f, O = 0.f;
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) {
@@ -175,16 +160,18 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
         if (mw == -INFINITY) continue;  // a wave that saw no chunk: identity
         const float wt = fast_exp2(mw - M);
         L += wt * st.l[w][n];
-        O += wt * st.o[w][c][n];
+        O += wt * *reinterpret_cast<const f32x4*>(&st.o[w][n][c]);
       }
     }
     const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
     if (np_r == 1) {
-      a.out[row * D + c] = (L > 0.f) ? O / L : 0.f;
+      const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(a.out + row * D + c) = res;
       if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = row * a.n_parts + part;
-      st_state(a.ws_u + prow * D + c, O);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st_state(a.ws_u + prow * D + c + e, O[e]);
       if (c == 0) {
         st_state(a.ws_ml + prow * 2 + 0, M);
         st_state(a.ws_ml + prow * 2 + 1, L);
@@ -200,7 +187,7 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
                np_r - 1);
   __syncthreads();
   if (!st.last) return;
-  merge_partitions<D>(a, r, h, np_r, st.w);
+  merge_partitions<D>(a, r, h, np_r);
   if (threadIdx.x == 0) *counter = 0;  // ready for the next call on this workspace
 }
 
@@ -212,53 +199,70 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
 // not queue behind the vector K/V loads.
 typedef const int32_t __attribute__((address_space(4))) table_t;
 
+// What the first loads of a work-group depend on: its block-table row, the
+// pool bases and strides.  These values reach the kernel as separate scalar
+// arguments ahead of the argument bundle, which the build preloads into SGPRs
+// (kernarg preload), so the first table read does not wait for a fetch of the
+// kernel arguments.
+struct PoolView {
+  table_t* trow;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_sb, k_sh, v_sb, v_sh;
+  int max_blocks;
+  int last_block;  // num_blocks - 1: clamp for ids read ahead of the length
+  int log2P;
+};
+
 // Physical block ids of the chunk starting at t0 (one when P >= 32, two when
 // P == 16).  Ids are clamped into the pool so that a lookup made before the
 // request length is known (or past it) only ever addresses pool memory; rows
 // past the length are masked out of the result regardless.
-__device__ __forceinline__ void chunk_blocks(const DecodeArgs& a, table_t* trow, int t0,
-                                             int64_t& pb0, int64_t& pb1) {
-  const int j0 = min(t0 >> a.log2P, a.max_blocks - 1);
-  const int last = a.num_blocks - 1;
-  pb0 = min(max(trow[j0], 0), last);
+__device__ __forceinline__ void chunk_blocks(const PoolView& pv, int t0, int64_t& pb0,
+                                             int64_t& pb1) {
+  const int j0 = min(t0 >> pv.log2P, pv.max_blocks - 1);
+  pb0 = min(max(pv.trow[j0], 0), pv.last_block);
   pb1 = pb0;
-  if (a.log2P == 4) pb1 = min(max(trow[min(j0 + 1, a.max_blocks - 1)], 0), last);
+  if (pv.log2P == 4) pb1 = min(max(pv.trow[min(j0 + 1, pv.max_blocks - 1)], 0), pv.last_block);
 }
 
 template <int D>
-__device__ __forceinline__ void load_k(u32x4 (&kf)[2][D / 32], const uint16_t* kpool,
-                                       const DecodeArgs& a, int h, int t0, int64_t pb0,
-                                       int64_t pb1, int n, int g) {
-  const int P = 1 << a.log2P;
+__device__ __forceinline__ void load_k(u32x4 (&kf)[2][D / 32], const PoolView& pv, int h, int t0,
+                                       int64_t pb0, int64_t pb1, int n, int g) {
+  const int P = 1 << pv.log2P;
 #pragma unroll
   for (int at = 0; at < 2; ++at) {
     // A-operand row n of tile `at` holds chunk token 8(n>>2) + 4at + (n&3).
     const int tk = 8 * (n >> 2) + 4 * at + (n & 3);
-    const int64_t pb = (tk >= 16 && a.log2P == 4) ? pb1 : pb0;
+    const int64_t pb = (tk >= 16 && pv.log2P == 4) ? pb1 : pb0;
     const int off = (t0 + tk) & (P - 1);
-    const uint16_t* kp = kpool + pb * a.k_sb + (int64_t)h * a.k_sh + (int64_t)off * D + 8 * g;
+    const uint16_t* kp = pv.k + pb * pv.k_sb + (int64_t)h * pv.k_sh + (int64_t)off * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) kf[at][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const uint16_t* vpool,
-                                       const DecodeArgs& a, int h, int t0, int64_t pb0,
-                                       int64_t pb1, int n, int g) {
-  const int P = 1 << a.log2P;
+__device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, int h, int t0,
+                                       int64_t pb0, int64_t pb1, int n, int g) {
+  const int P = 1 << pv.log2P;
   // A-operand row n of tile mt is dim 16mt + n; its k-slots are tokens 8g..8g+7.
   const int tv = 8 * g;
-  const int64_t pb = (tv >= 16 && a.log2P == 4) ? pb1 : pb0;
+  const int64_t pb = (tv >= 16 && pv.log2P == 4) ? pb1 : pb0;
   const int off = (t0 + tv) & (P - 1);
-  const uint16_t* vp = vpool + pb * a.v_sb + (int64_t)h * a.v_sh + (int64_t)n * P + off;
+  const uint16_t* vp = pv.v + pb * pv.v_sb + (int64_t)h * pv.v_sh + (int64_t)n * P + off;
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt)
     vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
 }
 
+// Grid: x = partition, y = kv head, z = request.
 template <int D>
-__global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
+    const void* __restrict__ kbase, const void* __restrict__ vbase, int32_t max_blocks,
+    int32_t part_tokens, int32_t log2P, int32_t last_block, int32_t k_sb, int32_t k_sh,
+    DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KK = D / 32;  // k-steps of the score product
   constexpr int MT = D / 16;  // 16-dim tiles of the value product
@@ -266,31 +270,30 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
 
   __shared__ WaveStates<D> st;
 
-  const int wg = blockIdx.x;
-  const int part = wg % a.n_parts;
-  const int rest = wg / a.n_parts;
-  const int h = rest % a.num_kv_heads;
-  const int r = rest / a.num_kv_heads;
+  const int part = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r = blockIdx.z;
   const int lane = threadIdx.x & 63;
   // Wave-uniform (SGPR): chunk positions and block-table reads become scalar.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15;  // head column of this lane
   const int g = lane >> 4;  // k-group of this lane
   const int G = a.G;
-  const int p_begin = part * a.part_tokens;
-  const uint16_t* kpool = static_cast<const uint16_t*>(a.k);
-  const uint16_t* vpool = static_cast<const uint16_t*>(a.v);
-  table_t* trow = (table_t*)(a.tables + (int64_t)r * a.max_blocks);
+  const int p_begin = part * part_tokens;
+  const PoolView pv{(table_t*)(tables + (int64_t)r * max_blocks),
+                    static_cast<const uint16_t*>(kbase),
+                    static_cast<const uint16_t*>(vbase),
+                    k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P};
 
   // Start-up, without waiting for the request length: the length, this wave's
   // first block-table entry, q, and the first chunk's K and V are all
   // requested at once.  Nothing is read out of bounds whatever the length
   // turns out to be (see chunk_blocks); the loads are simply unused when the
   // wave has no chunk.  Issue order q, K, V keeps the in-loop waits exact.
-  const int T = a.seq_lens[r];
+  const int T = seq_lens[r];
   int t0 = p_begin + wave * CH;
   int64_t pb0, pb1;
-  chunk_blocks(a, trow, t0, pb0, pb1);
+  chunk_blocks(pv, t0, pb0, pb1);
   bf16x8 qf[KK];
   {
     // Q^T fragments (B operand of the score product): lane holds dims
@@ -307,13 +310,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
   __builtin_amdgcn_sched_barrier(0);
   u32x4 kf[2][KK];
   u32x4 vf[MT];
-  load_k<D>(kf, kpool, a, h, t0, pb0, pb1, n, g);
+  load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
   __builtin_amdgcn_sched_barrier(0);
-  load_v<D>(vf, vpool, a, h, t0, pb0, pb1, n, g);
+  load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
   __builtin_amdgcn_sched_barrier(0);
 
   if (p_begin >= T) return;  // empty partition: never counted, never read
-  const int p_end = min(T, p_begin + a.part_tokens);
+  const int p_end = min(T, p_begin + part_tokens);
   // This wave's chunks: p_begin + wave*CH + k*kWaves*CH for k < n_w.
   const int span = p_end - p_begin - wave * CH;
   const int n_w = span > 0 ? (span + kWaves * CH - 1) / (kWaves * CH) : 0;
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
     // loads in flight the same on every iteration.
     const int tn = it + 1 < n_w ? t0 + kWaves * CH : t0;
     int64_t nb0, nb1;
-    chunk_blocks(a, trow, tn, nb0, nb1);
+    chunk_blocks(pv, tn, nb0, nb1);
 
     // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
     f32x4 s[2];
@@ -342,7 +345,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
         s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[at][kk]),
                                                          qf[kk], s[at], 0, 0, 0);
     }
-    load_k<D>(kf, kpool, a, h, tn, nb0, nb1, n, g);
+    load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
 
     const int tbase = t0 + 8 * g;  // token of k-slot j = 0 of this lane
     float x[8];
@@ -401,10 +404,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[mt], 0, 0, 0);
       acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[mt], 0, 0, 0);
     }
-    load_v<D>(vf, vpool, a, h, tn, nb0, nb1, n, g);
+    load_v<D>(vf, pv, h, tn, nb0, nb1, n, g);
   }
 
-  // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n].
+  // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n]: four
+  // consecutive dims of one head per lane.
   l_run += __shfl_xor(l_run, 16, 64);
   l_run += __shfl_xor(l_run, 32, 64);
   if (g == 0) {
@@ -412,9 +416,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(DecodeArgs 
     st.l[wave][n] = l_run;
   }
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st.o[wave][16 * mt + 4 * g + i][n] = acc[mt][i];
+  for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(&st.o[wave][n][16 * mt + 4 * g]) = acc[mt];
   __syncthreads();
   finish_workgroup<D>(a, st, r, h, part, T);
 }
@@ -433,11 +435,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
   __shared__ float sq[16][D];
   __shared__ float sp[kWaves][16][CH];
 
-  const int wg = blockIdx.x;
-  const int part = wg % a.n_parts;
-  const int rest = wg / a.n_parts;
-  const int h = rest % a.num_kv_heads;
-  const int r = rest / a.num_kv_heads;
+  const int part = blockIdx.x;
+  const int h = blockIdx.y;
+  const int r = blockIdx.z;
 
   const int T = a.seq_lens[r];
   const int p_begin = part * a.part_tokens;
@@ -547,51 +547,44 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
       st.l[wave][gg] = l;
     }
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) st.o[wave][lane + 64 * e][gg] = u[gg][e];
+    for (int e = 0; e < DPL; ++e) st.o[wave][gg][lane + 64 * e] = u[gg][e];
   }
   __syncthreads();
   finish_workgroup<D>(a, st, r, h, part, T);
 }
 
-template <typename K>
-static int occupancy(K kernel) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, kDecodeThreads, 0) != hipSuccess) {
-    (void)hipGetLastError();
-    return 0;
-  }
-  return n;
-}
-
-int decode_workgroups_per_cu(int dtype, int head_dim) {
-  static int cache[2][2] = {{-1, -1}, {-1, -1}};
-  const int i = dtype == PBA_BF16 ? 1 : 0, j = head_dim == 128 ? 1 : 0;
-  if (cache[i][j] < 0) {
-    int n;
-    if (dtype == PBA_BF16)
-      n = head_dim == 128 ? occupancy(decode_bf16_kernel<128>) : occupancy(decode_bf16_kernel<64>);
-    else
-      n = head_dim == 128 ? occupancy(decode_f32_kernel<128>) : occupancy(decode_f32_kernel<64>);
-    cache[i][j] = n;
-  }
-  return cache[i][j];
-}
-
 hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
-  const int64_t wgs = (int64_t)a.n_parts * a.num_kv_heads * a.batch;
-  const dim3 grid((unsigned)wgs), block(kDecodeThreads);
-  if (dtype == PBA_BF16) {
-    if (head_dim == 128)
-      hipLaunchKernelGGL(decode_bf16_kernel<128>, grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, block, 0, stream, a);
-  } else {
-    if (head_dim == 128)
-      hipLaunchKernelGGL(decode_f32_kernel<128>, grid, block, 0, stream, a);
-    else
-      hipLaunchKernelGGL(decode_f32_kernel<64>, grid, block, 0, stream, a);
+  // Requests go on the grid's z axis, at most kMaxGridZ per launch; a larger
+  // batch is launched in slices whose per-request pointers are offset.
+  constexpr int kMaxGridZ = 65535;
+  for (int r0 = 0; r0 < a.batch; r0 += kMaxGridZ) {
+    const int nb = min(a.batch - r0, kMaxGridZ);
+    DecodeArgs s = a;
+    const int64_t rows = (int64_t)r0 * a.num_q_heads;
+    s.q = static_cast<const char*>(a.q) + rows * head_dim * (dtype == PBA_BF16 ? 2 : 4);
+    s.tables = a.tables + (int64_t)r0 * a.max_blocks;
+    s.seq_lens = a.seq_lens + r0;
+    s.out = a.out + rows * head_dim;
+    s.lse = a.lse ? a.lse + rows : nullptr;
+    s.ws_ml = a.ws_ml ? a.ws_ml + rows * a.n_parts * 2 : nullptr;
+    s.ws_u = a.ws_u ? a.ws_u + rows * a.n_parts * head_dim : nullptr;
+    s.counters = a.counters ? a.counters + (int64_t)r0 * a.num_kv_heads : nullptr;
+    s.batch = nb;
+    const dim3 grid((unsigned)a.n_parts, (unsigned)a.num_kv_heads, (unsigned)nb);
+    const dim3 block(kDecodeThreads);
+    if (dtype == PBA_BF16) {
+      auto kern = head_dim == 128 ? decode_bf16_kernel<128> : decode_bf16_kernel<64>;
+      hipLaunchKernelGGL(kern, grid, block, 0, stream, s.tables, s.seq_lens, s.k, s.v,
+                         s.max_blocks, s.part_tokens, s.log2P, s.num_blocks - 1,
+                         (int32_t)s.k_sb, (int32_t)s.k_sh, s);
+    } else {
+      auto kern = head_dim == 128 ? decode_f32_kernel<128> : decode_f32_kernel<64>;
+      hipLaunchKernelGGL(kern, grid, block, 0, stream, s);
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipGetLastError();
+  return hipSuccess;
 }
 
 }  // namespace pba

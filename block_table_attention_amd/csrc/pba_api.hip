@@ -58,6 +58,22 @@ int check_pool(const pba_kv_pool* pool) {
   return PBA_OK;
 }
 
+// Shape checks shared by the decode entry points (pool checked first).  The
+// decode kernel takes the K strides as int32 and the kv heads on a grid axis
+// of at most 65535.
+int check_decode_shape(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
+                       int32_t max_blocks_per_seq) {
+  const int st = check_pool(pool);
+  if (st) return st;
+  if (num_q_heads <= 0 || batch < 0 || max_blocks_per_seq <= 0) return PBA_ERR_BAD_SHAPE;
+  if (num_q_heads % pool->num_kv_heads) return PBA_ERR_BAD_SHAPE;
+  if (num_q_heads / pool->num_kv_heads > 16) return PBA_ERR_UNSUPPORTED;
+  if (pool->k_stride_block > INT32_MAX || pool->k_stride_head > INT32_MAX ||
+      pool->num_kv_heads > 65535)
+    return PBA_ERR_UNSUPPORTED;
+  return PBA_OK;
+}
+
 int device_cu_count() {
   static std::mutex mu;
   static std::vector<int> cache;
@@ -240,11 +256,8 @@ int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* d
 int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
                           int32_t max_blocks_per_seq, int32_t partition_tokens,
                           int32_t* partition_tokens_out, int32_t* num_partitions_out) {
-  int st = check_pool(pool);
+  int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
-  if (num_q_heads <= 0 || batch < 0 || max_blocks_per_seq <= 0) return PBA_ERR_BAD_SHAPE;
-  if (num_q_heads % pool->num_kv_heads) return PBA_ERR_BAD_SHAPE;
-  if (num_q_heads / pool->num_kv_heads > 16) return PBA_ERR_UNSUPPORTED;
   int32_t pt = 0, np = 0;
   st = plan_partitions(pool, batch > 0 ? batch : 1, max_blocks_per_seq, partition_tokens, &pt, &np);
   if (st) return st;
@@ -269,21 +282,17 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
                      const int32_t* seq_lens, int32_t batch, float scale, float* out, float* lse,
                      int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  int st = check_pool(pool);
+  int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
-  if (batch < 0 || num_q_heads <= 0 || max_blocks_per_seq <= 0) return PBA_ERR_BAD_SHAPE;
-  if (num_q_heads % pool->num_kv_heads) return PBA_ERR_BAD_SHAPE;
   const int G = num_q_heads / pool->num_kv_heads;
-  if (G > 16) return PBA_ERR_UNSUPPORTED;
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
-  if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
+  if (!aligned16(q) || !aligned16(out)) return PBA_ERR_UNSUPPORTED;
   int32_t pt = 0, np = 0;
   st = plan_partitions(pool, batch, max_blocks_per_seq, partition_tokens, &pt, &np);
   if (st) return st;
   const int64_t rows = (int64_t)batch * num_q_heads;
-  const int64_t wgs = (int64_t)np * pool->num_kv_heads * batch;
-  if (wgs > INT32_MAX || rows > INT32_MAX) return PBA_ERR_UNSUPPORTED;
+  if (rows > INT32_MAX) return PBA_ERR_UNSUPPORTED;
   const WsLayout ws = workspace_layout(batch, pool->num_kv_heads, rows, np, pool->head_dim);
   const size_t need = ws.bytes;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))

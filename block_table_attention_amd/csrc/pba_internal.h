@@ -32,7 +32,8 @@ struct CopyArgs {
   int32_t esize;
 };
 
-// Decode: one work-group per (partition, kv head, request).
+// Decode: one work-group per (partition, kv head, request).  The decode kernel
+// takes k_sb and k_sh as int32 (the host rejects larger strides).
 struct DecodeArgs {
   const void* k;
   const void* v;
@@ -60,8 +61,6 @@ struct DecodeArgs {
 hipError_t launch_kv_append(const AppendArgs& a, int esize, hipStream_t stream);
 hipError_t launch_block_copy(const CopyArgs& a, int64_t n_pairs, int kv_heads, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
-// Resident work-groups per CU of the decode kernel for (dtype, head_dim); 0 if unknown.
-int decode_workgroups_per_cu(int dtype, int head_dim);
 // Work-group size and the token granule partitions are cut at, per dtype.
 #ifndef PBA_DECODE_WAVES
 #define PBA_DECODE_WAVES 4

@@ -104,6 +104,23 @@ def test_decode_shape_rejections():
     need = lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, 2, 64, 256)
     assert call(8, 64, 256, 0x80000, need - 1) == -5
     assert call(8, 64, 256, 0x80008, need) == -5  # misaligned workspace
+    # The output takes 16-byte stores.
+    assert lib.pba_paged_decode(ctypes.byref(d), 0x30000, 8, 0x40000, 4, 0x50000, 2,
+                                ctypes.c_float(0.1), 0x60004, NULL, 0, NULL, 0, NULL) == -4
+
+
+def test_decode_stride_limit():
+    """The decode kernel takes the K strides as int32: larger ones are rejected
+    by all three decode entry points, while append and copy accept them."""
+    lib = _lib()
+    big = _desc(k_stride_block=1 << 31)
+    pt, npart = ctypes.c_int32(), ctypes.c_int32()
+    assert lib.pba_paged_decode(ctypes.byref(big), 0x30000, 8, 0x40000, 4, 0x50000, 2,
+                                ctypes.c_float(0.1), 0x60000, NULL, 0, NULL, 0, NULL) == -4
+    assert lib.pba_paged_decode_plan(ctypes.byref(big), 8, 2, 4, 0, ctypes.byref(pt),
+                                     ctypes.byref(npart)) == -4
+    assert lib.pba_paged_decode_workspace_bytes(ctypes.byref(big), 8, 2, 64, 256) == 0
+    assert lib.pba_kv_append(ctypes.byref(big), NULL, 0, NULL, NULL, NULL) == 0
 
 
 def test_workspace_and_plan():
