@@ -1,20 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark: one decode step of paged attention on one MI355X.
 
-A step is one pass of the whole hot path over the batch: kv_append of one new
-token per request, block_copy of the step's copy-on-write pairs (none in the
-long-context workloads), and paged_decode of one query row per request.
+A step is one pass of the whole hot path over the decode batch:
+  block_copy of the step's copy-on-write pairs, kv_append of the step's new
+  tokens (the trailing one-token appends of the workload's script), and
+  paged_decode of one query row per request of the batch.
 
 Default workload: long16k -- 8 requests x 16,384 tokens of context at decode
 (16,383 prefilled + 1 appended per step), block size 64, 64 q-heads / 8
-kv-heads (GQA 8), head_dim 128, bf16 K/V, pool of 4096 blocks (1 GiB).  All
-inputs are seeded synthetic data and resident in HBM before timing starts.
+kv-heads (GQA 8), head_dim 128, bf16 K/V, pool of 4096 blocks (1 GiB).  The
+other workloads (--workload, or --sweep for all of them) follow the same step
+on their own scripts.  All inputs are seeded synthetic data, and everything
+the step reads is resident in HBM before timing starts.  Block placement comes
+from the package's caller-side BlockManager run over the workload's script
+from its seeded free-FIFO order.
 
-Prints one JSON line: metric, value (K/V GB/s of a whole step), step time,
-query rows/s, the roofline of the decode kernel (its average launch time over
-a back-to-back burst, timed with HIP events on its stream, against HBM peak),
-and cpu_baseline (the CPU oracle timed on a bounded sample of the same
-workload).
+Prints one JSON line per workload: metric, value (unique K/V bytes the decode
+must read, per second of whole steps), step time, query rows/s, the roofline of
+the decode kernel (its average launch time over a back-to-back burst, timed
+with HIP events on its stream, against HBM peak), and cpu_baseline (the CPU
+oracle timed on a bounded sample of the same workload; single-workload runs
+only).
 """
 from __future__ import annotations
 
@@ -24,6 +30,8 @@ import math
 import os
 import sys
 import time
+from dataclasses import dataclass
+from typing import List, Tuple
 
 import numpy as np
 
@@ -31,6 +39,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+WORKLOADS = ["long16k", "long64k", "batch32", "shared_prefix", "lognormal_p16",
+             "lognormal_p64", "lognormal_p256", "tiny"]
 
 
 def parse():
@@ -38,7 +48,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="long16k", choices=["long16k", "long64k", "batch32"])
+    ap.add_argument("--workload", default="long16k", choices=WORKLOADS)
+    ap.add_argument("--sweep", action="store_true",
+                    help="every workload in turn, one JSON line each (no cpu_baseline)")
     ap.add_argument("--partition-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -50,31 +62,97 @@ def parse():
     return ap.parse_args()
 
 
+def make_workload(name: str):
+    import workloads as wl
+
+    if name.startswith("lognormal_p"):
+        return wl.lognormal(int(name[len("lognormal_p"):]))
+    return getattr(wl, name)()
+
+
 # ---------------------------------------------------------------------------
-# The caller's side of allocation for workloads without sharing: a fresh pool
-# hands out blocks from its free FIFO head, request by request.
+# The caller's side: run the script through the block manager.
 # ---------------------------------------------------------------------------
-def fresh_pool_layout(order: np.ndarray, lengths, P: int):
-    """Block tables [B, max_blocks] (int32) for a fresh pool, request-major."""
-    need = [-(-int(T) // P) for T in lengths]
-    tables = np.full((len(lengths), max(need)), -1, dtype=np.int32)
-    cursor = 0
-    for r, n in enumerate(need):
-        tables[r, :n] = order[cursor:cursor + n]
-        cursor += n
-    return tables
+@dataclass
+class Plan:
+    setup: List[Tuple]          # ("copy", src, dst) | ("append", slots, row_lo, row_hi)
+    step_src: np.ndarray        # copy-on-write pairs of the step
+    step_dst: np.ndarray
+    step_slots: np.ndarray      # slots of the step's appended tokens
+    step_rows: Tuple[int, int]  # their K/V rows in script order
+    tables: np.ndarray          # int32 [B, max_blocks] of the decode batch
+    seq_lens: np.ndarray        # int32 [B]
+    n_writes: int
 
 
-def slots_for(tables: np.ndarray, r: int, positions: np.ndarray, P: int) -> np.ndarray:
-    return tables[r, positions // P].astype(np.int64) * P + positions % P
+def plan_script(w) -> Plan:
+    """Setup = every action before the script's trailing one-token appends;
+    the step = those appends (with the copies they cause) and the decode."""
+    import workloads as wl
+    from block_table_attention_amd.blocks import BlockManager
+
+    m = BlockManager(w.shape.num_blocks, w.shape.block_size, free_order=wl.fifo_order(w))
+    n_tail = 0
+    for act in reversed(w.actions):
+        if act[0] != "append":
+            break
+        n_tail += 1
+    first_step = len(w.actions) - n_tail
+    setup: List[Tuple] = []
+    src: List[int] = []
+    dst: List[int] = []
+    step_slots: List[np.ndarray] = []
+    row = 0
+    step_lo = None
+    for i, act in enumerate(w.actions):
+        kind = act[0]
+        if kind == "new":
+            m.new_request()
+        elif kind == "fork":
+            m.fork(act[1])
+        elif kind == "release":
+            m.release(act[1])
+        else:
+            n = act[2] if kind == "prefill" else 1
+            slots, copies = m.append(act[1], n)
+            if i >= first_step:
+                step_lo = row if step_lo is None else step_lo
+                src += [c[0] for c in copies]
+                dst += [c[1] for c in copies]
+                step_slots.append(slots)
+            else:
+                for s, d in copies:
+                    setup.append(("copy", np.array([s], np.int32), np.array([d], np.int32)))
+                setup.append(("append", slots, row, row + n))
+            row += n
+    step_lo = row if step_lo is None else step_lo
+    return Plan(setup, np.array(src, np.int32), np.array(dst, np.int32),
+                np.concatenate(step_slots) if step_slots else np.zeros(0, np.int64),
+                (step_lo, row), m.block_tables(w.decode), m.seq_lens(w.decode), row)
 
 
-def decode_bytes(lengths, P, Hq, Hkv, d, esize):
-    kv = int(sum(lengths)) * Hkv * d * 2 * esize
-    q = len(lengths) * Hq * d * esize
-    out = len(lengths) * Hq * d * 4 + len(lengths) * Hq * 4
-    tbl = sum(-(-int(T) // P) for T in lengths) * 4 + len(lengths) * 4
-    return kv, kv + q + out + tbl
+def visible_slots(tables: np.ndarray, lens: np.ndarray, P: int) -> np.ndarray:
+    """Physical slot of every (request, position < T) the decode reads."""
+    out = []
+    for r, T in enumerate(lens):
+        t = np.arange(int(T), dtype=np.int64)
+        out.append(tables[r, t // P].astype(np.int64) * P + t % P)
+    return np.concatenate(out)
+
+
+def decode_bytes(plan: Plan, shape):
+    """(unique K/V bytes, logical K/V bytes, algorithmic bytes of one decode)."""
+    P, Hq, Hkv, d = shape.block_size, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
+    es = 2 if shape.dtype == "bf16" else 4
+    row = Hkv * d * 2 * es
+    lens = plan.seq_lens
+    B = len(lens)
+    kv_unique = int(np.unique(visible_slots(plan.tables, lens, P)).size) * row
+    kv_logical = int(lens.sum()) * row
+    q = B * Hq * d * es
+    out = B * Hq * d * 4 + B * Hq * 4
+    tbl = int(sum(-(-int(T) // P) for T in lens)) * 4 + B * 4
+    return kv_unique, kv_logical, kv_unique + q + out + tbl
 
 
 def profiled_traffic(workload: str):
@@ -109,31 +187,34 @@ def main():
 
     import torch
     import block_table_attention_amd as pba
-    import workloads as wl
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     if args.copy_calibration_mib:
         return copy_calibration(args, pba, torch, dev)
+    names = WORKLOADS if args.sweep else [args.workload]
+    for name in names:
+        result = run_workload(args, name, pba, torch, dev)
+        if not (args.sweep or args.no_cpu_baseline):
+            w = make_workload(name)
+            result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, result["_kv_value_bytes"])
+        result.pop("_kv_value_bytes")
+        print(json.dumps(result), flush=True)
 
-    w = {"long16k": wl.long16k, "long64k": wl.long64k, "batch32": wl.batch32}[args.workload]()
+
+def run_workload(args, name, pba, torch, dev):
+    import workloads as wl
+
+    w = make_workload(name)
     sh = w.shape
     P, Hq, Hkv, d = sh.block_size, sh.num_q_heads, sh.num_kv_heads, sh.head_dim
     tdtype = torch.bfloat16 if sh.dtype == "bf16" else torch.float32
-    esize = 2 if sh.dtype == "bf16" else 4
-
-    # Script shape of these workloads: per request a prefill, then one
-    # appended token per request (the step's append).
-    prefill = [a[2] for a in w.actions if a[0] == "prefill"]
-    B = len(prefill)
-    ctx = [T + 1 for T in prefill]          # context at decode
-    order = wl.fifo_order(w)
-    tables = fresh_pool_layout(order, ctx, P)
-    n_pre = sum(prefill)
     t0 = time.time()
-    k_rows, v_rows = wl.kv_rows(w, n_pre + B)
-    print(f"[bench] drew {n_pre + B} K/V rows in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    plan = plan_script(w)
+    k_rows, v_rows = wl.kv_rows(w, plan.n_writes)
+    print(f"[bench] {name}: planned the script and drew {plan.n_writes} K/V rows in "
+          f"{time.time() - t0:.1f}s", file=sys.stderr, flush=True)
 
     def dev_bits(bits):
         view = np.int16 if sh.dtype == "bf16" else np.int32
@@ -142,74 +223,93 @@ def main():
     k0, v0 = wl.pool_poison(w)
     pool = pba.KVPool(dev_bits(k0), dev_bits(v0))
     del k0, v0
-    pre_slots = np.concatenate([slots_for(tables, r, np.arange(prefill[r]), P) for r in range(B)])
-    step_slots = np.array([slots_for(tables, r, np.array([prefill[r]]), P)[0] for r in range(B)])
-    pba.kv_append(pool, torch.from_numpy(pre_slots).to(dev), dev_bits(k_rows[:n_pre]),
-                  dev_bits(v_rows[:n_pre]))
-    k_step, v_step = dev_bits(k_rows[n_pre:]), dev_bits(v_rows[n_pre:])
-    step_slots_d = torch.from_numpy(step_slots).to(dev)
-    copy_src = torch.empty(0, dtype=torch.int32, device=dev)
-    copy_dst = torch.empty(0, dtype=torch.int32, device=dev)
-    qb = wl.q_bits(w)
-    q = dev_bits(qb)
-    tab_d = torch.from_numpy(tables).to(dev)
-    lens_d = torch.from_numpy(np.array(ctx, dtype=np.int32)).to(dev)
+    for op in plan.setup:
+        if op[0] == "copy":
+            pba.block_copy(pool, torch.from_numpy(op[1]).to(dev), torch.from_numpy(op[2]).to(dev))
+        else:
+            pba.kv_append(pool, torch.from_numpy(op[1]).to(dev), dev_bits(k_rows[op[2]:op[3]]),
+                          dev_bits(v_rows[op[2]:op[3]]))
+    lo, hi = plan.step_rows
+    k_step, v_step = dev_bits(k_rows[lo:hi]), dev_bits(v_rows[lo:hi])
+    del k_rows, v_rows
+    step_slots = torch.from_numpy(plan.step_slots).to(dev)
+    copy_src = torch.from_numpy(plan.step_src).to(dev)
+    copy_dst = torch.from_numpy(plan.step_dst).to(dev)
+    q = dev_bits(wl.q_bits(w))
+    B = len(plan.seq_lens)
+    tab_d = torch.from_numpy(plan.tables).to(dev)
+    lens_d = torch.from_numpy(plan.seq_lens).to(dev)
     scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    pt, n_parts = pba.paged_decode_plan(pool, Hq, B, tables.shape[1], args.partition_tokens)
-    ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, tables.shape[1], args.partition_tokens)
+    mb = plan.tables.shape[1]
+    pt, n_parts = pba.paged_decode_plan(pool, Hq, B, mb, args.partition_tokens)
+    ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, mb, args.partition_tokens)
     # Zero-filled once: the library keeps the completion counters at zero.
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
 
-    def step(ev0=None, ev1=None):
-        if not args.decode_only:
-            pba.kv_append(pool, step_slots_d, k_step, v_step, stream=stream)
-            pba.block_copy(pool, copy_src, copy_dst, stream=stream)
-        if ev0 is not None:
-            ev0.record(stream)
+    def decode():
         pba.paged_decode(pool, q, tab_d, lens_d, scale, out=out, lse=lse,
                          partition_tokens=args.partition_tokens, workspace=ws, stream=stream)
-        if ev1 is not None:
-            ev1.record(stream)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        if not args.decode_only:
+            pba.block_copy(pool, copy_src, copy_dst, stream=stream)
+            if evs is not None:
+                evs[1].record(stream)
+            pba.kv_append(pool, step_slots, k_step, v_step, stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+        decode()
+        if evs is not None:
+            evs[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
     K = args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(K):
-        step(*evs[i])
+        step(evs[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
-    dec_ms = [a.elapsed_time(b) for a, b in evs]
     ms_per_step = elapsed * 1e3 / K
-    dec_step_ms = float(np.mean(dec_ms))
+    dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    if args.decode_only:
+        copy_ms = append_ms = np.zeros(1)
+    else:
+        copy_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+        append_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     # Roofline timing of the decode kernel: K launches back to back on the same
     # stream, HIP events only at the two ends (a per-launch event pair adds its
     # own idle gap to every launch).
     b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     b0.record(stream)
     for _ in range(K):
-        pba.paged_decode(pool, q, tab_d, lens_d, scale, out=out, lse=lse,
-                         partition_tokens=args.partition_tokens, workspace=ws, stream=stream)
+        decode()
     b1.record(stream)
     torch.cuda.synchronize()
     dec_avg_ms = b0.elapsed_time(b1) / K
-    print(f"[bench] timed {K} steps: {ms_per_step * 1e3:.1f} us/step, decode in step "
-          f"{dec_step_ms * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
+    print(f"[bench] {name}: timed {K} steps: {ms_per_step * 1e3:.1f} us/step, decode in step "
+          f"{dec_ms.mean() * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
           f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); decode burst {dec_avg_ms * 1e3:.1f} us/launch",
           file=sys.stderr, flush=True)
 
-    kv_bytes, alg_bytes = decode_bytes(ctx, P, Hq, Hkv, d, esize)
-    traffic = profiled_traffic(w.name) if args.partition_tokens == 0 else None
-    step_kv_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    kv_unique, kv_logical, alg_bytes = decode_bytes(plan, sh)
+    traffic = profiled_traffic(name) if args.partition_tokens == 0 else None
+    step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg_ms * 1e-3) / 1e9
+    lens = plan.seq_lens
+    es = 2 if sh.dtype == "bf16" else 4
+    ctx = (f"context {int(lens[0])}" if lens.min() == lens.max()
+           else f"context {int(lens.min())}..{int(lens.max())} (sum {int(lens.sum())})")
     result = {
         "metric": "paged decode: KV GB/s achieved (% of HBM peak) + query rows/s at 1 GPU",
         "value": round(step_kv_gbs, 2),
@@ -223,31 +323,41 @@ def main():
         "vs_baseline": None,
         "dtype": sh.dtype,
         "data": "synthetic (seeded N(0,1) K/V/q rounded to bf16; seeded free-FIFO block placement)",
-        "config": {"workload": f"{w.name}: batch {B} x context {ctx[0]}, block_size {P}, "
-                               f"{Hq} q-heads / {Hkv} kv-heads, head_dim {d}, {sh.dtype}, "
-                               f"pool {sh.num_blocks} blocks",
-                   "batch": B, "context": ctx[0], "block_size": P, "num_q_heads": Hq,
+        "config": {"workload": f"{name}: batch {B}, {ctx}, block_size {P}, {Hq} q-heads / "
+                               f"{Hkv} kv-heads, head_dim {d}, {sh.dtype}, pool {sh.num_blocks} blocks",
+                   "batch": B, "context_min": int(lens.min()), "context_max": int(lens.max()),
+                   "context_sum": int(lens.sum()), "block_size": P, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": d, "pool_blocks": sh.num_blocks,
                    "partition_tokens": pt, "num_partitions": n_parts,
-                   "step": "kv_append(1 token/request) + block_copy(0 pairs) + paged_decode"},
+                   "step": f"block_copy({len(plan.step_src)} pairs) + kv_append("
+                           f"{len(plan.step_slots)} tokens) + paged_decode"},
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(step_kv_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_avg_ms * 1e3, 2),
-        "decode_us_in_step": round(dec_step_ms * 1e3, 2),
+        "decode_us_in_step": round(float(dec_ms.mean()) * 1e3, 2),
+        "decode_rows_per_s": round(B / (dec_avg_ms * 1e-3), 1),
+        "append_us": round(float(append_ms.mean()) * 1e3, 2),
+        "copy_us": round(float(copy_ms.mean()) * 1e3, 2),
+        "kv_unique_bytes": kv_unique,
+        "kv_logical_bytes": kv_logical,
+        "kv_logical_gbs_decode": round(kv_logical / (dec_avg_ms * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_bf16_kernel<128> (partition merge fused in)",
+                     "kernel": f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in)",
                      "algorithmic_bytes_per_launch": alg_bytes},
+        "_kv_value_bytes": kv_unique,
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, ctx, args.cpu_seconds, kv_bytes, B)
-    print(json.dumps(result), flush=True)
+    del pool, ws
+    torch.cuda.empty_cache()
+    return result
 
 
-def cpu_baseline(w, ctx, seconds, kv_bytes_total, B):
+def cpu_baseline(w, seconds, kv_bytes_total):
     """Time the CPU oracle (binary64 numpy) on a bounded sample of the same
-    workload: whole requests, all kv heads, until ~`seconds` have elapsed."""
+    workload: whole decode rows (all kv heads), in batch order, until about
+    `seconds` have elapsed.  Bytes are the same count as the GPU value, scaled by
+    the fraction of the batch done."""
     from threadpoolctl import threadpool_limits
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
@@ -264,8 +374,8 @@ def cpu_baseline(w, ctx, seconds, kv_bytes_total, B):
     scale = 1.0 / math.sqrt(w.shape.head_dim)
     print(f"[bench] cpu oracle set-up {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     Hkv = w.shape.num_kv_heads
+    B = len(w.decode)
     done_rows = 0
-    done_bytes = 0
     with threadpool_limits(limits=1):
         start = time.perf_counter()
         r = 0
@@ -273,16 +383,16 @@ def cpu_baseline(w, ctx, seconds, kv_bytes_total, B):
             att.paged_decode(opool, qb, list(ex.tables), ex.seq_lens, scale,
                              rows=[(r, h) for h in range(Hkv)])
             done_rows += 1
-            done_bytes += kv_bytes_total // B
             r = (r + 1) % B
             if time.perf_counter() - start >= seconds:
                 break
         el = time.perf_counter() - start
-    return {"value": round(done_bytes / el / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "rows_per_s": round(done_rows / el, 3),
-            "sample": f"{done_rows} whole decode rows (all {w.shape.num_q_heads} q-heads, context "
-                      f"{ctx[0]}) of the same workload, binary64 numpy oracle, 1 BLAS thread, "
-                      f"{el:.1f}s"}
+    lens = ex.seq_lens
+    return {"value": round(kv_bytes_total * done_rows / B / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "rows_per_s": round(done_rows / el, 3),
+            "sample": f"{done_rows} whole decode rows (all {w.shape.num_q_heads} q-heads; contexts "
+                      f"{int(lens.min())}..{int(lens.max())}) of the same workload, binary64 numpy "
+                      f"oracle, 1 BLAS thread, {el:.1f}s"}
 
 
 def copy_calibration(args, pba, torch, dev):

@@ -81,15 +81,13 @@ __device__ __forceinline__ float ld_state(const float* p) {
 
 // Final merge of the partition states of one (request, kv head):
 //   O = sum_p w_p u_p / L,  w_p = 2^(m_p - M),  M = max_p m_p,  L = sum_p w_p l_p,
-// partitions in index order, kMergeTile at a time with a running (M, L, O).
+// partitions in index order, TILE at a time with a running (M, L, O).
 // A thread owns four consecutive dims of one head, so it needs only that
 // head's (m, l): every load of a tile is issued before any is used and none
 // sits under a lane-dependent branch (partition indices are clamped in bounds
 // and the surplus ignored), so a tile costs one memory round trip and the
 // merge needs no LDS and no barrier.
-constexpr int kMergeTile = 8;
-
-template <int D>
+template <int D, int TILE>
 __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
   constexpr int C4 = D / 4;
   const int G = a.G;
@@ -102,11 +100,11 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
     const float* uu = a.ws_u + row * a.n_parts * D + c;
     float M = -INFINITY, L = 0.f;
     f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < np_r; p0 += kMergeTile) {
-      float mt[kMergeTile], lt[kMergeTile];
-      f32x4 ut[kMergeTile];
+    for (int p0 = 0; p0 < np_r; p0 += TILE) {
+      float mt[TILE], lt[TILE];
+      f32x4 ut[TILE];
 #pragma unroll
-      for (int j = 0; j < kMergeTile; ++j) {
+      for (int j = 0; j < TILE; ++j) {
         const int64_t pp = min(p0 + j, np_r - 1);
         mt[j] = ld_state(ml + 2 * pp);
         lt[j] = ld_state(ml + 2 * pp + 1);
@@ -115,14 +113,14 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
       }
       float Mt = M;
 #pragma unroll
-      for (int j = 0; j < kMergeTile; ++j)
+      for (int j = 0; j < TILE; ++j)
         if (p0 + j < np_r) Mt = fmaxf(Mt, mt[j]);
       if (Mt == -INFINITY) continue;  // only empty states so far: identity
       const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mt);
       L *= sc;
       O *= sc;
 #pragma unroll
-      for (int j = 0; j < kMergeTile; ++j) {
+      for (int j = 0; j < TILE; ++j) {
         if (p0 + j < np_r && mt[j] != -INFINITY) {
           const float w = fast_exp2(mt[j] - Mt);
           L += w * lt[j];
@@ -187,7 +185,14 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
                np_r - 1);
   __syncthreads();
   if (!st.last) return;
-  merge_partitions<D>(a, r, h, np_r);
+  // The tile is sized to the partition count: clamped surplus loads in a
+  // tile are real memory requests.
+  if (np_r <= 4)
+    merge_partitions<D, 4>(a, r, h, np_r);
+  else if (np_r <= 8)
+    merge_partitions<D, 8>(a, r, h, np_r);
+  else
+    merge_partitions<D, 16>(a, r, h, np_r);
   if (threadIdx.x == 0) *counter = 0;  // ready for the next call on this workspace
 }
 
@@ -256,7 +261,10 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
     vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
 }
 
-// Grid: x = partition, y = kv head, z = request.
+// Grid: x = kv head, y = request, z = partition.  Work-groups reach the
+// XCDs round-robin in linear order, so with the partition as the slowest axis
+// every XCD gets an even share of the first partitions (never empty) and of
+// the later ones (empty past a short request's end).
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
@@ -270,9 +278,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
 
   __shared__ WaveStates<D> st;
 
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int r = blockIdx.z;
+  const int h = blockIdx.x;
+  const int r = blockIdx.y;
+  const int part = blockIdx.z;
   const int lane = threadIdx.x & 63;
   // Wave-uniform (SGPR): chunk positions and block-table reads become scalar.
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -285,41 +293,48 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
                     static_cast<const uint16_t*>(vbase),
                     k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P};
 
-  // Start-up, without waiting for the request length: the length, this wave's
-  // first block-table entry, q, and the first chunk's K and V are all
-  // requested at once.  Nothing is read out of bounds whatever the length
-  // turns out to be (see chunk_blocks); the loads are simply unused when the
-  // wave has no chunk.  Issue order q, K, V keeps the in-loop waits exact.
+  // Start-up: the request length and this wave's first block-table entries
+  // come back in one scalar round trip; q and the first chunk's K and V are
+  // requested right after, and only by waves that have a chunk, so the
+  // work-groups of partitions past a short request's end, and waves past it,
+  // read nothing else.  Issue order q, K, V keeps the in-loop waits exact.
   const int T = seq_lens[r];
   int t0 = p_begin + wave * CH;
   int64_t pb0, pb1;
   chunk_blocks(pv, t0, pb0, pb1);
-  bf16x8 qf[KK];
-  {
-    // Q^T fragments (B operand of the score product): lane holds dims
-    // 32kk + 8g .. +8 of query head n; padding heads are zero.
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((int64_t)r * a.num_q_heads + (int64_t)h * G + (n < G ? n : 0)) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      u32x4 raw = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
-      if (n >= G) raw = u32x4{0u, 0u, 0u, 0u};
-      qf[kk] = __builtin_bit_cast(bf16x8, raw);
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  u32x4 kf[2][KK];
-  u32x4 vf[MT];
-  load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
-  __builtin_amdgcn_sched_barrier(0);
-  load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
-  __builtin_amdgcn_sched_barrier(0);
-
+  // The bundle fields the first loads need are fetched with the length, not
+  // after the test on it (which would add a scalar round trip).
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
+  const int num_q_heads = a.num_q_heads;
+  asm volatile("" ::"s"(qbase), "s"(num_q_heads), "s"(G), "s"(pv.v_sb), "s"(pv.v_sh));
   if (p_begin >= T) return;  // empty partition: never counted, never read
   const int p_end = min(T, p_begin + part_tokens);
   // This wave's chunks: p_begin + wave*CH + k*kWaves*CH for k < n_w.
   const int span = p_end - p_begin - wave * CH;
   const int n_w = span > 0 ? (span + kWaves * CH - 1) / (kWaves * CH) : 0;
+
+  u32x4 qraw[KK];
+  u32x4 kf[2][KK];
+  u32x4 vf[MT];
+  if (n_w > 0) {
+    // Q^T fragments (B operand of the score product): lane holds dims
+    // 32kk + 8g .. +8 of query head n (padding lanes read head 0).
+    const uint16_t* qrow =
+        qbase + ((int64_t)r * num_q_heads + (int64_t)h * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // Padding heads (n >= G) get zero queries; applied after every first load
+  // is in flight.
+  bf16x8 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8, n < G ? qraw[kk] : u32x4{0u, 0u, 0u, 0u});
 
   float m_run = -INFINITY;  // running max (log2 domain) of head n
   float l_run = 0.f;        // this lane's share of the running sum
@@ -435,9 +450,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
   __shared__ float sq[16][D];
   __shared__ float sp[kWaves][16][CH];
 
-  const int part = blockIdx.x;
-  const int h = blockIdx.y;
-  const int r = blockIdx.z;
+  const int h = blockIdx.x;
+  const int r = blockIdx.y;
+  const int part = blockIdx.z;
 
   const int T = a.seq_lens[r];
   const int p_begin = part * a.part_tokens;
@@ -554,11 +569,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
 }
 
 hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream) {
-  // Requests go on the grid's z axis, at most kMaxGridZ per launch; a larger
+  // Requests go on the grid's y axis, at most kMaxGridY per launch; a larger
   // batch is launched in slices whose per-request pointers are offset.
-  constexpr int kMaxGridZ = 65535;
-  for (int r0 = 0; r0 < a.batch; r0 += kMaxGridZ) {
-    const int nb = min(a.batch - r0, kMaxGridZ);
+  constexpr int kMaxGridY = 65535;
+  for (int r0 = 0; r0 < a.batch; r0 += kMaxGridY) {
+    const int nb = min(a.batch - r0, kMaxGridY);
     DecodeArgs s = a;
     const int64_t rows = (int64_t)r0 * a.num_q_heads;
     s.q = static_cast<const char*>(a.q) + rows * head_dim * (dtype == PBA_BF16 ? 2 : 4);
@@ -570,7 +585,7 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     s.ws_u = a.ws_u ? a.ws_u + rows * a.n_parts * head_dim : nullptr;
     s.counters = a.counters ? a.counters + (int64_t)r0 * a.num_kv_heads : nullptr;
     s.batch = nb;
-    const dim3 grid((unsigned)a.n_parts, (unsigned)a.num_kv_heads, (unsigned)nb);
+    const dim3 grid((unsigned)a.num_kv_heads, (unsigned)nb, (unsigned)a.n_parts);
     const dim3 block(kDecodeThreads);
     if (dtype == PBA_BF16) {
       auto kern = head_dim == 128 ? decode_bf16_kernel<128> : decode_bf16_kernel<64>;

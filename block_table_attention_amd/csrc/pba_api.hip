@@ -60,7 +60,7 @@ int check_pool(const pba_kv_pool* pool) {
 
 // Shape checks shared by the decode entry points (pool checked first).  The
 // decode kernel takes the K strides as int32 and the kv heads on a grid axis
-// of at most 65535.
+// (at most 65535; the partitions, checked by the planner, likewise).
 int check_decode_shape(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
                        int32_t max_blocks_per_seq) {
   const int st = check_pool(pool);
@@ -122,7 +122,8 @@ int plan_partitions(const pba_kv_pool* pool, int32_t batch, int32_t max_blocks, 
     pt = (per + granule - 1) / granule * granule;
   }
   const int64_t np = (max_T + pt - 1) / pt;
-  if (pt > INT32_MAX || np > INT32_MAX) return PBA_ERR_UNSUPPORTED;
+  // Partitions go on a grid axis of at most 65535.
+  if (pt > INT32_MAX || np > 65535) return PBA_ERR_UNSUPPORTED;
   *part_tokens = (int32_t)pt;
   *n_parts = (int32_t)np;
   return PBA_OK;

@@ -158,19 +158,58 @@ def test_validate_flag_roundtrip():
     assert pba.set_validate(False) is True
 
 
-def test_bench_fresh_layout_matches_oracle_allocator():
-    """bench.py builds tables itself (the caller's allocator for a fresh pool);
-    they must equal what the oracle allocator hands out for the same script."""
+@pytest.mark.parametrize("name", ["long16k", "batch32", "shared_prefix", "lognormal_p64", "tiny"])
+def test_bench_plan_matches_oracle_allocator(name):
+    """bench.py runs each workload script through the package's BlockManager;
+    the tables, lengths, setup calls and step calls must be exactly the
+    oracle allocator's trace for the same script (same slots, same copy pairs,
+    same K/V rows), and the byte counts must follow from the tables."""
     import numpy as np
 
     import bench
-    import workloads as wl
     from harness import execute
 
-    w = wl.long_context(3, 1000, num_blocks=64, block_size=64)
+    w = bench.make_workload(name)
+    plan = bench.plan_script(w)
     ex = execute(w)
-    prefill = [a[2] for a in w.actions if a[0] == "prefill"]
-    tables = bench.fresh_pool_layout(wl.fifo_order(w), [T + 1 for T in prefill], 64)
-    assert np.array_equal(tables, ex.tables)
-    slots = bench.slots_for(tables, 1, np.arange(5), 64)
-    assert slots.tolist() == [int(ex.tables[1, 0]) * 64 + i for i in range(5)]
+    assert np.array_equal(plan.tables, ex.tables)
+    assert np.array_equal(plan.seq_lens, ex.seq_lens)
+    assert plan.n_writes == ex.n_writes
+    # Flatten both traces to (kind, payload) in program order.
+    mine = []
+    for op in plan.setup:
+        if op[0] == "copy":
+            mine += [("copy", int(s), int(d)) for s, d in zip(op[1], op[2])]
+        else:
+            mine += [("write", int(s), r) for s, r in zip(op[1], range(op[2], op[3]))]
+    lo, hi = plan.step_rows
+    assert hi - lo == len(plan.step_slots)
+    step = [("copy", int(s), int(d)) for s, d in zip(plan.step_src, plan.step_dst)]
+    step += [("write", int(s), r) for s, r in zip(plan.step_slots, range(lo, hi))]
+    theirs = []
+    for op in ex.ops:
+        if op[0] == "copy":
+            theirs += [("copy", int(s), int(d)) for s, d in zip(op[1], op[2])]
+        else:
+            theirs += [("write", int(s), r) for s, r in zip(op[1], range(op[2], op[3]))]
+    # The step batches its copies ahead of its writes; the oracle interleaves
+    # them per request.  Same multiset, and every copy precedes the writes
+    # into its destination block in both.
+    n_setup = len(mine)
+    assert theirs[:n_setup] == mine
+    assert sorted(theirs[n_setup:]) == sorted(step)
+    P = w.shape.block_size
+    # Batching is exact only if no step write lands in a block a step copy
+    # reads (a copy then sees the same bytes in either order).
+    src_blocks = {c[1] for c in step if c[0] == "copy"}
+    assert all(op[1] // P not in src_blocks for op in step if op[0] == "write")
+    kv_unique, kv_logical, alg = bench.decode_bytes(plan, w.shape)
+    es = 2 if w.shape.dtype == "bf16" else 4
+    row = w.shape.num_kv_heads * w.shape.head_dim * 2 * es
+    assert kv_logical == int(ex.seq_lens.sum()) * row
+    assert kv_unique <= kv_logical
+    if name != "shared_prefix":
+        assert kv_unique == kv_logical
+    else:
+        # The 2000-token prefix is read once by the 128 rows that map it.
+        assert kv_logical - kv_unique >= 2000 * 127 * row

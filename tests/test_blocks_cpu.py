@@ -1,0 +1,158 @@
+"""The package's caller-side BlockManager against the oracle allocator.
+
+Both follow the same rules (free FIFO, reference counts, fork, the three append
+paths); given the same FIFO start they must produce identical tables, slots,
+copy pairs and free lists for any script.  The bench executes workload scripts
+with BlockManager, so this pins the bench's inputs to the oracle's.
+"""
+import copy
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from block_table_attention_amd.blocks import BlockManager, OutOfBlocks
+from oracle.allocator import BlockAllocator, OutOfBlocks as OracleOut
+
+
+def _state(m: BlockManager, rids):
+    return (tuple(m._free), tuple(int(x) for x in m._ref),
+            tuple((r, tuple(m.table(r)), m.length(r)) for r in rids))
+
+
+def _oracle_state(a: BlockAllocator, rids):
+    return (tuple(a.free), tuple(a.ref), tuple((r, tuple(a.table(r)), a.length(r)) for r in rids))
+
+
+def _run_both(w: wl.Workload):
+    order = wl.fifo_order(w)
+    a = BlockAllocator(w.shape.num_blocks, w.shape.block_size, free_order=order)
+    m = BlockManager(w.shape.num_blocks, w.shape.block_size, free_order=order)
+    for act in w.actions:
+        if act[0] == "new":
+            assert a.new_request() == m.new_request()
+        elif act[0] in ("prefill", "append"):
+            rid = act[1]
+            n = act[2] if act[0] == "prefill" else 1
+            before = len(a.trace)
+            a.prefill(rid, n)
+            ops = a.trace[before:]
+            slots, copies = m.append(rid, n)
+            assert [op[1:] for op in ops if op[0] == "copy"] == copies
+            assert [op[3] for op in ops if op[0] == "write"] == slots.tolist()
+            # Copies come before the first write of the call.
+            if copies:
+                assert ops[0][0] == "copy"
+        elif act[0] == "fork":
+            assert a.fork(act[1]) == m.fork(act[1])
+        elif act[0] == "release":
+            a.release(act[1])
+            m.release(act[1])
+    live = sorted(a.tables)
+    assert _oracle_state(a, live) == _state(m, live)
+    np.testing.assert_array_equal(
+        m.block_tables(w.decode),
+        np.array([a.table(r) + [-1] * (max(len(a.table(x)) for x in w.decode) - len(a.table(r)))
+                  for r in w.decode], dtype=np.int32))
+    np.testing.assert_array_equal(m.seq_lens(w.decode), [a.length(r) for r in w.decode])
+    return a, m
+
+
+@pytest.mark.parametrize("make", [
+    wl.tiny,
+    wl.batch32,
+    lambda: wl.shared_prefix(children=16),
+    lambda: wl.shared_prefix(prefix=37, children=5, lo=1, hi=40, num_blocks=64),
+    lambda: wl.lognormal(16, batch=32),
+    lambda: wl.lognormal(256, batch=32),
+], ids=["tiny", "batch32", "shared_prefix16", "shared_prefix_small", "lognormal16", "lognormal256"])
+def test_workload_scripts_match_oracle(make):
+    _run_both(make())
+
+
+def test_shared_prefix_step_copies():
+    """Every sibling's divergent append copies the shared tail exactly when the
+    child's length is not a multiple of P (the pages' boundary rule)."""
+    w = wl.shared_prefix(children=16)
+    _, m = _run_both(w)
+    kids = w.decode[:16]
+    sibs = w.decode[16:]
+    for k, s in zip(kids, sibs):
+        tk, ts = m.table(k), m.table(s)
+        T = m.length(k)
+        assert m.length(s) == T + 1
+        if T % 16:
+            assert ts[:-1] == tk[:-1] and ts[-1] != tk[-1]
+        else:
+            assert ts[:-1] == tk and len(ts) == len(tk) + 1
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_scripts(seed):
+    """Random new / fork / release / multi-token appends on a tiny pool, with
+    out-of-blocks failures that must leave the state unchanged."""
+    rng = np.random.default_rng(1000 + seed)
+    nb, P = 10, 4
+    order = rng.permutation(nb)
+    a = BlockAllocator(nb, P, free_order=order)
+    m = BlockManager(nb, P, free_order=order)
+    live = []
+    for _ in range(60):
+        op = rng.integers(0, 10)
+        if op == 0 or not live:
+            assert a.new_request() == m.new_request()
+            live.append(m._next_rid - 1)
+        elif op == 1:
+            r = live[rng.integers(len(live))]
+            assert a.fork(r) == m.fork(r)
+            live.append(m._next_rid - 1)
+        elif op == 2 and len(live) > 1:
+            r = live.pop(rng.integers(len(live)))
+            a.release(r)
+            m.release(r)
+        else:
+            r = live[rng.integers(len(live))]
+            n = int(rng.integers(0, 7))
+            snap = _state(m, live)
+            try:
+                slots, copies = m.append(r, n)
+            except OutOfBlocks:
+                assert _state(m, live) == snap
+                # The oracle runs out too on the same tokens (it may have
+                # written some of them first, so it runs on a copy).
+                with pytest.raises(OracleOut):
+                    copy.deepcopy(a).prefill(r, n)
+                continue
+            before = len(a.trace)
+            a.prefill(r, n)
+            ops = a.trace[before:]
+            assert [op[1:] for op in ops if op[0] == "copy"] == copies
+            assert [op[3] for op in ops if op[0] == "write"] == slots.tolist()
+        a.check_invariants()
+        assert _oracle_state(a, live) == _state(m, live)
+
+
+def test_out_of_blocks_is_atomic():
+    m = BlockManager(3, 4)
+    r = m.new_request()
+    m.append(r, 8)                       # two blocks
+    c = m.fork(r)
+    snap = _state(m, [r, c])
+    with pytest.raises(OutOfBlocks):
+        m.append(c, 5)                   # 8 -> 13 tokens needs 2 more blocks, 1 free
+    assert _state(m, [r, c]) == snap
+    slots, copies = m.append(c, 4)       # exactly one fresh block
+    assert copies == [] and len(slots) == 4
+
+
+def test_block_tables_padding():
+    m = BlockManager(8, 16)
+    a, b = m.new_request(), m.new_request()
+    m.append(a, 40)
+    m.append(b, 1)
+    t = m.block_tables([a, b])
+    assert t.shape == (2, 3) and t.dtype == np.int32
+    assert (t[1, 1:] == -1).all()
+    assert m.block_tables([a, b], width=5).shape == (2, 5)
+    with pytest.raises(ValueError):
+        m.block_tables([a, b], width=2)
