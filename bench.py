@@ -51,11 +51,16 @@ def parse():
     ap.add_argument("--workload", default="long16k", choices=WORKLOADS)
     ap.add_argument("--sweep", action="store_true",
                     help="every workload in turn, one JSON line each (no cpu_baseline)")
-    ap.add_argument("--partition-tokens", type=int, default=0)
+    ap.add_argument("--partition-tokens", type=int, default=-1,
+                    help="decode partition length; 0 = the library's plan; default: chosen "
+                         "from the batch's lengths by blocks.suggest_partition_tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call (profiling runs)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay the step as a HIP graph (measured slower than eager launches "
+                         "for these steps on ROCm 7.2)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="instead of the benchmark, run block_copy over this many MiB "
                          "(a plain copy of known size for counter calibration)")
@@ -243,44 +248,66 @@ def run_workload(args, name, pba, torch, dev):
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
     mb = plan.tables.shape[1]
-    pt, n_parts = pba.paged_decode_plan(pool, Hq, B, mb, args.partition_tokens)
-    ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, mb, args.partition_tokens)
+    # The bench is the caller: it knows the lengths and may pick the split.
+    req_pt = args.partition_tokens
+    if req_pt < 0:
+        from block_table_attention_amd.blocks import suggest_partition_tokens
+        req_pt = suggest_partition_tokens(plan.seq_lens, Hkv)
+    pt, n_parts = pba.paged_decode_plan(pool, Hq, B, mb, req_pt)
+    ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, mb, req_pt)
     # Zero-filled once: the library keeps the completion counters at zero.
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
-    def decode():
+    def decode(st=stream):
         pba.paged_decode(pool, q, tab_d, lens_d, scale, out=out, lse=lse,
-                         partition_tokens=args.partition_tokens, workspace=ws, stream=stream)
+                         partition_tokens=req_pt, workspace=ws, stream=st)
 
-    def step(evs=None):
+    def step(evs=None, st=stream):
         if evs is not None:
-            evs[0].record(stream)
+            evs[0].record(st)
         if not args.decode_only:
-            pba.block_copy(pool, copy_src, copy_dst, stream=stream)
+            pba.block_copy(pool, copy_src, copy_dst, stream=st)
             if evs is not None:
-                evs[1].record(stream)
-            pba.kv_append(pool, step_slots, k_step, v_step, stream=stream)
+                evs[1].record(st)
+            pba.kv_append(pool, step_slots, k_step, v_step, stream=st)
         if evs is not None:
-            evs[2].record(stream)
-        decode()
+            evs[2].record(st)
+        decode(st)
         if evs is not None:
-            evs[3].record(stream)
+            evs[3].record(st)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
     K = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    # The timed steps: K eager steps with no events inside, or with --graph one
+    # HIP graph of the whole step (copy, append, decode) replayed K times.
+    use_graph = args.graph and not args.decode_only
+    if use_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(st=None)
+        graph.replay()
+        torch.cuda.synchronize()
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(K):
-        step(evs[i])
+    for _ in range(K):
+        if use_graph:
+            graph.replay()
+        else:
+            step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t_start
     ms_per_step = elapsed * 1e3 / K
+    # Per-call breakdown: K eager steps with events between the calls (the
+    # events add their own small gaps, so this pass is not the step time).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
     dec_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
     if args.decode_only:
         copy_ms = append_ms = np.zeros(1)
@@ -297,13 +324,14 @@ def run_workload(args, name, pba, torch, dev):
     b1.record(stream)
     torch.cuda.synchronize()
     dec_avg_ms = b0.elapsed_time(b1) / K
-    print(f"[bench] {name}: timed {K} steps: {ms_per_step * 1e3:.1f} us/step, decode in step "
+    print(f"[bench] {name}: timed {K} steps ({'graph' if use_graph else 'eager'}): "
+          f"{ms_per_step * 1e3:.1f} us/step, decode in eager step "
           f"{dec_ms.mean() * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
           f"p90 {np.percentile(dec_ms, 90) * 1e3:.1f}); decode burst {dec_avg_ms * 1e3:.1f} us/launch",
           file=sys.stderr, flush=True)
 
     kv_unique, kv_logical, alg_bytes = decode_bytes(plan, sh)
-    traffic = profiled_traffic(name) if args.partition_tokens == 0 else None
+    traffic = profiled_traffic(name) if args.partition_tokens < 0 else None
     step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg_ms * 1e-3) / 1e9
     lens = plan.seq_lens
@@ -329,8 +357,11 @@ def run_workload(args, name, pba, torch, dev):
                    "context_sum": int(lens.sum()), "block_size": P, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": d, "pool_blocks": sh.num_blocks,
                    "partition_tokens": pt, "num_partitions": n_parts,
+                   "partition_choice": "library plan" if req_pt == 0 else
+                   ("caller (suggest_partition_tokens)" if args.partition_tokens < 0 else "fixed"),
                    "step": f"block_copy({len(plan.step_src)} pairs) + kv_append("
-                           f"{len(plan.step_slots)} tokens) + paged_decode"},
+                           f"{len(plan.step_slots)} tokens) + paged_decode",
+                   "step_launch": "HIP graph replay" if use_graph else "eager"},
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(step_kv_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_avg_ms * 1e3, 2),

@@ -144,3 +144,28 @@ class BlockManager:
         self._ref[b] -= 1
         if self._ref[b] == 0:
             self._free.append(b)
+
+
+def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 256) -> int:
+    """A partition length for ``paged_decode`` chosen from the lengths the
+    caller knows (the library sees only the table width and the batch).
+
+    Returns 0 (the library's own plan) unless the batch already gives every
+    CU a (request, kv head) of its own and its longest request is far above
+    the mean; then the long requests are cut near twice the mean length, so
+    that they stop setting the kernel's duration while the short ones keep a
+    single partition.  Measured on MI355X: a lognormal batch of 128 requests
+    (median 100, max 8192 tokens) decodes in 62 us with 1024-token partitions
+    against 102 us unsplit; uniform or mildly ragged batches are fastest
+    unsplit.
+    """
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    if lens.size == 0 or lens.size * num_kv_heads < num_cus:
+        return 0
+    mean = float(lens.mean())
+    longest = int(lens.max())
+    if longest <= 4 * mean:
+        return 0
+    pt = int(-(-int(2 * mean) // 256) * 256)
+    pt = max(512, pt)
+    return 0 if pt >= longest else pt

@@ -82,8 +82,10 @@ __device__ __forceinline__ float ld_state(const float* p) {
 // Final merge of the partition states of one (request, kv head):
 //   O = sum_p w_p u_p / L,  w_p = 2^(m_p - M),  M = max_p m_p,  L = sum_p w_p l_p,
 // partitions in index order, TILE at a time with a running (M, L, O).
-// A thread owns four consecutive dims of one head, so it needs only that
-// head's (m, l): every load of a tile is issued before any is used and none
+// A thread owns dims j, j + D/4, j + D/2, j + 3D/4 of one head, so it needs
+// only that head's (m, l), and each load or store instruction of a wave covers
+// whole runs of consecutive dims.  Every load of a tile is issued before any
+// is used and none
 // sits under a lane-dependent branch (partition indices are clamped in bounds
 // and the surplus ignored), so a tile costs one memory round trip and the
 // merge needs no LDS and no barrier.
@@ -94,7 +96,7 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
   const int64_t row0 = (int64_t)r * a.num_q_heads + (int64_t)h * G;
   for (int idx = threadIdx.x; idx < G * C4; idx += kDecodeThreads) {
     const int n = idx / C4;
-    const int c = 4 * (idx - n * C4);
+    const int c = idx - n * C4;  // dims c + C4 * e, e < 4
     const int64_t row = row0 + n;
     const float* ml = a.ws_ml + row * a.n_parts * 2;
     const float* uu = a.ws_u + row * a.n_parts * D + c;
@@ -109,7 +111,7 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
         mt[j] = ld_state(ml + 2 * pp);
         lt[j] = ld_state(ml + 2 * pp + 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(uu + pp * D + e);
+        for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(uu + pp * D + C4 * e);
       }
       float Mt = M;
 #pragma unroll
@@ -130,7 +132,8 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
       M = Mt;
     }
     const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(a.out + row * D + c) = res;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) a.out[row * D + c + C4 * e] = res[e];
     if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
   }
 }
@@ -145,7 +148,7 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
   const int np_r = (T + a.part_tokens - 1) / a.part_tokens;
   for (int idx = threadIdx.x; idx < G * C4; idx += kDecodeThreads) {
     const int n = idx / C4;
-    const int c = 4 * (idx - n * C4);
+    const int c = idx - n * C4;  // dims c + C4 * e, e < 4
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, st.m[w][n]);
@@ -158,18 +161,20 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
         if (mw == -INFINITY) continue;  // a wave that saw no chunk: identity
         const float wt = fast_exp2(mw - M);
         L += wt * st.l[w][n];
-        O += wt * *reinterpret_cast<const f32x4*>(&st.o[w][n][c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] += wt * st.o[w][n][c + C4 * e];
       }
     }
     const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
     if (np_r == 1) {
       const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(a.out + row * D + c) = res;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.out[row * D + c + C4 * e] = res[e];
       if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
     } else {
       const int64_t prow = row * a.n_parts + part;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st_state(a.ws_u + prow * D + c + e, O[e]);
+      for (int e = 0; e < 4; ++e) st_state(a.ws_u + prow * D + c + C4 * e, O[e]);
       if (c == 0) {
         st_state(a.ws_ml + prow * 2 + 0, M);
         st_state(a.ws_ml + prow * 2 + 1, L);

@@ -288,7 +288,7 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   const int G = num_q_heads / pool->num_kv_heads;
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
-  if (!aligned16(q) || !aligned16(out)) return PBA_ERR_UNSUPPORTED;
+  if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
   int32_t pt = 0, np = 0;
   st = plan_partitions(pool, batch, max_blocks_per_seq, partition_tokens, &pt, &np);
   if (st) return st;

@@ -139,7 +139,7 @@ int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* d
  *   seq_lens      device int32 [batch]; 1 <= T <= max_blocks_per_seq * P
  *                 (validate mode: PBA_ERR_OUT_OF_RANGE)
  *   scale         score scale, normally 1/sqrt(head_dim)
- *   out           device float32 [batch, num_q_heads, head_dim], 16-byte aligned
+ *   out           device float32 [batch, num_q_heads, head_dim]
  *   lse           device float32 [batch, num_q_heads], or NULL
  *   partition_tokens  0: the library splits each row into partitions of its
  *                 choice (sized so that all work-groups are resident at once);

@@ -104,9 +104,9 @@ def test_decode_shape_rejections():
     need = lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, 2, 64, 256)
     assert call(8, 64, 256, 0x80000, need - 1) == -5
     assert call(8, 64, 256, 0x80008, need) == -5  # misaligned workspace
-    # The output takes 16-byte stores.
-    assert lib.pba_paged_decode(ctypes.byref(d), 0x30000, 8, 0x40000, 4, 0x50000, 2,
-                                ctypes.c_float(0.1), 0x60004, NULL, 0, NULL, 0, NULL) == -4
+    # q is read in 16-byte pieces.
+    assert lib.pba_paged_decode(ctypes.byref(d), 0x30008, 8, 0x40000, 4, 0x50000, 2,
+                                ctypes.c_float(0.1), 0x60000, NULL, 0, NULL, 0, NULL) == -4
 
 
 def test_decode_stride_limit():

@@ -272,3 +272,83 @@ def test_workspace_counters_reset_between_calls(pba, gpu):
     assert torch.equal(outs[0], outs[2]) and torch.equal(outs[0], outs[4])
     n_counters = B * base.shape.num_kv_heads
     assert torch.count_nonzero(ws[:4 * n_counters]).item() == 0
+
+
+def test_graph_replay_matches_eager(pba, gpu):
+    """The decode step (block_copy -> kv_append -> paged_decode with a split
+    and its fused merge) captured in a HIP graph.  Every replay, with eager
+    library calls and synchronisations between replays, must equal the eager
+    step bit for bit (pool bytes, out, lse), and the oracle within TOL.  No
+    call of the step records a memset: the workspace counters return to zero
+    inside the kernel."""
+    import bench
+
+    w = wl.shared_prefix(children=6, prefix=300, lo=3, hi=40, num_blocks=160)
+    say("graph replay", w.shape, "seed", w.seed)
+    plan = bench.plan_script(w)
+    assert len(plan.step_src) > 0 and len(plan.step_slots) == 6
+    ex = execute(w)
+    k_rows, v_rows = wl.kv_rows(w, ex.n_writes)
+    opool = oracle_pool(ex, k_rows, v_rows)
+    dt = w.shape.dtype
+    kd, vd = to_device(k_rows, dt, gpu), to_device(v_rows, dt, gpu)
+    k0, v0 = wl.pool_poison(w)
+    pools = [pba.KVPool(to_device(k0, dt, gpu), to_device(v0, dt, gpu)) for _ in range(2)]
+    for pool in pools:
+        for op in plan.setup:
+            if op[0] == "copy":
+                pba.block_copy(pool, torch.from_numpy(op[1]).to(gpu), torch.from_numpy(op[2]).to(gpu))
+            else:
+                pba.kv_append(pool, torch.from_numpy(op[1]).to(gpu), kd[op[2]:op[3]], vd[op[2]:op[3]])
+    lo, hi = plan.step_rows
+    slots = torch.from_numpy(plan.step_slots).to(gpu)
+    src = torch.from_numpy(plan.step_src).to(gpu)
+    dst = torch.from_numpy(plan.step_dst).to(gpu)
+    q = to_device(wl.q_bits(w), dt, gpu)
+    tables = torch.from_numpy(plan.tables).to(gpu)
+    lens = torch.from_numpy(plan.seq_lens).to(gpu)
+    B, Hq, D = q.shape
+    pt = 256
+    ws_bytes = pba.paged_decode_workspace_bytes(pools[0], Hq, B, plan.tables.shape[1], pt)
+    assert ws_bytes > 0
+    bufs = [dict(out=torch.empty((B, Hq, D), dtype=torch.float32, device=gpu),
+                 lse=torch.empty((B, Hq), dtype=torch.float32, device=gpu),
+                 ws=torch.zeros(ws_bytes, dtype=torch.uint8, device=gpu)) for _ in range(2)]
+
+    def step(pool, b):
+        pba.block_copy(pool, src, dst)
+        pba.kv_append(pool, slots, kd[lo:hi], vd[lo:hi])
+        pba.paged_decode(pool, q, tables, lens, out=b["out"], lse=b["lse"], partition_tokens=pt,
+                         workspace=b["ws"])
+
+    pba.set_validate(False)
+    try:
+        step(pools[0], bufs[0])                    # eager reference
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(pools[1], bufs[1])                # warm the graph's buffers once
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(pools[1], bufs[1])
+        for rep in range(3):
+            bufs[1]["out"].fill_(float("nan"))
+            bufs[1]["lse"].fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(bufs[1]["out"], bufs[0]["out"]), rep
+            assert torch.equal(bufs[1]["lse"], bufs[0]["lse"]), rep
+            assert torch.equal(pools[1].k.view(torch.int16), pools[0].k.view(torch.int16)), rep
+            assert torch.equal(pools[1].v.view(torch.int16), pools[0].v.view(torch.int16)), rep
+            assert torch.count_nonzero(bufs[1]["ws"][:4 * B * w.shape.num_kv_heads]).item() == 0
+            step(pools[0], bufs[0])                # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        pba.set_validate(True)
+    assert np.array_equal(to_bits(pools[1].k), opool.k) and np.array_equal(to_bits(pools[1].v), opool.v)
+    ref, ref_lse = att.paged_decode(opool, wl.q_bits(w), list(ex.tables), ex.seq_lens,
+                                    1 / math.sqrt(D))
+    assert np.max(np.abs(bufs[1]["out"].cpu().numpy() - ref)) <= TOL
