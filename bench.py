@@ -160,6 +160,18 @@ def decode_bytes(plan: Plan, shape):
     return kv_unique, kv_logical, kv_unique + q + out + tbl
 
 
+def table_ledger(plan: Plan, P: int) -> dict:
+    """Block-size accounting of the decode batch: tail slots (allocated but
+    past T), and dense versus used block-table cells."""
+    lens = plan.seq_lens.astype(np.int64)
+    blocks = -(-lens // P)
+    tail = int((blocks * P - lens).sum())
+    return {"blocks_mapped": int(blocks.sum()), "tail_slots": tail,
+            "tail_fraction": round(tail / float((blocks * P).sum()), 4),
+            "table_cells_dense": int(len(lens) * plan.tables.shape[1]),
+            "table_cells_used": int(blocks.sum())}
+
+
 def profiled_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 summary, or None
     when there is none for this workload or the decode source changed since."""
@@ -372,6 +384,7 @@ def run_workload(args, name, pba, torch, dev):
         "kv_unique_bytes": kv_unique,
         "kv_logical_bytes": kv_logical,
         "kv_logical_gbs_decode": round(kv_logical / (dec_avg_ms * 1e-3) / 1e9, 2),
+        "ledger": table_ledger(plan, P),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,

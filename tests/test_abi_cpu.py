@@ -213,3 +213,22 @@ def test_bench_plan_matches_oracle_allocator(name):
     else:
         # The 2000-token prefix is read once by the 128 rows that map it.
         assert kv_logical - kv_unique >= 2000 * 127 * row
+
+
+@pytest.mark.parametrize("name", ["lognormal_p16", "lognormal_p64", "lognormal_p256", "batch32"])
+def test_bench_ledger_matches_oracle(name):
+    """The bench's block-size accounting equals the oracle's ledgers (request
+    view tail slots, dense and used table cells) for the same decode batch."""
+    import bench
+    from oracle import ledgers
+
+    w = bench.make_workload(name)
+    plan = bench.plan_script(w)
+    P = w.shape.block_size
+    got = bench.table_ledger(plan, P)
+    lens = [int(T) for T in plan.seq_lens]
+    view = ledgers.request_view_ledger(lens, P)
+    cells = ledgers.table_cells(lens, P)
+    assert got["tail_slots"] == view["tail_slots"]
+    assert got["blocks_mapped"] == view["refs"] == cells["used"]
+    assert got["table_cells_dense"] == cells["table"]
