@@ -17,6 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_plan",
+           "paged_decode_shared", "paged_decode_shared_workspace_bytes", "SharedPlan",
            "paged_decode_workspace_bytes", "decode_workspace", "set_validate", "PBAError", "lib_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -50,8 +51,15 @@ class PoolDesc(ctypes.Structure):
                 ("v_stride_head", ctypes.c_int64)]
 
 
+class SharedPlanDesc(ctypes.Structure):
+    _fields_ = [("num_items", ctypes.c_int32), ("max_slots", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("items", ctypes.c_void_p), ("row_private", ctypes.c_void_p)]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _P = ctypes.POINTER(PoolDesc)
+_SP = ctypes.POINTER(SharedPlanDesc)
 _SIGS = {
     "pba_kv_append": (ctypes.c_int, [_P, _vp, _i64, _vp, _vp, _vp]),
     "pba_block_copy": (ctypes.c_int, [_P, _vp, _vp, _i64, _vp]),
@@ -60,6 +68,9 @@ _SIGS = {
     "pba_paged_decode_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _i32]),
     "pba_paged_decode_plan": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "pba_paged_decode_shared_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _SP]),
+    "pba_paged_decode_shared": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float,
+                                               _vp, _vp, _SP, _vp, _sz, _vp]),
     "pba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pba_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pba_version": (ctypes.c_int, []),
@@ -253,6 +264,90 @@ def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
         pool._ref, q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks, seq_lens.data_ptr(), B,
         ctypes.c_float(scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
         partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+    return out, lse
+
+
+@dataclass(frozen=True)
+class SharedPlan:
+    """A shared-prefix plan on the device (see ``blocks.shared_plan`` for how a
+    caller builds one from its block tables): chunk-first items int32
+    [n, 8] and each row's private range int32 [B, 2]."""
+
+    items: torch.Tensor
+    row_private: torch.Tensor
+    max_slots: int
+    partition_tokens: int
+
+    def __post_init__(self):
+        dev = self.row_private.device
+        _require(self.row_private, "row_private", torch.int32, dev, 2)
+        _require(self.items, "items", torch.int32, dev, 2)
+        if self.items.shape[1] != 8 or self.row_private.shape[1] != 2:
+            raise ValueError("items must be [n, 8] and row_private [B, 2]")
+        desc = SharedPlanDesc(self.items.shape[0], self.max_slots, self.partition_tokens, 0,
+                              self.items.data_ptr() if self.items.numel() else None,
+                              self.row_private.data_ptr())
+        object.__setattr__(self, "_desc", desc)
+        object.__setattr__(self, "_ref", ctypes.byref(desc))
+
+    @classmethod
+    def from_host(cls, host, device) -> "SharedPlan":
+        """From a ``blocks.HostSharedPlan`` (numpy arrays)."""
+        items = torch.from_numpy(host.items).to(device)
+        if items.numel() == 0:
+            items = torch.zeros((0, 8), dtype=torch.int32, device=device)
+        return cls(items, torch.from_numpy(host.row_private).to(device), host.max_slots,
+                   host.partition_tokens)
+
+
+def paged_decode_shared_workspace_bytes(pool: KVPool, num_q_heads: int, batch: int,
+                                        max_blocks_per_seq: int, plan: SharedPlan) -> int:
+    return int(_lib.pba_paged_decode_shared_workspace_bytes(pool._ref, num_q_heads, batch,
+                                                            max_blocks_per_seq, plan._ref))
+
+
+def paged_decode_shared(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
+                        seq_lens: torch.Tensor, plan: SharedPlan, scale: Optional[float] = None,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        want_lse: bool = True, workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    """paged_decode with shared-prefix execution reuse: same arguments and
+    results, the plan in place of ``partition_tokens``.  A caller supplied
+    workspace must be zero-filled before its first use."""
+    dev = pool.k.device
+    _require(q, "q", pool.dtype, dev, 3)
+    _require(block_tables, "block_tables", torch.int32, dev, 2)
+    _require(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, block_tables, seq_lens and the pool")
+    if plan.row_private.shape[0] != B:
+        raise ValueError("the plan describes another batch")
+    max_blocks = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    else:
+        _require(out, "out", torch.float32, dev, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _require(lse, "lse", torch.float32, dev, 2)
+    if workspace is None and B > 0:
+        need = paged_decode_shared_workspace_bytes(pool, Hq, B, max_blocks, plan)
+        if need:
+            key = (dev, _stream(stream), need)
+            workspace = _WORKSPACES.get(key)
+            if workspace is None:
+                workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
+                _WORKSPACES[key] = workspace
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pba_paged_decode_shared", _lib.pba_paged_decode_shared(
+        pool._ref, q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks, seq_lens.data_ptr(), B,
+        ctypes.c_float(scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        plan._ref, ws_ptr, ws_bytes, _stream(stream)))
     return out, lse
 
 

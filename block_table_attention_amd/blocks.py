@@ -26,6 +26,7 @@ cannot get the blocks it needs raises ``OutOfBlocks`` and changes nothing.
 from __future__ import annotations
 
 from collections import deque
+from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
@@ -169,3 +170,112 @@ def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus
     pt = int(-(-int(2 * mean) // 256) * 256)
     pt = max(512, pt)
     return 0 if pt >= longest else pt
+
+
+# ---------------------------------------------------------------------------
+# Shared-prefix execution plans ("M5.3", 0x0BB-0x0BE)
+# ---------------------------------------------------------------------------
+def sharing_order(tables: np.ndarray) -> np.ndarray:
+    """A batch order in which rows that map the same leading blocks are
+    adjacent (lexicographic order of the block tables), so that each shared
+    chunk covers one contiguous range of rows."""
+    t = np.asarray(tables)
+    return np.lexsort(t.T[::-1]).astype(np.int64)
+
+
+def shared_chunks(tables: np.ndarray, seq_lens: Sequence[int], block_size: int,
+                  threshold: int = 1):
+    """Chunks of a batch, in tree pre-order, and each row's first private token.
+
+    A chunk (row_begin, row_end, tok_begin, tok_end) is a maximal run of whole,
+    fully visible blocks that every row of [row_begin, row_end) maps to the same
+    physical ids, below the chunks of its ancestors; only runs covering more
+    than ``threshold`` rows become chunks (0x0BD's coverage threshold).  Rows
+    sharing leading blocks must be adjacent (see ``sharing_order``).
+    """
+    t = np.asarray(tables)
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    P = block_size
+    full = lens // P                         # whole blocks each row can see
+    B = len(lens)
+    chunks = []
+    private = np.zeros(B, dtype=np.int64)
+
+    def visit(a: int, b: int, j0: int) -> None:
+        if b - a <= threshold:
+            private[a:b] = j0 * P
+            return
+        lim = int(full[a:b].min())
+        j = j0
+        while j < lim and bool((t[a:b, j] == t[a, j]).all()):
+            j += 1
+        if j > j0:
+            chunks.append((a, b, j0 * P, j * P))
+        r = a
+        while r < b:
+            if full[r] <= j:
+                private[r] = j * P
+                r += 1
+                continue
+            e = r + 1
+            while e < b and full[e] > j and t[e, j] == t[r, j]:
+                e += 1
+            visit(r, e, j)
+            r = e
+
+    visit(0, B, 0)
+    return chunks, private
+
+
+@dataclass
+class HostSharedPlan:
+    items: np.ndarray          # int32 [n, 8]: row0, nrows, tb, te, slot, tiled, 0, 0
+    row_private: np.ndarray    # int32 [B, 2]: first private token, its slot
+    max_slots: int
+    partition_tokens: int
+    chunks: List[Tuple[int, int, int, int]]
+
+
+def shared_plan(tables: np.ndarray, seq_lens: Sequence[int], block_size: int, group: int,
+                partition_tokens: int = 256, threshold: int = 1) -> HostSharedPlan:
+    """The work items of ``paged_decode_shared`` for a batch.
+
+    Every chunk is cut into pieces of ``partition_tokens`` keys from its first
+    key; each piece is one partial state (slot) of every row it covers.  Rows
+    of a piece go in 16-column tiles of 16 // group rows; groups of four tiles
+    form one "tiled" item (one K/V read for 64 columns), a single leftover
+    tile an "interleaved" one.  A row's slots: its chunks' pieces in path
+    order, then its private pieces.
+    """
+    if partition_tokens <= 0 or partition_tokens % 256:
+        raise ValueError("partition_tokens must be a positive multiple of 256")
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    chunks, private = shared_chunks(tables, lens, block_size, threshold)
+    pt = partition_tokens
+    rpt = 16 // group
+    if rpt < 1:
+        raise ValueError("group (q-heads per kv head) must be at most 16")
+    next_slot = np.zeros(len(lens), dtype=np.int64)
+    items = []
+    for a, b, t0, t1 in chunks:
+        base = int(next_slot[a])
+        if not (next_slot[a:b] == base).all():
+            raise AssertionError("rows of a chunk disagree on their ancestors")
+        pieces = -(-(t1 - t0) // pt)
+        tiles = -(-(b - a) // rpt)
+        for k in range(pieces):
+            tb = t0 + k * pt
+            te = min(t1, tb + pt)
+            ti = 0
+            while ti < tiles:
+                n_t = min(4, tiles - ti)
+                row0 = a + ti * rpt
+                nrows = min(b, a + (ti + n_t) * rpt) - row0
+                items.append((row0, nrows, tb, te, base + k, 1 if n_t > 1 else 0, 0, 0))
+                ti += n_t
+        next_slot[a:b] += pieces
+    row_private = np.stack([private, next_slot], axis=1).astype(np.int32)
+    priv_pieces = -(-np.maximum(lens - private, 0) // pt)
+    max_slots = int(max(1, (next_slot + priv_pieces).max()))
+    arr = np.array(items, dtype=np.int32).reshape(-1, 8)
+    return HostSharedPlan(arr, row_private, max_slots, pt, chunks)

@@ -138,6 +138,18 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
   }
 }
 
+// The tile is sized to the partition count: clamped surplus loads in a tile
+// are real memory requests.
+template <int D>
+__device__ void merge_row(const DecodeArgs& a, int r, int h, int np_r) {
+  if (np_r <= 4)
+    merge_partitions<D, 4>(a, r, h, np_r);
+  else if (np_r <= 8)
+    merge_partitions<D, 8>(a, r, h, np_r);
+  else
+    merge_partitions<D, 16>(a, r, h, np_r);
+}
+
 // Merge the wave states of one work-group; write the row (one partition) or
 // the partition state; the last partition of a (request, kv head) merges all.
 template <int D>
@@ -190,14 +202,7 @@ __device__ void finish_workgroup(const DecodeArgs& a, WaveStates<D>& st, int r, 
                np_r - 1);
   __syncthreads();
   if (!st.last) return;
-  // The tile is sized to the partition count: clamped surplus loads in a
-  // tile are real memory requests.
-  if (np_r <= 4)
-    merge_partitions<D, 4>(a, r, h, np_r);
-  else if (np_r <= 8)
-    merge_partitions<D, 8>(a, r, h, np_r);
-  else
-    merge_partitions<D, 16>(a, r, h, np_r);
+  merge_row<D>(a, r, h, np_r);
   if (threadIdx.x == 0) *counter = 0;  // ready for the next call on this workspace
 }
 
@@ -264,6 +269,95 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt)
     vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
+}
+
+// One 32-token chunk of a wave: the score product over its K fragments, the
+// online-softmax update of (m_run, l_run), the value product into acc, and
+// the loads of the wave's next chunk tn, each issued as soon as the registers
+// it overwrites are consumed.  Tokens at or past t_end are masked out;
+// columns at or past ncols carry no probability mass.
+template <int D>
+__device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, int tn, int t_end,
+                                           int ncols, float scale_log2,
+                                           const bf16x8 (&qf)[D / 32], u32x4 (&kf)[2][D / 32],
+                                           u32x4 (&vf)[D / 16], float& m_run, float& l_run,
+                                           f32x4 (&acc)[D / 16], int n, int g) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int CH = 32;
+  int64_t nb0, nb1;
+  chunk_blocks(pv, tn, nb0, nb1);
+
+  // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
+  f32x4 s[2];
+#pragma unroll
+  for (int at = 0; at < 2; ++at) {
+    s[at] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[at][kk]),
+                                                       qf[kk], s[at], 0, 0, 0);
+  }
+  load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
+
+  const int tbase = t0 + 8 * g;  // token of k-slot j = 0 of this lane
+  float x[8];
+#pragma unroll
+  for (int at = 0; at < 2; ++at)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int j = 4 * at + i;
+      const float v = s[at][i] * scale_log2;
+      x[j] = (tbase + j < t_end) ? v : -INFINITY;
+    }
+  float cmax = x[0];
+#pragma unroll
+  for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  const float m_new = fmaxf(m_run, cmax);
+  const float alpha = fast_exp2(m_run - m_new);
+  m_run = m_new;
+
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = (n < ncols) ? fast_exp2(x[j] - m_new) : 0.f;
+    psum += p[j];
+  }
+  l_run = l_run * alpha + psum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+  }
+
+  bf16x8 phi, plo;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const __bf16 hi = (__bf16)p[j];
+    phi[j] = hi;
+    plo[j] = (__bf16)(p[j] - (float)hi);
+  }
+
+  // Tail chunk: zero the V scalars of tokens >= t_end (they may hold NaN).
+  if (t0 + CH > t_end) {
+    const int cnt = t_end - tbase;  // valid tokens among this lane's 8
+    u32x4 mask;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      mask[q] = (cnt >= 2 * q + 2) ? 0xFFFFFFFFu : ((cnt == 2 * q + 1) ? 0x0000FFFFu : 0u);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) vf[mt] &= mask;
+  }
+
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const bf16x8 va = __builtin_bit_cast(bf16x8, vf[mt]);
+    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[mt], 0, 0, 0);
+    acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[mt], 0, 0, 0);
+  }
+  load_v<D>(vf, pv, h, tn, nb0, nb1, n, g);
 }
 
 // Grid: x = kv head, y = request, z = partition.  Work-groups reach the
@@ -352,79 +446,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     // requested again (in bounds, served from L2), which keeps the number of
     // loads in flight the same on every iteration.
     const int tn = it + 1 < n_w ? t0 + kWaves * CH : t0;
-    int64_t nb0, nb1;
-    chunk_blocks(pv, tn, nb0, nb1);
-
-    // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
-    f32x4 s[2];
-#pragma unroll
-    for (int at = 0; at < 2; ++at) {
-      s[at] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[at][kk]),
-                                                         qf[kk], s[at], 0, 0, 0);
-    }
-    load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
-
-    const int tbase = t0 + 8 * g;  // token of k-slot j = 0 of this lane
-    float x[8];
-#pragma unroll
-    for (int at = 0; at < 2; ++at)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * at + i;
-        const float v = s[at][i] * a.scale_log2;
-        x[j] = (tbase + j < T) ? v : -INFINITY;
-      }
-    float cmax = x[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run, cmax);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
-
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = (n < G) ? fast_exp2(x[j] - m_new) : 0.f;
-      psum += p[j];
-    }
-    l_run = l_run * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-    }
-
-    bf16x8 phi, plo;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 hi = (__bf16)p[j];
-      phi[j] = hi;
-      plo[j] = (__bf16)(p[j] - (float)hi);
-    }
-
-    // Tail chunk: zero the V scalars of tokens >= T (they may hold NaN).
-    if (t0 + CH > T) {
-      const int cnt = T - tbase;  // valid tokens among this lane's 8
-      u32x4 mask;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        mask[q] = (cnt >= 2 * q + 2) ? 0xFFFFFFFFu : ((cnt == 2 * q + 1) ? 0x0000FFFFu : 0u);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) vf[mt] &= mask;
-    }
-
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const bf16x8 va = __builtin_bit_cast(bf16x8, vf[mt]);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[mt], 0, 0, 0);
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[mt], 0, 0, 0);
-    }
-    load_v<D>(vf, pv, h, tn, nb0, nb1, n, g);
+    chunk_step<D>(pv, h, t0, tn, T, G, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
   }
 
   // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n]: four
@@ -439,6 +461,219 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(&st.o[wave][n][16 * mt + 4 * g]) = acc[mt];
   __syncthreads();
   finish_workgroup<D>(a, st, r, h, part, T);
+}
+
+// ---------------------------------------------------------------------------
+// Shared-prefix execution: chunk-first and sequence-first items in one launch
+// ---------------------------------------------------------------------------
+// A chunk is a run of whole blocks that every row of a contiguous range of the
+// batch maps to the same physical ids.  Each (row, q-head) pair is one column
+// of the MFMA products; a 16-column tile holds 16/G rows of one kv head.
+//  * chunk-first item (grid z < nz_items): a piece [tb, te) of a chunk and the
+//    rows it covers.  "Tiled" items give wave w its own 16-column tile and let
+//    it walk every 32-token chunk of the piece, so the four waves read each
+//    K/V chunk at the same moment (HBM once, the cache for the other three)
+//    and the shared keys are multiplied against up to 64 query columns;
+//    "interleaved" items (one tile) split the chunks among the waves as the
+//    plain decode does.
+//  * sequence-first item (grid z >= nz_items): a piece of one row's private
+//    range [private_begin, T), split from private_begin.
+// Every item leaves one partial state per column in its row's slot list; the
+// last contributor of a (row, kv head) merges the row's slots in slot order,
+// so the result does not depend on which work-group finishes last.
+// Grid: x = kv head, y = request (chunk-first: item index low part), z as above.
+typedef const int32_t __attribute__((address_space(4))) item_t;
+
+constexpr int kItemInts = 8;      // row0, nrows, tb, te, slot, tiled, 0, 0
+constexpr int kMaxItemRows = 64;  // 4 tiles x 16 rows (G = 1)
+
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
+    const void* __restrict__ kbase, const void* __restrict__ vbase, int32_t max_blocks,
+    int32_t part_tokens, int32_t log2P, int32_t last_block, int32_t k_sb, int32_t k_sh,
+    DecodeArgs a, SharedArgs sa) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int CH = 32;
+  constexpr int C4 = D / 4;
+
+  __shared__ WaveStates<D> st;
+  __shared__ int s_slots[kMaxItemRows];  // slot count of each row of the item
+  __shared__ int s_last[kMaxItemRows];
+
+  const int h = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int G = a.G;
+  const int rpt = 16 / G;  // rows per 16-column tile
+
+  int row0, nrows, tb, te, slot, tiled;
+  if ((int)blockIdx.z < sa.nz_items) {
+    const int fa = blockIdx.y + gridDim.y * blockIdx.z;
+    if (fa >= sa.n_items) return;
+    item_t* it = (item_t*)(sa.items + (int64_t)kItemInts * fa);
+    row0 = it[0];
+    nrows = it[1];
+    tb = it[2];
+    te = it[3];
+    slot = it[4];
+    tiled = it[5] != 0;
+    // Items are device data checked only in validate mode: a malformed one
+    // must not address outside the batch, the LDS row arrays or the slots.
+    if (row0 < 0 || nrows < 1 || nrows > (tiled ? kWaves : 1) * rpt || row0 + nrows > a.batch ||
+        tb < 0 || te <= tb)
+      return;
+  } else {
+    const int r = blockIdx.y;
+    const int part = blockIdx.z - sa.nz_items;
+    item_t* rp = (item_t*)(sa.row_private + 2 * (int64_t)r);
+    const int T = seq_lens[r];
+    const int pbeg = rp[0];
+    tb = pbeg + part * part_tokens;
+    if (tb >= T || pbeg < 0) return;  // empty piece: never counted, never read
+    te = min(T, tb + part_tokens);
+    row0 = r;
+    nrows = 1;
+    slot = rp[1] + part;
+    tiled = 0;
+  }
+  if (slot < 0 || slot >= a.n_parts) return;
+  // Length and private range of the item's rows: requested now, used after
+  // the loop (slot counts), so the loads wait in flight meanwhile.
+  int rT = 0, rpb = 0, rps = 0;
+  if ((int)threadIdx.x < nrows) {
+    const int rr = row0 + threadIdx.x;
+    rT = seq_lens[rr];
+    rpb = sa.row_private[2 * rr];
+    rps = sa.row_private[2 * rr + 1];
+  }
+
+  const PoolView pv{(table_t*)(tables + (int64_t)row0 * max_blocks),
+                    static_cast<const uint16_t*>(kbase), static_cast<const uint16_t*>(vbase),
+                    k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P};
+  // This wave's columns and chunk walk.
+  const int tile = tiled ? wave : 0;
+  const int trow0 = tile * rpt;                       // first item row of the tile
+  const int wrows = max(0, min(rpt, nrows - trow0));  // rows of the tile
+  const int ncols = wrows * G;
+  const int first = tiled ? tb : tb + wave * CH;
+  const int stride = tiled ? CH : kWaves * CH;
+  const int span = te - first;
+  const int n_w = (span > 0 && ncols > 0) ? (span + stride - 1) / stride : 0;
+
+  int t0 = first;
+  u32x4 qraw[KK];
+  u32x4 kf[2][KK];
+  u32x4 vf[MT];
+  if (n_w > 0) {
+    int64_t pb0, pb1;
+    chunk_blocks(pv, t0, pb0, pb1);
+    const int cn = n < ncols ? n : 0;
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)(row0 + trow0 + cn / G) * a.num_q_heads +
+                            (int64_t)h * G + cn % G) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 qf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qf[kk] = __builtin_bit_cast(bf16x8, n < ncols ? qraw[kk] : u32x4{0u, 0u, 0u, 0u});
+
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+  f32x4 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < n_w; ++it, t0 += stride) {
+    const int tn = it + 1 < n_w ? t0 + stride : t0;
+    chunk_step<D>(pv, h, t0, tn, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
+  }
+
+  l_run += __shfl_xor(l_run, 16, 64);
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (g == 0) {
+    st.m[wave][n] = m_run;
+    st.l[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(&st.o[wave][n][16 * mt + 4 * g]) = acc[mt];
+  // Slot count of each row, clamped to the workspace's slots per row.
+  if ((int)threadIdx.x < nrows) {
+    const int ns = rps + (rT > rpb ? (rT - rpb + part_tokens - 1) / part_tokens : 0);
+    s_slots[threadIdx.x] = min(max(ns, 0), a.n_parts);
+  }
+  __syncthreads();
+
+  // Columns of the item: tile t, column n -> item row t*rpt + n/G, q-head
+  // h*G + n%G.  Tiled items take each tile's state from its own wave;
+  // interleaved items merge the four waves of tile 0.
+  const int tiles = tiled ? kWaves : 1;
+  for (int idx = threadIdx.x; idx < tiles * 16 * C4; idx += kDecodeThreads) {
+    const int col = idx / C4;
+    const int c = idx - col * C4;  // dims c + C4 * e, e < 4
+    const int t = col >> 4;
+    const int cn = col & 15;
+    const int ri = t * rpt + cn / G;
+    if (cn >= rpt * G || ri >= nrows) continue;
+    const int w0 = tiled ? t : 0;
+    const int w1 = tiled ? t + 1 : kWaves;
+    float M = -INFINITY;
+    for (int w = w0; w < w1; ++w) M = fmaxf(M, st.m[w][cn]);
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int w = w0; w < w1; ++w) {
+        const float mw = st.m[w][cn];
+        if (mw == -INFINITY) continue;
+        const float wt = fast_exp2(mw - M);
+        L += wt * st.l[w][cn];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) O[e] += wt * st.o[w][cn][c + C4 * e];
+      }
+    }
+    const int64_t row = (int64_t)(row0 + ri) * a.num_q_heads + (int64_t)h * G + cn % G;
+    if (s_slots[ri] == 1) {
+      const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) a.out[row * D + c + C4 * e] = res[e];
+      if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const int64_t prow = row * a.n_parts + slot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st_state(a.ws_u + prow * D + c + C4 * e, O[e]);
+      if (c == 0) {
+        st_state(a.ws_ml + prow * 2 + 0, M);
+        st_state(a.ws_ml + prow * 2 + 1, L);
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's state stores are complete
+  __syncthreads();
+  if ((int)threadIdx.x < nrows) {
+    const int ns = s_slots[threadIdx.x];
+    int last = 0;
+    if (ns > 1) {
+      int32_t* counter = a.counters + (int64_t)(row0 + threadIdx.x) * a.num_kv_heads + h;
+      last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == ns - 1;
+    }
+    s_last[threadIdx.x] = last;
+  }
+  __syncthreads();
+  for (int i = 0; i < nrows; ++i) {
+    if (!s_last[i]) continue;
+    merge_row<D>(a, row0 + i, h, s_slots[i]);
+    if (threadIdx.x == 0) a.counters[(int64_t)(row0 + i) * a.num_kv_heads + h] = 0;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -605,6 +840,18 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_paged_decode_shared(const DecodeArgs& a, const SharedArgs& sa, int head_dim,
+                                      int private_parts, hipStream_t stream) {
+  const dim3 grid((unsigned)a.num_kv_heads, (unsigned)a.batch,
+                  (unsigned)(sa.nz_items + private_parts));
+  const dim3 block(kDecodeThreads);
+  auto kern = head_dim == 128 ? decode_bf16_shared_kernel<128> : decode_bf16_shared_kernel<64>;
+  hipLaunchKernelGGL(kern, grid, block, 0, stream, a.tables, a.seq_lens, a.k, a.v, a.max_blocks,
+                     a.part_tokens, a.log2P, a.num_blocks - 1, (int32_t)a.k_sb, (int32_t)a.k_sh, a,
+                     sa);
+  return hipGetLastError();
 }
 
 }  // namespace pba

@@ -4,6 +4,7 @@
 // Memory Layout and Exact Reuse", 0x05G: rejected operations preserve the
 // predecessor state; "Cache Concepts: Prefix Matching vs. Storage": validate
 // every id before touching bytes).
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -162,7 +163,7 @@ bool copy_to_host(std::vector<T>& dst, const T* src, int64_t n, hipStream_t stre
 
 extern "C" {
 
-int pba_version(void) { return 100; }
+int pba_version(void) { return 200; }
 
 int pba_set_validate(int on) { return g_validate.exchange(on ? 1 : 0); }
 
@@ -342,6 +343,181 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   a.scale_log2 = scale * 1.4426950408889634f;
   return pba::launch_paged_decode(a, pool->dtype, pool->head_dim, s) == hipSuccess ? PBA_OK
                                                                                   : PBA_ERR_HIP;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Host-visible checks of a shared-prefix plan (the device arrays are checked
+// in validate mode only).
+int check_shared_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
+                      int32_t max_blocks, const pba_shared_plan* plan, int32_t* nz_items,
+                      int32_t* private_parts) {
+  if (!plan) return PBA_ERR_NULL_ARG;
+  if (pool->dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
+  if (plan->reserved0 != 0 || plan->num_items < 0 || plan->max_slots < 1) return PBA_ERR_BAD_SHAPE;
+  const int32_t pt = plan->partition_tokens;
+  if (pt <= 0 || pt % kPartGranule) return PBA_ERR_UNSUPPORTED;
+  if (batch > 65535) return PBA_ERR_UNSUPPORTED;
+  if (batch > 0 && (!plan->row_private || (plan->num_items > 0 && !plan->items)))
+    return PBA_ERR_NULL_ARG;
+  const int64_t max_T = (int64_t)max_blocks * pool->block_size;
+  const int64_t pp = (max_T + pt - 1) / pt;
+  const int64_t nz = batch > 0 ? ((int64_t)plan->num_items + batch - 1) / batch : 0;
+  if (pp + nz > 65535) return PBA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * num_q_heads > INT32_MAX) return PBA_ERR_UNSUPPORTED;
+  *nz_items = (int32_t)nz;
+  *private_parts = (int32_t)pp;
+  return PBA_OK;
+}
+
+// Validate mode: every row's key positions [0, T) are covered exactly once by
+// the chunk-first items covering it and its private pieces, its slots are
+// exactly 0 .. n-1 with n <= max_slots, and every row an item covers maps the
+// item's blocks to the same physical ids as the item's first row.
+int validate_shared_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
+                         int32_t max_blocks, const pba_shared_plan* plan,
+                         const std::vector<int32_t>& lens, const std::vector<int32_t>& tab,
+                         hipStream_t s) {
+  const int P = pool->block_size;
+  const int align = P < 32 ? P : 32;
+  const int G = num_q_heads / pool->num_kv_heads;
+  const int rpt = 16 / G;
+  const int32_t pt = plan->partition_tokens;
+  std::vector<int32_t> items, priv;
+  if (!copy_to_host(items, plan->items, (int64_t)plan->num_items * 8, s)) return PBA_ERR_HIP;
+  if (!copy_to_host(priv, plan->row_private, (int64_t)batch * 2, s)) return PBA_ERR_HIP;
+  // Per row: (token begin, token end) pieces and slots.
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> spans(batch);
+  std::vector<std::vector<int32_t>> slots(batch);
+  for (int32_t i = 0; i < plan->num_items; ++i) {
+    const int32_t* it = &items[(size_t)i * 8];
+    const int32_t row0 = it[0], nrows = it[1], tb = it[2], te = it[3], slot = it[4];
+    const bool tiled = it[5] != 0;
+    if (row0 < 0 || nrows < 1 || nrows > (tiled ? 4 : 1) * rpt || (int64_t)row0 + nrows > batch)
+      return PBA_ERR_OUT_OF_RANGE;
+    if (tb < 0 || te <= tb || tb % align || slot < 0 || slot >= plan->max_slots)
+      return PBA_ERR_OUT_OF_RANGE;
+    const int64_t j0 = tb / P, j1 = ((int64_t)te + P - 1) / P;
+    for (int32_t r = row0; r < row0 + nrows; ++r) {
+      if (te > lens[r]) return PBA_ERR_OUT_OF_RANGE;
+      for (int64_t j = j0; j < j1; ++j)
+        if (tab[(size_t)r * max_blocks + j] != tab[(size_t)row0 * max_blocks + j])
+          return PBA_ERR_OUT_OF_RANGE;
+      spans[r].push_back({tb, te});
+      slots[r].push_back(slot);
+    }
+  }
+  for (int32_t r = 0; r < batch; ++r) {
+    const int32_t T = lens[r], pb = priv[2 * (size_t)r], ps = priv[2 * (size_t)r + 1];
+    if (pb < 0 || pb > T || pb % align || ps < 0) return PBA_ERR_OUT_OF_RANGE;
+    int32_t k = 0;
+    for (int64_t t = pb; t < T; t += pt, ++k) {
+      spans[r].push_back({t, std::min<int64_t>(T, t + pt)});
+      slots[r].push_back(ps + k);
+    }
+    std::sort(spans[r].begin(), spans[r].end());
+    int64_t at = 0;
+    for (const auto& sp : spans[r]) {
+      if (sp.first != at) return sp.first < at ? PBA_ERR_OVERLAP : PBA_ERR_OUT_OF_RANGE;
+      at = sp.second;
+    }
+    if (at != T) return PBA_ERR_OUT_OF_RANGE;
+    std::sort(slots[r].begin(), slots[r].end());
+    for (size_t q = 0; q < slots[r].size(); ++q) {
+      if (q > 0 && slots[r][q] == slots[r][q - 1]) return PBA_ERR_OVERLAP;
+      if (slots[r][q] != (int32_t)q) return PBA_ERR_OUT_OF_RANGE;
+    }
+    if ((int64_t)slots[r].size() > plan->max_slots) return PBA_ERR_OUT_OF_RANGE;
+  }
+  return PBA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pba_paged_decode_shared_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_heads,
+                                               int32_t batch, int32_t max_blocks_per_seq,
+                                               const pba_shared_plan* plan) {
+  if (check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq)) return 0;
+  int32_t nz = 0, pp = 0;
+  if (check_shared_plan(pool, num_q_heads, batch, max_blocks_per_seq, plan, &nz, &pp)) return 0;
+  return workspace_layout(batch, pool->num_kv_heads, (int64_t)batch * num_q_heads,
+                          plan->max_slots, pool->head_dim).bytes;
+}
+
+int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                            float* lse, const pba_shared_plan* plan, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
+  if (st) return st;
+  int32_t nz = 0, pp = 0;
+  st = check_shared_plan(pool, num_q_heads, batch, max_blocks_per_seq, plan, &nz, &pp);
+  if (st) return st;
+  if (batch == 0) return PBA_OK;
+  if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
+  if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)batch * num_q_heads;
+  const WsLayout ws = workspace_layout(batch, pool->num_kv_heads, rows, plan->max_slots,
+                                       pool->head_dim);
+  if (ws.bytes > 0 && (!workspace || workspace_bytes < ws.bytes || !aligned16(workspace)))
+    return PBA_ERR_WORKSPACE_TOO_SMALL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    std::vector<int32_t> lens, tab;
+    if (!copy_to_host(lens, seq_lens, batch, s)) return PBA_ERR_HIP;
+    if (!copy_to_host(tab, block_tables, (int64_t)batch * max_blocks_per_seq, s)) return PBA_ERR_HIP;
+    const int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
+    for (int32_t r = 0; r < batch; ++r) {
+      const int64_t T = lens[r];
+      if (T < 1 || T > cap) return PBA_ERR_OUT_OF_RANGE;
+      const int64_t nb = (T + pool->block_size - 1) / pool->block_size;
+      for (int64_t j = 0; j < nb; ++j) {
+        const int32_t b = tab[(size_t)r * max_blocks_per_seq + j];
+        if (b < 0 || b >= pool->num_blocks) return PBA_ERR_OUT_OF_RANGE;
+      }
+    }
+    st = validate_shared_plan(pool, num_q_heads, batch, max_blocks_per_seq, plan, lens, tab, s);
+    if (st) return st;
+  }
+  pba::DecodeArgs a;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.k_sb = pool->k_stride_block;
+  a.k_sh = pool->k_stride_head;
+  a.v_sb = pool->v_stride_block;
+  a.v_sh = pool->v_stride_head;
+  a.q = q;
+  a.tables = block_tables;
+  a.seq_lens = seq_lens;
+  a.out = out;
+  a.lse = lse;
+  char* wsb = static_cast<char*>(workspace);
+  a.counters = ws.bytes ? reinterpret_cast<int32_t*>(wsb) : nullptr;
+  a.ws_ml = ws.bytes ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
+  a.ws_u = ws.bytes ? reinterpret_cast<float*>(wsb + ws.u_off) : nullptr;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = pool->num_blocks;
+  a.log2P = log2_exact(pool->block_size);
+  a.G = num_q_heads / pool->num_kv_heads;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.batch = batch;
+  a.part_tokens = plan->partition_tokens;
+  a.n_parts = plan->max_slots;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  pba::SharedArgs sa;
+  sa.items = plan->items;
+  sa.row_private = plan->row_private;
+  sa.n_items = plan->num_items;
+  sa.nz_items = nz;
+  return pba::launch_paged_decode_shared(a, sa, pool->head_dim, (int)pp, s) == hipSuccess
+             ? PBA_OK
+             : PBA_ERR_HIP;
 }
 
 }  // extern "C"

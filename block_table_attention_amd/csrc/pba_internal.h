@@ -58,9 +58,22 @@ struct DecodeArgs {
   float scale_log2;  // scale * log2(e): scores live in the log2 domain
 };
 
+// Shared-prefix decode: chunk-first items (int32 x 8 each: row0, nrows, tb,
+// te, slot, tiled, 0, 0) and each row's private range (first token, slot).
+struct SharedArgs {
+  const int32_t* items;
+  const int32_t* row_private;  // [batch][2]
+  int32_t n_items;
+  int32_t nz_items;  // grid z planes of chunk-first items: ceil(n_items / batch)
+};
+
 hipError_t launch_kv_append(const AppendArgs& a, int esize, hipStream_t stream);
 hipError_t launch_block_copy(const CopyArgs& a, int64_t n_pairs, int kv_heads, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);
+// bf16 only; a.n_parts is the slot stride (max_slots); private_parts bounds the
+// private pieces of any row (ceil(max T / part_tokens)).
+hipError_t launch_paged_decode_shared(const DecodeArgs& a, const SharedArgs& sa, int head_dim,
+                                      int private_parts, hipStream_t stream);
 // Work-group size and the token granule partitions are cut at, per dtype.
 #ifndef PBA_DECODE_WAVES
 #define PBA_DECODE_WAVES 4

@@ -177,6 +177,64 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
                           int32_t max_blocks_per_seq, int32_t partition_tokens,
                           int32_t* partition_tokens_out, int32_t* num_partitions_out);
 
+/*
+ * Shared-prefix execution reuse ("M5.3", 0x0BA-0x0BE: disjoint key partitions
+ * of one score row merged by log-sum-exp; Hydragen's batching of the queries
+ * that share K/V; ChunkAttention's chunk-first / sequence-first phases).
+ *
+ * The batch is described as chunks: a chunk is a run of whole blocks that every
+ * row of a contiguous range of the batch maps to the same physical ids.  The
+ * plan lists chunk-first work items and each row's private range:
+ *
+ *   items        device int32 [num_items][8], one work item per entry:
+ *                  [0] row0, [1] nrows: the batch rows [row0, row0 + nrows)
+ *                  [2] tb, [3] te: the key positions [tb, te) of those rows
+ *                  [4] slot: index of the item's partial state in each row
+ *                  [5] tiled: 0 -> nrows <= 16/G, the 4 waves of a work-group
+ *                      split the positions; 1 -> nrows <= 4 * (16/G), each
+ *                      wave takes 16/G rows and all positions (one K/V read
+ *                      serves up to 64 query columns)
+ *                  [6], [7]: 0
+ *   row_private  device int32 [batch][2]: (pb, ps): row r's positions
+ *                [pb, T) are decoded alone in pieces of partition_tokens from
+ *                pb, the k-th piece writing slot ps + k.
+ *
+ * Contract (checked in validate mode, PBA_ERR_OUT_OF_RANGE / PBA_ERR_OVERLAP):
+ * for every row the item ranges covering it and its private pieces tile
+ * [0, T) exactly, and its slots are exactly 0 .. n-1 with n <= max_slots; tb
+ * and pb are multiples of min(P, 32); te <= T of every covered row; every
+ * covered row maps blocks [tb/P, ceil(te/P)) to the same ids as row0.  Outside
+ * validate mode a plan that breaks the contract gives undefined results but
+ * stays inside the caller's buffers.  The result equals pba_paged_decode's up
+ * to rounding and is deterministic for a fixed plan.
+ *
+ * bf16 pools only (PBA_ERR_UNSUPPORTED otherwise); batch <= 65535.
+ */
+typedef struct pba_shared_plan {
+  int32_t num_items;
+  int32_t max_slots;         /* partial states per (row, q-head) in the workspace */
+  int32_t partition_tokens;  /* piece length: a positive multiple of 256 */
+  int32_t reserved0;         /* must be 0 */
+  const int32_t* items;
+  const int32_t* row_private;
+} pba_shared_plan;
+
+/* Workspace bytes pba_paged_decode_shared needs (0 when max_slots == 1);
+ * returns 0 for arguments it would reject.  The first 4 * batch *
+ * num_kv_heads bytes are completion counters with the same zero-once rule as
+ * pba_paged_decode's workspace. */
+size_t pba_paged_decode_shared_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_heads,
+                                               int32_t batch, int32_t max_blocks_per_seq,
+                                               const pba_shared_plan* plan);
+
+/* paged_decode over a batch described by a shared-prefix plan; arguments as
+ * pba_paged_decode, with the plan in place of partition_tokens. */
+int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                            float* lse, const pba_shared_plan* plan, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* pba_status_string(int status);
 

@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     assert declared == sorted(pba.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pba.version() == 100
+    assert pba.version() == 200
 
 
 def _desc(**kw):
@@ -232,3 +232,45 @@ def test_bench_ledger_matches_oracle(name):
     assert got["tail_slots"] == view["tail_slots"]
     assert got["blocks_mapped"] == view["refs"] == cells["used"]
     assert got["table_cells_dense"] == cells["table"]
+
+
+def test_shared_decode_host_rejections():
+    """Host-side checks of pba_paged_decode_shared: fp32 pools, a missing or
+    malformed plan, and partition lengths that are not multiples of 256 are
+    rejected before any launch; the workspace size follows max_slots."""
+    import block_table_attention_amd as pba
+
+    lib = _lib()
+    d = _desc()
+    items, rowp = 0x90000, 0xA0000
+
+    def plan(num_items=2, max_slots=3, pt=256, reserved=0, it=items, rp=rowp):
+        return pba.SharedPlanDesc(num_items, max_slots, pt, reserved, it, rp)
+
+    def call(desc, p, ws=0x80000, wsb=1 << 30, batch=2, q=0x30000):
+        return lib.pba_paged_decode_shared(ctypes.byref(desc), q, 8, 0x40000, 4, 0x50000, batch,
+                                           ctypes.c_float(0.1), 0x60000, NULL,
+                                           None if p is None else ctypes.byref(p), ws, wsb, NULL)
+
+    assert call(d, None) == -1
+    assert call(_desc(dtype=0), plan()) == -4            # bf16 only
+    assert call(d, plan(pt=100)) == -4
+    assert call(d, plan(pt=0)) == -4
+    assert call(d, plan(reserved=1)) == -3
+    assert call(d, plan(max_slots=0)) == -3
+    assert call(d, plan(num_items=-1)) == -3
+    assert call(d, plan(it=None)) == -1
+    assert call(d, plan(rp=None)) == -1
+    assert call(d, plan(), batch=70000) == -4
+    assert call(d, plan(), batch=0) == 0
+    need = lib.pba_paged_decode_shared_workspace_bytes(ctypes.byref(d), 8, 2, 4, ctypes.byref(plan()))
+    rows = 2 * 8
+    up = lambda x: (x + 255) // 256 * 256
+    assert need == up(2 * 2 * 4) + up(rows * 3 * 2 * 4) + rows * 3 * 128 * 4
+    assert call(d, plan(), ws=NULL, wsb=0) == -5
+    assert call(d, plan(), wsb=need - 1) == -5
+    assert lib.pba_paged_decode_shared_workspace_bytes(
+        ctypes.byref(d), 8, 2, 4, ctypes.byref(plan(max_slots=1))) == 0
+    assert lib.pba_paged_decode_shared_workspace_bytes(
+        ctypes.byref(_desc(dtype=0)), 8, 2, 4, ctypes.byref(plan())) == 0
+    assert call(d, plan(), q=0x30008) == -4
