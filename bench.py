@@ -54,6 +54,13 @@ def parse():
     ap.add_argument("--partition-tokens", type=int, default=-1,
                     help="decode partition length; 0 = the library's plan; default: chosen "
                          "from the batch's lengths by blocks.suggest_partition_tokens")
+    ap.add_argument("--decode", default="auto", choices=["auto", "plain", "shared"],
+                    help="decode entry point: paged_decode, paged_decode_shared (shared-prefix "
+                         "execution reuse), or auto = shared when the batch shares chunks")
+    ap.add_argument("--shared-partition-tokens", type=int, default=1024,
+                    help="piece length of the shared-prefix plan")
+    ap.add_argument("--shared-tiles", type=int, default=2, choices=[1, 2, 4],
+                    help="16-column tiles per chunk-first item of the shared-prefix plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--decode-only", action="store_true",
@@ -252,10 +259,24 @@ def run_workload(args, name, pba, torch, dev):
     step_slots = torch.from_numpy(plan.step_slots).to(dev)
     copy_src = torch.from_numpy(plan.step_src).to(dev)
     copy_dst = torch.from_numpy(plan.step_dst).to(dev)
-    q = dev_bits(wl.q_bits(w))
+    qb = wl.q_bits(w)
     B = len(plan.seq_lens)
-    tab_d = torch.from_numpy(plan.tables).to(dev)
-    lens_d = torch.from_numpy(plan.seq_lens).to(dev)
+    tables, lens_h = plan.tables, plan.seq_lens
+    # Shared-prefix execution: the caller orders the batch so rows sharing
+    # leading blocks are adjacent and describes the shared chunks.
+    from block_table_attention_amd.blocks import shared_plan, sharing_order
+    path = args.decode
+    host_plan = None
+    if path != "plain" and sh.dtype == "bf16":
+        order = sharing_order(tables)
+        cand = shared_plan(tables[order], lens_h[order], P, Hq // Hkv, args.shared_partition_tokens,
+                           tiles_per_item=args.shared_tiles)
+        if path == "shared" or any(b - a > 1 for a, b, _, _ in cand.chunks):
+            tables, lens_h, qb, host_plan = tables[order], lens_h[order], qb[order], cand
+    path = "shared" if host_plan is not None else "plain"
+    q = dev_bits(qb)
+    tab_d = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
+    lens_d = torch.from_numpy(np.ascontiguousarray(lens_h)).to(dev)
     scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
@@ -265,16 +286,25 @@ def run_workload(args, name, pba, torch, dev):
     if req_pt < 0:
         from block_table_attention_amd.blocks import suggest_partition_tokens
         req_pt = suggest_partition_tokens(plan.seq_lens, Hkv)
-    pt, n_parts = pba.paged_decode_plan(pool, Hq, B, mb, req_pt)
-    ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, mb, req_pt)
+    if host_plan is None:
+        pt, n_parts = pba.paged_decode_plan(pool, Hq, B, mb, req_pt)
+        ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, mb, req_pt)
+    else:
+        splan = pba.SharedPlan.from_host(host_plan, dev)
+        pt, n_parts = host_plan.partition_tokens, host_plan.max_slots
+        ws_bytes = pba.paged_decode_shared_workspace_bytes(pool, Hq, B, mb, splan)
     # Zero-filled once: the library keeps the completion counters at zero.
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     torch.cuda.synchronize()
 
     def decode(st=stream):
-        pba.paged_decode(pool, q, tab_d, lens_d, scale, out=out, lse=lse,
-                         partition_tokens=req_pt, workspace=ws, stream=st)
+        if host_plan is None:
+            pba.paged_decode(pool, q, tab_d, lens_d, scale, out=out, lse=lse,
+                             partition_tokens=req_pt, workspace=ws, stream=st)
+        else:
+            pba.paged_decode_shared(pool, q, tab_d, lens_d, splan, scale, out=out, lse=lse,
+                                    workspace=ws, stream=st)
 
     def step(evs=None, st=stream):
         if evs is not None:
@@ -343,7 +373,9 @@ def run_workload(args, name, pba, torch, dev):
           file=sys.stderr, flush=True)
 
     kv_unique, kv_logical, alg_bytes = decode_bytes(plan, sh)
-    traffic = profiled_traffic(name) if args.partition_tokens < 0 else None
+    traffic = (profiled_traffic(name if host_plan is None else f"shared_{name}")
+               if args.partition_tokens < 0 and args.shared_partition_tokens == 1024
+               and args.shared_tiles == 2 else None)
     step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg_ms * 1e-3) / 1e9
     lens = plan.seq_lens
@@ -369,10 +401,17 @@ def run_workload(args, name, pba, torch, dev):
                    "context_sum": int(lens.sum()), "block_size": P, "num_q_heads": Hq,
                    "num_kv_heads": Hkv, "head_dim": d, "pool_blocks": sh.num_blocks,
                    "partition_tokens": pt, "num_partitions": n_parts,
-                   "partition_choice": "library plan" if req_pt == 0 else
-                   ("caller (suggest_partition_tokens)" if args.partition_tokens < 0 else "fixed"),
+                   "partition_choice": "shared-prefix plan" if host_plan is not None else
+                   ("library plan" if req_pt == 0 else
+                    ("caller (suggest_partition_tokens)" if args.partition_tokens < 0 else "fixed")),
+                   "decode_path": path,
+                   "shared_plan": None if host_plan is None else
+                   {"chunks": len(host_plan.chunks), "items": int(host_plan.items.shape[0]),
+                    "max_slots": host_plan.max_slots,
+                    "chunk_rows": int(sum(b - a for a, b, _, _ in host_plan.chunks))},
                    "step": f"block_copy({len(plan.step_src)} pairs) + kv_append("
-                           f"{len(plan.step_slots)} tokens) + paged_decode",
+                           f"{len(plan.step_slots)} tokens) + "
+                           f"{'paged_decode_shared' if host_plan is not None else 'paged_decode'}",
                    "step_launch": "HIP graph replay" if use_graph else "eager"},
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(step_kv_gbs / HBM_PEAK_GBS, 4),
@@ -388,7 +427,9 @@ def run_workload(args, name, pba, torch, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in)",
+                     "kernel": (f"decode_bf16_shared_kernel<{d}> (chunk-first + sequence-first, "
+                                "merge fused in)") if host_plan is not None else
+                               f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in)",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "_kv_value_bytes": kv_unique,
     }

@@ -53,7 +53,7 @@ class PoolDesc(ctypes.Structure):
 
 class SharedPlanDesc(ctypes.Structure):
     _fields_ = [("num_items", ctypes.c_int32), ("max_slots", ctypes.c_int32),
-                ("partition_tokens", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32), ("private_parts", ctypes.c_int32),
                 ("items", ctypes.c_void_p), ("row_private", ctypes.c_void_p)]
 
 
@@ -277,6 +277,7 @@ class SharedPlan:
     row_private: torch.Tensor
     max_slots: int
     partition_tokens: int
+    private_parts: int = 0
 
     def __post_init__(self):
         dev = self.row_private.device
@@ -284,7 +285,8 @@ class SharedPlan:
         _require(self.items, "items", torch.int32, dev, 2)
         if self.items.shape[1] != 8 or self.row_private.shape[1] != 2:
             raise ValueError("items must be [n, 8] and row_private [B, 2]")
-        desc = SharedPlanDesc(self.items.shape[0], self.max_slots, self.partition_tokens, 0,
+        desc = SharedPlanDesc(self.items.shape[0], self.max_slots, self.partition_tokens,
+                              self.private_parts,
                               self.items.data_ptr() if self.items.numel() else None,
                               self.row_private.data_ptr())
         object.__setattr__(self, "_desc", desc)
@@ -297,7 +299,7 @@ class SharedPlan:
         if items.numel() == 0:
             items = torch.zeros((0, 8), dtype=torch.int32, device=device)
         return cls(items, torch.from_numpy(host.row_private).to(device), host.max_slots,
-                   host.partition_tokens)
+                   host.partition_tokens, host.private_parts)
 
 
 def paged_decode_shared_workspace_bytes(pool: KVPool, num_q_heads: int, batch: int,

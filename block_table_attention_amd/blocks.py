@@ -229,24 +229,28 @@ def shared_chunks(tables: np.ndarray, seq_lens: Sequence[int], block_size: int,
 
 @dataclass
 class HostSharedPlan:
-    items: np.ndarray          # int32 [n, 8]: row0, nrows, tb, te, slot, tiled, 0, 0
+    items: np.ndarray          # int32 [n, 8]: row0, nrows, tb, te, slot, tiles, 0, 0
     row_private: np.ndarray    # int32 [B, 2]: first private token, its slot
     max_slots: int
     partition_tokens: int
     chunks: List[Tuple[int, int, int, int]]
+    private_parts: int = 0     # most private pieces of any row
 
 
 def shared_plan(tables: np.ndarray, seq_lens: Sequence[int], block_size: int, group: int,
-                partition_tokens: int = 256, threshold: int = 1) -> HostSharedPlan:
+                partition_tokens: int = 256, threshold: int = 1,
+                tiles_per_item: int = 4) -> HostSharedPlan:
     """The work items of ``paged_decode_shared`` for a batch.
 
     Every chunk is cut into pieces of ``partition_tokens`` keys from its first
     key; each piece is one partial state (slot) of every row it covers.  Rows
-    of a piece go in 16-column tiles of 16 // group rows; groups of four tiles
-    form one "tiled" item (one K/V read for 64 columns), a single leftover
-    tile an "interleaved" one.  A row's slots: its chunks' pieces in path
-    order, then its private pieces.
+    of a piece go in 16-column tiles of 16 // group rows, up to
+    ``tiles_per_item`` (1, 2 or 4) tiles per item: one K/V read serves them
+    all, and the 4 / tiles waves of a tile split its keys.  A row's slots: its
+    chunks' pieces in path order, then its private pieces.
     """
+    if tiles_per_item not in (1, 2, 4):
+        raise ValueError("tiles_per_item must be 1, 2 or 4")
     if partition_tokens <= 0 or partition_tokens % 256:
         raise ValueError("partition_tokens must be a positive multiple of 256")
     lens = np.asarray(seq_lens, dtype=np.int64)
@@ -268,14 +272,18 @@ def shared_plan(tables: np.ndarray, seq_lens: Sequence[int], block_size: int, gr
             te = min(t1, tb + pt)
             ti = 0
             while ti < tiles:
-                n_t = min(4, tiles - ti)
+                left = tiles - ti
+                n_t = min(tiles_per_item, 4 if left >= 4 else (2 if left >= 2 else 1))
                 row0 = a + ti * rpt
                 nrows = min(b, a + (ti + n_t) * rpt) - row0
-                items.append((row0, nrows, tb, te, base + k, 1 if n_t > 1 else 0, 0, 0))
+                items.append((row0, nrows, tb, te, base + k, n_t, 0, 0))
                 ti += n_t
         next_slot[a:b] += pieces
     row_private = np.stack([private, next_slot], axis=1).astype(np.int32)
     priv_pieces = -(-np.maximum(lens - private, 0) // pt)
     max_slots = int(max(1, (next_slot + priv_pieces).max()))
     arr = np.array(items, dtype=np.int32).reshape(-1, 8)
-    return HostSharedPlan(arr, row_private, max_slots, pt, chunks)
+    # The launch holds one grid plane per possible private piece; the true
+    # bound keeps it from filling with empty work-groups.
+    return HostSharedPlan(arr, row_private, max_slots, pt, chunks,
+                          int(max(1, priv_pieces.max())))

@@ -470,12 +470,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
 // batch maps to the same physical ids.  Each (row, q-head) pair is one column
 // of the MFMA products; a 16-column tile holds 16/G rows of one kv head.
 //  * chunk-first item (grid z < nz_items): a piece [tb, te) of a chunk and the
-//    rows it covers.  "Tiled" items give wave w its own 16-column tile and let
-//    it walk every 32-token chunk of the piece, so the four waves read each
-//    K/V chunk at the same moment (HBM once, the cache for the other three)
-//    and the shared keys are multiplied against up to 64 query columns;
-//    "interleaved" items (one tile) split the chunks among the waves as the
-//    plain decode does.
+//    rows it covers, in 1, 2 or 4 tiles of 16 columns.  The 4 / tiles waves
+//    of a tile split its 32-token chunks (as the plain decode does with one
+//    tile); the tiles read each K/V chunk at the same moment (HBM once, the
+//    cache for the others), so one read serves up to 64 query columns.
 //  * sequence-first item (grid z >= nz_items): a piece of one row's private
 //    range [private_begin, T), split from private_begin.
 // Every item leaves one partial state per column in its row's slot list; the
@@ -484,7 +482,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
 // Grid: x = kv head, y = request (chunk-first: item index low part), z as above.
 typedef const int32_t __attribute__((address_space(4))) item_t;
 
-constexpr int kItemInts = 8;      // row0, nrows, tb, te, slot, tiled, 0, 0
+constexpr int kItemInts = 8;      // row0, nrows, tb, te, slot, tiles, 0, 0
 constexpr int kMaxItemRows = 64;  // 4 tiles x 16 rows (G = 1)
 
 template <int D>
@@ -511,7 +509,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   const int G = a.G;
   const int rpt = 16 / G;  // rows per 16-column tile
 
-  int row0, nrows, tb, te, slot, tiled;
+  int row0, nrows, tb, te, slot, tiles;
   if ((int)blockIdx.z < sa.nz_items) {
     const int fa = blockIdx.y + gridDim.y * blockIdx.z;
     if (fa >= sa.n_items) return;
@@ -521,11 +519,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     tb = it[2];
     te = it[3];
     slot = it[4];
-    tiled = it[5] != 0;
+    tiles = it[5];
     // Items are device data checked only in validate mode: a malformed one
     // must not address outside the batch, the LDS row arrays or the slots.
-    if (row0 < 0 || nrows < 1 || nrows > (tiled ? kWaves : 1) * rpt || row0 + nrows > a.batch ||
-        tb < 0 || te <= tb)
+    if ((tiles != 1 && tiles != 2 && tiles != 4) || row0 < 0 || nrows < 1 ||
+        nrows > tiles * rpt || row0 + nrows > a.batch || tb < 0 || te <= tb)
       return;
   } else {
     const int r = blockIdx.y;
@@ -539,7 +537,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     row0 = r;
     nrows = 1;
     slot = rp[1] + part;
-    tiled = 0;
+    tiles = 1;
   }
   if (slot < 0 || slot >= a.n_parts) return;
   // Length and private range of the item's rows: requested now, used after
@@ -555,13 +553,15 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   const PoolView pv{(table_t*)(tables + (int64_t)row0 * max_blocks),
                     static_cast<const uint16_t*>(kbase), static_cast<const uint16_t*>(vbase),
                     k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P};
-  // This wave's columns and chunk walk.
-  const int tile = tiled ? wave : 0;
+  // This wave's columns and chunk walk: wpt waves per tile split its chunks.
+  const int wpt = kWaves / tiles;
+  const int tile = wave / wpt;
+  const int sub = wave - tile * wpt;
   const int trow0 = tile * rpt;                       // first item row of the tile
   const int wrows = max(0, min(rpt, nrows - trow0));  // rows of the tile
   const int ncols = wrows * G;
-  const int first = tiled ? tb : tb + wave * CH;
-  const int stride = tiled ? CH : kWaves * CH;
+  const int first = tb + sub * CH;
+  const int stride = wpt * CH;
   const int span = te - first;
   const int n_w = (span > 0 && ncols > 0) ? (span + stride - 1) / stride : 0;
 
@@ -615,9 +615,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   __syncthreads();
 
   // Columns of the item: tile t, column n -> item row t*rpt + n/G, q-head
-  // h*G + n%G.  Tiled items take each tile's state from its own wave;
-  // interleaved items merge the four waves of tile 0.
-  const int tiles = tiled ? kWaves : 1;
+  // h*G + n%G; a tile's state merges the states of its wpt waves.
   for (int idx = threadIdx.x; idx < tiles * 16 * C4; idx += kDecodeThreads) {
     const int col = idx / C4;
     const int c = idx - col * C4;  // dims c + C4 * e, e < 4
@@ -625,8 +623,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     const int cn = col & 15;
     const int ri = t * rpt + cn / G;
     if (cn >= rpt * G || ri >= nrows) continue;
-    const int w0 = tiled ? t : 0;
-    const int w1 = tiled ? t + 1 : kWaves;
+    const int w0 = t * wpt;
+    const int w1 = w0 + wpt;
     float M = -INFINITY;
     for (int w = w0; w < w1; ++w) M = fmaxf(M, st.m[w][cn]);
     float L = 0.f;

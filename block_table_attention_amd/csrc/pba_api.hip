@@ -356,14 +356,14 @@ int check_shared_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batc
                       int32_t* private_parts) {
   if (!plan) return PBA_ERR_NULL_ARG;
   if (pool->dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
-  if (plan->reserved0 != 0 || plan->num_items < 0 || plan->max_slots < 1) return PBA_ERR_BAD_SHAPE;
+  if (plan->private_parts < 0 || plan->num_items < 0 || plan->max_slots < 1) return PBA_ERR_BAD_SHAPE;
   const int32_t pt = plan->partition_tokens;
   if (pt <= 0 || pt % kPartGranule) return PBA_ERR_UNSUPPORTED;
   if (batch > 65535) return PBA_ERR_UNSUPPORTED;
   if (batch > 0 && (!plan->row_private || (plan->num_items > 0 && !plan->items)))
     return PBA_ERR_NULL_ARG;
   const int64_t max_T = (int64_t)max_blocks * pool->block_size;
-  const int64_t pp = (max_T + pt - 1) / pt;
+  const int64_t pp = plan->private_parts > 0 ? plan->private_parts : (max_T + pt - 1) / pt;
   const int64_t nz = batch > 0 ? ((int64_t)plan->num_items + batch - 1) / batch : 0;
   if (pp + nz > 65535) return PBA_ERR_UNSUPPORTED;
   if ((int64_t)batch * num_q_heads > INT32_MAX) return PBA_ERR_UNSUPPORTED;
@@ -394,8 +394,9 @@ int validate_shared_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t b
   for (int32_t i = 0; i < plan->num_items; ++i) {
     const int32_t* it = &items[(size_t)i * 8];
     const int32_t row0 = it[0], nrows = it[1], tb = it[2], te = it[3], slot = it[4];
-    const bool tiled = it[5] != 0;
-    if (row0 < 0 || nrows < 1 || nrows > (tiled ? 4 : 1) * rpt || (int64_t)row0 + nrows > batch)
+    const int32_t tiles = it[5];
+    if ((tiles != 1 && tiles != 2 && tiles != 4) || it[6] || it[7]) return PBA_ERR_OUT_OF_RANGE;
+    if (row0 < 0 || nrows < 1 || nrows > tiles * rpt || (int64_t)row0 + nrows > batch)
       return PBA_ERR_OUT_OF_RANGE;
     if (tb < 0 || te <= tb || tb % align || slot < 0 || slot >= plan->max_slots)
       return PBA_ERR_OUT_OF_RANGE;
@@ -417,6 +418,7 @@ int validate_shared_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t b
       spans[r].push_back({t, std::min<int64_t>(T, t + pt)});
       slots[r].push_back(ps + k);
     }
+    if (plan->private_parts > 0 && k > plan->private_parts) return PBA_ERR_OUT_OF_RANGE;
     std::sort(spans[r].begin(), spans[r].end());
     int64_t at = 0;
     for (const auto& sp : spans[r]) {

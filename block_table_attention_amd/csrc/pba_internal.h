@@ -59,7 +59,7 @@ struct DecodeArgs {
 };
 
 // Shared-prefix decode: chunk-first items (int32 x 8 each: row0, nrows, tb,
-// te, slot, tiled, 0, 0) and each row's private range (first token, slot).
+// te, slot, tiles, 0, 0) and each row's private range (first token, slot).
 struct SharedArgs {
   const int32_t* items;
   const int32_t* row_private;  // [batch][2]

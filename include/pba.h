@@ -190,10 +190,10 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
  *                  [0] row0, [1] nrows: the batch rows [row0, row0 + nrows)
  *                  [2] tb, [3] te: the key positions [tb, te) of those rows
  *                  [4] slot: index of the item's partial state in each row
- *                  [5] tiled: 0 -> nrows <= 16/G, the 4 waves of a work-group
- *                      split the positions; 1 -> nrows <= 4 * (16/G), each
- *                      wave takes 16/G rows and all positions (one K/V read
- *                      serves up to 64 query columns)
+ *                  [5] tiles: 1, 2 or 4 tiles of 16/G rows (16 columns);
+ *                      nrows <= tiles * (16/G).  The 4/tiles waves of a tile
+ *                      split its positions; one K/V read serves every tile,
+ *                      up to 64 query columns
  *                  [6], [7]: 0
  *   row_private  device int32 [batch][2]: (pb, ps): row r's positions
  *                [pb, T) are decoded alone in pieces of partition_tokens from
@@ -201,7 +201,8 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
  *
  * Contract (checked in validate mode, PBA_ERR_OUT_OF_RANGE / PBA_ERR_OVERLAP):
  * for every row the item ranges covering it and its private pieces tile
- * [0, T) exactly, and its slots are exactly 0 .. n-1 with n <= max_slots; tb
+ * [0, T) exactly, its slots are exactly 0 .. n-1 with n <= max_slots, its
+ * private pieces number at most private_parts (when that is nonzero); tb
  * and pb are multiples of min(P, 32); te <= T of every covered row; every
  * covered row maps blocks [tb/P, ceil(te/P)) to the same ids as row0.  Outside
  * validate mode a plan that breaks the contract gives undefined results but
@@ -214,7 +215,8 @@ typedef struct pba_shared_plan {
   int32_t num_items;
   int32_t max_slots;         /* partial states per (row, q-head) in the workspace */
   int32_t partition_tokens;  /* piece length: a positive multiple of 256 */
-  int32_t reserved0;         /* must be 0 */
+  int32_t private_parts;     /* bound on any row's private pieces, ceil((T - pb) /
+                                partition_tokens); 0: from the table width */
   const int32_t* items;
   const int32_t* row_private;
 } pba_shared_plan;

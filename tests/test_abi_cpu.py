@@ -244,8 +244,8 @@ def test_shared_decode_host_rejections():
     d = _desc()
     items, rowp = 0x90000, 0xA0000
 
-    def plan(num_items=2, max_slots=3, pt=256, reserved=0, it=items, rp=rowp):
-        return pba.SharedPlanDesc(num_items, max_slots, pt, reserved, it, rp)
+    def plan(num_items=2, max_slots=3, pt=256, private_parts=0, it=items, rp=rowp):
+        return pba.SharedPlanDesc(num_items, max_slots, pt, private_parts, it, rp)
 
     def call(desc, p, ws=0x80000, wsb=1 << 30, batch=2, q=0x30000):
         return lib.pba_paged_decode_shared(ctypes.byref(desc), q, 8, 0x40000, 4, 0x50000, batch,
@@ -256,7 +256,7 @@ def test_shared_decode_host_rejections():
     assert call(_desc(dtype=0), plan()) == -4            # bf16 only
     assert call(d, plan(pt=100)) == -4
     assert call(d, plan(pt=0)) == -4
-    assert call(d, plan(reserved=1)) == -3
+    assert call(d, plan(private_parts=-1)) == -3
     assert call(d, plan(max_slots=0)) == -3
     assert call(d, plan(num_items=-1)) == -3
     assert call(d, plan(it=None)) == -1

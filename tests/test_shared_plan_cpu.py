@@ -28,7 +28,7 @@ def _pieces(plan, lens):
     """Per row: list of (tb, te, slot) from items and private pieces."""
     B = len(lens)
     per = [[] for _ in range(B)]
-    for row0, nrows, tb, te, slot, tiled, _, _ in plan.items.tolist():
+    for row0, nrows, tb, te, slot, tiles, _, _ in plan.items.tolist():
         for r in range(row0, row0 + nrows):
             per[r].append((tb, te, slot))
     for r in range(B):
@@ -43,9 +43,9 @@ def _pieces(plan, lens):
 def check_contract(plan, tables, lens, P, G):
     rpt = 16 // G
     align = min(P, 32)
-    for row0, nrows, tb, te, slot, tiled, z0, z1 in plan.items.tolist():
+    for row0, nrows, tb, te, slot, tiles, z0, z1 in plan.items.tolist():
         assert z0 == 0 and z1 == 0 and tb % align == 0 and tb < te
-        assert 1 <= nrows <= (4 if tiled else 1) * rpt
+        assert tiles in (1, 2, 4) and 1 <= nrows <= tiles * rpt
         for r in range(row0, row0 + nrows):
             assert te <= lens[r]
             j0, j1 = tb // P, -(-te // P)
@@ -96,9 +96,14 @@ def test_shared_prefix_workload_plan(pt):
     assert plan_kv_rows(plan, lens) * 7 < logical     # 303,270 logical rows, 40,182 read
 
 
-def _items_per_piece(rows, G):
+def _items_per_piece(rows, G, per_item=4):
     tiles = -(-rows // (16 // G))
-    return -(-tiles // 4)
+    n = 0
+    while tiles > 0:
+        t = min(per_item, 4 if tiles >= 4 else (2 if tiles >= 2 else 1))
+        tiles -= t
+        n += 1
+    return n
 
 
 def test_no_sharing_is_all_private():
