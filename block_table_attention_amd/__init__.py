@@ -17,6 +17,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_plan",
+           "paged_decode_ragged", "expand_block_tables", "pack_block_tables",
            "paged_decode_shared", "paged_decode_shared_workspace_bytes", "SharedPlan",
            "paged_decode_workspace_bytes", "decode_workspace", "set_validate", "PBAError", "lib_path", "STATUS"]
 
@@ -46,7 +47,7 @@ class PoolDesc(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("dtype", ctypes.c_int32),
                 ("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
-                ("reserved0", ctypes.c_int32), ("k_stride_block", ctypes.c_int64),
+                ("split_log2", ctypes.c_int32), ("k_stride_block", ctypes.c_int64),
                 ("k_stride_head", ctypes.c_int64), ("v_stride_block", ctypes.c_int64),
                 ("v_stride_head", ctypes.c_int64)]
 
@@ -68,6 +69,10 @@ _SIGS = {
     "pba_paged_decode_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _i32]),
     "pba_paged_decode_plan": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
+    "pba_paged_decode_ragged": (ctypes.c_int, [_P, _vp, _i32, _vp, _vp, _i32, _vp, _i32,
+                                               ctypes.c_float, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "pba_expand_block_tables": (ctypes.c_int, [_vp, _i64, _i32, _vp, _vp]),
+    "pba_pack_block_tables": (ctypes.c_int, [_vp, _i32, _i32, _vp, _vp, _vp]),
     "pba_paged_decode_shared_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _SP]),
     "pba_paged_decode_shared": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float,
                                                _vp, _vp, _SP, _vp, _sz, _vp]),
@@ -112,6 +117,7 @@ class KVPool:
 
     k: torch.Tensor
     v: torch.Tensor
+    split_log2: int = 0   # > 0: kernel view, 2^split_log2 kernel blocks per tile
 
     def __post_init__(self):
         k, v = self.k, self.v
@@ -122,7 +128,10 @@ class KVPool:
             raise TypeError(f"pool dtype {k.dtype} not supported")
         if k.stride(2) != d or k.stride(3) != 1 or v.stride(2) != p or v.stride(3) != 1:
             raise ValueError("pool tiles must be dense ([P][d] for K, [d][P] for V)")
-        desc = PoolDesc(k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], nb, p, h, d, 0,
+        s = self.split_log2
+        if s < 0 or p % (1 << s):
+            raise ValueError("split_log2 must split the tile into whole kernel blocks")
+        desc = PoolDesc(k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], nb << s, p >> s, h, d, s,
                         k.stride(0), k.stride(1), v.stride(0), v.stride(1))
         object.__setattr__(self, "_desc", desc)
         object.__setattr__(self, "_ref", ctypes.byref(desc))
@@ -134,9 +143,18 @@ class KVPool:
         v = torch.empty((num_blocks, num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
         return cls(k, v)
 
+    def kernel_view(self, kernel_block_size: int) -> "KVPool":
+        """The same memory exposed as blocks of kernel_block_size tokens
+        (allocator block a = kernel blocks a q .. a q + q - 1): for the decode
+        calls, with tables from expand_block_tables."""
+        q = self.k.shape[2] // kernel_block_size
+        if q < 1 or q * kernel_block_size != self.k.shape[2] or q & (q - 1):
+            raise ValueError("the kernel block must divide the tile by a power of two")
+        return KVPool(self.k, self.v, q.bit_length() - 1)
+
     @property
     def num_blocks(self) -> int:
-        return self.k.shape[0]
+        return self.k.shape[0] << self.split_log2
 
     @property
     def num_kv_heads(self) -> int:
@@ -144,7 +162,7 @@ class KVPool:
 
     @property
     def block_size(self) -> int:
-        return self.k.shape[2]
+        return self.k.shape[2] >> self.split_log2
 
     @property
     def head_dim(self) -> int:
@@ -351,6 +369,67 @@ def paged_decode_shared(pool: KVPool, q: torch.Tensor, block_tables: torch.Tenso
         ctypes.c_float(scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
         plan._ref, ws_ptr, ws_bytes, _stream(stream)))
     return out, lse
+
+
+def paged_decode_ragged(pool: KVPool, q: torch.Tensor, block_entries: torch.Tensor,
+                        row_offsets: torch.Tensor, seq_lens: torch.Tensor, max_blocks_per_seq: int,
+                        scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                        lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                        partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    """paged_decode over a compact table: row r is block_entries[row_offsets[r] :
+    row_offsets[r + 1]] (int32 entries, int64 offsets [B + 1])."""
+    dev = pool.k.device
+    _require(q, "q", pool.dtype, dev, 3)
+    _require(block_entries, "block_entries", torch.int32, dev, 1)
+    _require(row_offsets, "row_offsets", torch.int64, dev, 1)
+    _require(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, Hq, D = q.shape
+    if D != pool.head_dim or row_offsets.shape[0] != B + 1 or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, row_offsets, seq_lens and the pool")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    if workspace is None and B > 0:
+        workspace = decode_workspace(pool, Hq, B, max_blocks_per_seq, partition_tokens, stream)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pba_paged_decode_ragged", _lib.pba_paged_decode_ragged(
+        pool._ref, q.data_ptr(), Hq, block_entries.data_ptr() if block_entries.numel() else None,
+        row_offsets.data_ptr(), max_blocks_per_seq, seq_lens.data_ptr(), B, ctypes.c_float(scale),
+        out.data_ptr(), None if lse is None else lse.data_ptr(), partition_tokens, ws_ptr,
+        ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def expand_block_tables(tables: torch.Tensor, split_log2: int, stream=None) -> torch.Tensor:
+    """Allocator ids -> kernel ids (a -> a q .. a q + q - 1; -1 stays -1); the
+    last axis grows q-fold."""
+    if tables.dtype != torch.int32 or not tables.is_contiguous():
+        raise ValueError("tables must be contiguous int32")
+    q = 1 << split_log2
+    out = torch.empty(tables.shape[:-1] + (tables.shape[-1] * q,), dtype=torch.int32,
+                      device=tables.device)
+    _check("pba_expand_block_tables", _lib.pba_expand_block_tables(
+        tables.data_ptr() if tables.numel() else None, tables.numel(), split_log2,
+        out.data_ptr() if out.numel() else None, _stream(stream)))
+    return out
+
+
+def pack_block_tables(tables: torch.Tensor, row_offsets: torch.Tensor, total: int,
+                      stream=None) -> torch.Tensor:
+    """Dense [B, width] table -> compact entries (row r at row_offsets[r]);
+    ``total`` = row_offsets[B], known to the caller that computed the offsets."""
+    _require(tables, "tables", torch.int32, tables.device, 2)
+    _require(row_offsets, "row_offsets", torch.int64, tables.device, 1)
+    out = torch.empty(max(total, 1), dtype=torch.int32, device=tables.device)
+    B, width = tables.shape
+    _check("pba_pack_block_tables", _lib.pba_pack_block_tables(
+        tables.data_ptr(), B, width, row_offsets.data_ptr(), out.data_ptr(), _stream(stream)))
+    return out[:total]
 
 
 def set_validate(on: bool) -> bool:

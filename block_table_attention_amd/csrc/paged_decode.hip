@@ -227,7 +227,15 @@ struct PoolView {
   int max_blocks;
   int last_block;  // num_blocks - 1: clamp for ids read ahead of the length
   int log2P;
+  int split;       // kernel view: allocator tiles hold P << split rows
 };
+
+// Kernel block pb of a (possibly split) pool: allocator tile pb >> split, its
+// rows starting at (pb mod 2^split) * P.
+__device__ __forceinline__ int64_t tile_of(const PoolView& pv, int64_t pb) { return pb >> pv.split; }
+__device__ __forceinline__ int row_of(const PoolView& pv, int64_t pb) {
+  return (int)(pb & ((1 << pv.split) - 1)) << pv.log2P;
+}
 
 // Physical block ids of the chunk starting at t0 (one when P >= 32, two when
 // P == 16).  Ids are clamped into the pool so that a lookup made before the
@@ -250,8 +258,9 @@ __device__ __forceinline__ void load_k(u32x4 (&kf)[2][D / 32], const PoolView& p
     // A-operand row n of tile `at` holds chunk token 8(n>>2) + 4at + (n&3).
     const int tk = 8 * (n >> 2) + 4 * at + (n & 3);
     const int64_t pb = (tk >= 16 && pv.log2P == 4) ? pb1 : pb0;
-    const int off = (t0 + tk) & (P - 1);
-    const uint16_t* kp = pv.k + pb * pv.k_sb + (int64_t)h * pv.k_sh + (int64_t)off * D + 8 * g;
+    const int off = row_of(pv, pb) + ((t0 + tk) & (P - 1));
+    const uint16_t* kp =
+        pv.k + tile_of(pv, pb) * pv.k_sb + (int64_t)h * pv.k_sh + (int64_t)off * D + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) kf[at][kk] = *reinterpret_cast<const u32x4*>(kp + 32 * kk);
   }
@@ -264,11 +273,13 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
   // A-operand row n of tile mt is dim 16mt + n; its k-slots are tokens 8g..8g+7.
   const int tv = 8 * g;
   const int64_t pb = (tv >= 16 && pv.log2P == 4) ? pb1 : pb0;
-  const int off = (t0 + tv) & (P - 1);
-  const uint16_t* vp = pv.v + pb * pv.v_sb + (int64_t)h * pv.v_sh + (int64_t)n * P + off;
+  const int Pa = P << pv.split;  // rows of an allocator tile: V's dim stride
+  const int off = row_of(pv, pb) + ((t0 + tv) & (P - 1));
+  const uint16_t* vp =
+      pv.v + tile_of(pv, pb) * pv.v_sb + (int64_t)h * pv.v_sh + (int64_t)n * Pa + off;
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt)
-    vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * P);
+    vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * Pa);
 }
 
 // One 32-token chunk of a wave: the score product over its K fragments, the
@@ -364,7 +375,7 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
 // XCDs round-robin in linear order, so with the partition as the slowest axis
 // every XCD gets an even share of the first partitions (never empty) and of
 // the later ones (empty past a short request's end).
-template <int D>
+template <int D, bool RAGGED>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
     const void* __restrict__ kbase, const void* __restrict__ vbase, int32_t max_blocks,
@@ -387,10 +398,22 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   const int g = lane >> 4;  // k-group of this lane
   const int G = a.G;
   const int p_begin = part * part_tokens;
-  const PoolView pv{(table_t*)(tables + (int64_t)r * max_blocks),
+  // Dense tables: row r at r * max_blocks.  Ragged tables: row r is entries
+  // [row_offsets[r], row_offsets[r + 1]) of one array (one more scalar round
+  // trip before the first table read).
+  int64_t toff = (int64_t)r * max_blocks;
+  int nblk = max_blocks;
+  if constexpr (RAGGED) {
+    const int64_t __attribute__((address_space(4)))* ro =
+        (const int64_t __attribute__((address_space(4)))*)a.row_offsets;
+    toff = ro[r];
+    nblk = (int)(ro[r + 1] - toff);
+    if (nblk < 1) return;  // an empty row (rejected in validate mode)
+  }
+  const PoolView pv{(table_t*)(tables + toff),
                     static_cast<const uint16_t*>(kbase),
                     static_cast<const uint16_t*>(vbase),
-                    k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P};
+                    k_sb, k_sh, a.v_sb, a.v_sh, nblk, last_block, log2P, a.split_log2};
 
   // Start-up: the request length and this wave's first block-table entries
   // come back in one scalar round trip; q and the first chunk's K and V are
@@ -405,7 +428,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   // after the test on it (which would add a scalar round trip).
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
   const int num_q_heads = a.num_q_heads;
-  asm volatile("" ::"s"(qbase), "s"(num_q_heads), "s"(G), "s"(pv.v_sb), "s"(pv.v_sh));
+  asm volatile("" ::"s"(qbase), "s"(num_q_heads), "s"(G), "s"(pv.v_sb), "s"(pv.v_sh),
+               "s"(pv.split));
   if (p_begin >= T) return;  // empty partition: never counted, never read
   const int p_end = min(T, p_begin + part_tokens);
   // This wave's chunks: p_begin + wave*CH + k*kWaves*CH for k < n_w.
@@ -552,7 +576,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
 
   const PoolView pv{(table_t*)(tables + (int64_t)row0 * max_blocks),
                     static_cast<const uint16_t*>(kbase), static_cast<const uint16_t*>(vbase),
-                    k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P};
+                    k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P, a.split_log2};
   // This wave's columns and chunk walk: wpt waves per tile split its chunks.
   const int wpt = kWaves / tiles;
   const int tile = wave / wpt;
@@ -713,7 +737,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
 
   const float* kpool = static_cast<const float*>(a.k);
   const float* vpool = static_cast<const float*>(a.v);
-  const int32_t* trow = a.tables + (int64_t)r * a.max_blocks;
+  // Dense or ragged row of the block table (see decode_bf16_kernel).
+  const int32_t* trow =
+      a.tables + (a.row_offsets ? a.row_offsets[r] : (int64_t)r * a.max_blocks);
+  const int split = a.split_log2;
+  const int qmask = (1 << split) - 1;
 
   float m_run[16], l_run[16], u[16][DPL];
 #pragma unroll
@@ -729,7 +757,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
     const bool valid = t < T;
     const int j = min(t >> log2P, nblk - 1);
     const int64_t pb = trow[j];
-    const float* krow = kpool + pb * a.k_sb + (int64_t)h * a.k_sh + (int64_t)(t & (P - 1)) * D;
+    const float* krow = kpool + (pb >> split) * a.k_sb + (int64_t)h * a.k_sh +
+                        (int64_t)(((int)(pb & qmask) << log2P) + (t & (P - 1))) * D;
     float s[16];
 #pragma unroll
     for (int gg = 0; gg < 16; ++gg) s[gg] = 0.f;
@@ -773,8 +802,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
         const int c = lane + 64 * e;
-        f32x4 vv = *reinterpret_cast<const f32x4*>(vpool + pbv * a.v_sb + (int64_t)h * a.v_sh +
-                                                   (int64_t)c * P + off);
+        f32x4 vv = *reinterpret_cast<const f32x4*>(
+            vpool + (pbv >> split) * a.v_sb + (int64_t)h * a.v_sh + (int64_t)c * (P << split) +
+            ((int)(pbv & qmask) << log2P) + off);
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (tt + q >= T) vv[q] = 0.f;
@@ -815,7 +845,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     DecodeArgs s = a;
     const int64_t rows = (int64_t)r0 * a.num_q_heads;
     s.q = static_cast<const char*>(a.q) + rows * head_dim * (dtype == PBA_BF16 ? 2 : 4);
-    s.tables = a.tables + (int64_t)r0 * a.max_blocks;
+    if (a.row_offsets)
+      s.row_offsets = a.row_offsets + r0;  // entries stay put: offsets are absolute
+    else
+      s.tables = a.tables + (int64_t)r0 * a.max_blocks;
     s.seq_lens = a.seq_lens + r0;
     s.out = a.out + rows * head_dim;
     s.lse = a.lse ? a.lse + rows : nullptr;
@@ -826,7 +859,9 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     const dim3 grid((unsigned)a.num_kv_heads, (unsigned)nb, (unsigned)a.n_parts);
     const dim3 block(kDecodeThreads);
     if (dtype == PBA_BF16) {
-      auto kern = head_dim == 128 ? decode_bf16_kernel<128> : decode_bf16_kernel<64>;
+      auto kern = a.row_offsets
+                      ? (head_dim == 128 ? decode_bf16_kernel<128, true> : decode_bf16_kernel<64, true>)
+                      : (head_dim == 128 ? decode_bf16_kernel<128, false> : decode_bf16_kernel<64, false>);
       hipLaunchKernelGGL(kern, grid, block, 0, stream, s.tables, s.seq_lens, s.k, s.v,
                          s.max_blocks, s.part_tokens, s.log2P, s.num_blocks - 1,
                          (int32_t)s.k_sb, (int32_t)s.k_sh, s);

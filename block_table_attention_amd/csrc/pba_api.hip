@@ -35,13 +35,17 @@ int check_pool(const pba_kv_pool* pool) {
   if (!pool) return PBA_ERR_NULL_ARG;
   if (pool->dtype != PBA_F32 && pool->dtype != PBA_BF16) return PBA_ERR_BAD_DTYPE;
   if (pool->num_blocks <= 0 || pool->num_kv_heads <= 0 || pool->block_size <= 0 ||
-      pool->head_dim <= 0 || pool->reserved0 != 0)
+      pool->head_dim <= 0 || pool->split_log2 < 0)
     return PBA_ERR_BAD_SHAPE;
   const int lp = log2_exact(pool->block_size);
   if (lp < 4 || lp > 8) return PBA_ERR_UNSUPPORTED;  // P in {16, ..., 256}
   if (pool->head_dim != 64 && pool->head_dim != 128) return PBA_ERR_UNSUPPORTED;
+  if (pool->split_log2 > 4) return PBA_ERR_UNSUPPORTED;  // at most 16 kernel blocks per tile
+  if (pool->num_blocks % (1 << pool->split_log2)) return PBA_ERR_BAD_SHAPE;
   if (!pool->k || !pool->v) return PBA_ERR_NULL_ARG;
-  const int64_t tile = (int64_t)pool->block_size * pool->head_dim;
+  // An allocator tile holds P << split_log2 rows.
+  const int64_t tile = ((int64_t)pool->block_size << pool->split_log2) * pool->head_dim;
+  const int64_t tiles = pool->num_blocks >> pool->split_log2;
   const int es = esize_of(pool->dtype);
   const int64_t strides[4] = {pool->k_stride_block, pool->k_stride_head, pool->v_stride_block,
                               pool->v_stride_head};
@@ -52,8 +56,7 @@ int check_pool(const pba_kv_pool* pool) {
   // A tile must fit in its stride, and the heads of one block in the block stride.
   if (pool->num_kv_heads > 1 && (pool->k_stride_head < tile || pool->v_stride_head < tile))
     return PBA_ERR_BAD_SHAPE;
-  if (pool->num_blocks > 1 &&
-      (pool->k_stride_block < tile || pool->v_stride_block < tile))
+  if (tiles > 1 && (pool->k_stride_block < tile || pool->v_stride_block < tile))
     return PBA_ERR_BAD_SHAPE;
   if (!aligned16(pool->k) || !aligned16(pool->v)) return PBA_ERR_UNSUPPORTED;
   return PBA_OK;
@@ -186,6 +189,7 @@ int pba_kv_append(const pba_kv_pool* pool, const int64_t* slot_mapping, int64_t 
                   const void* k_new, const void* v_new, void* stream) {
   int st = check_pool(pool);
   if (st) return st;
+  if (pool->split_log2) return PBA_ERR_UNSUPPORTED;  // writes use the allocator view
   if (n_tokens < 0) return PBA_ERR_BAD_SHAPE;
   if (n_tokens == 0) return PBA_OK;
   if (!slot_mapping || !k_new || !v_new) return PBA_ERR_NULL_ARG;
@@ -225,6 +229,7 @@ int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* d
                    int64_t n_pairs, void* stream) {
   int st = check_pool(pool);
   if (st) return st;
+  if (pool->split_log2) return PBA_ERR_UNSUPPORTED;  // copies use the allocator view
   if (n_pairs < 0) return PBA_ERR_BAD_SHAPE;
   if (n_pairs == 0) return PBA_OK;
   if (!src || !dst) return PBA_ERR_NULL_ARG;
@@ -279,11 +284,13 @@ size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_h
                           pool->head_dim).bytes;
 }
 
-int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
-                     const int32_t* block_tables, int32_t max_blocks_per_seq,
-                     const int32_t* seq_lens, int32_t batch, float scale, float* out, float* lse,
-                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
-                     void* stream) {
+// Dense (row_offsets == nullptr: row r at r * max_blocks_per_seq) or ragged
+// (row r = block_tables[row_offsets[r] .. row_offsets[r + 1])) decode.
+static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                       const int32_t* block_tables, const int64_t* row_offsets,
+                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                       float scale, float* out, float* lse, int32_t partition_tokens,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
   const int G = num_q_heads / pool->num_kv_heads;
@@ -302,15 +309,27 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g_validate.load()) {
     std::vector<int32_t> lens, tab;
+    std::vector<int64_t> offs;
     if (!copy_to_host(lens, seq_lens, batch, s)) return PBA_ERR_HIP;
-    if (!copy_to_host(tab, block_tables, (int64_t)batch * max_blocks_per_seq, s)) return PBA_ERR_HIP;
+    if (row_offsets) {
+      if (!copy_to_host(offs, row_offsets, (int64_t)batch + 1, s)) return PBA_ERR_HIP;
+      if (offs[0] < 0) return PBA_ERR_OUT_OF_RANGE;
+      for (int32_t r = 0; r < batch; ++r)
+        if (offs[r + 1] < offs[r] || offs[r + 1] - offs[r] > max_blocks_per_seq)
+          return PBA_ERR_OUT_OF_RANGE;
+      if (!copy_to_host(tab, block_tables, offs[batch], s)) return PBA_ERR_HIP;
+    } else {
+      if (!copy_to_host(tab, block_tables, (int64_t)batch * max_blocks_per_seq, s)) return PBA_ERR_HIP;
+    }
     const int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
     for (int32_t r = 0; r < batch; ++r) {
       const int64_t T = lens[r];
       if (T < 1 || T > cap) return PBA_ERR_OUT_OF_RANGE;
       const int64_t nb = (T + pool->block_size - 1) / pool->block_size;
+      const int64_t base = row_offsets ? offs[r] : (int64_t)r * max_blocks_per_seq;
+      if (row_offsets && offs[r + 1] - offs[r] < nb) return PBA_ERR_OUT_OF_RANGE;
       for (int64_t j = 0; j < nb; ++j) {
-        const int32_t b = tab[(size_t)r * max_blocks_per_seq + j];
+        const int32_t b = tab[(size_t)(base + j)];
         if (b < 0 || b >= pool->num_blocks) return PBA_ERR_OUT_OF_RANGE;
       }
     }
@@ -333,6 +352,8 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   a.ws_u = need ? reinterpret_cast<float*>(wsb + ws.u_off) : nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = pool->num_blocks;
+  a.split_log2 = pool->split_log2;
+  a.row_offsets = row_offsets;
   a.log2P = log2_exact(pool->block_size);
   a.G = G;
   a.num_q_heads = num_q_heads;
@@ -343,6 +364,63 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
   a.scale_log2 = scale * 1.4426950408889634f;
   return pba::launch_paged_decode(a, pool->dtype, pool->head_dim, s) == hipSuccess ? PBA_OK
                                                                                   : PBA_ERR_HIP;
+}
+
+int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* seq_lens, int32_t batch, float scale, float* out, float* lse,
+                     int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return decode_impl(pool, q, num_q_heads, block_tables, nullptr, max_blocks_per_seq, seq_lens,
+                     batch, scale, out, lse, partition_tokens, workspace, workspace_bytes, stream);
+}
+
+int pba_paged_decode_ragged(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* block_entries, const int64_t* row_offsets,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                            float scale, float* out, float* lse, int32_t partition_tokens,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch > 0 && !row_offsets) return PBA_ERR_NULL_ARG;
+  return decode_impl(pool, q, num_q_heads, block_entries, row_offsets, max_blocks_per_seq,
+                     seq_lens, batch, scale, out, lse, partition_tokens, workspace,
+                     workspace_bytes, stream);
+}
+
+int pba_expand_block_tables(const int32_t* src, int64_t n_entries, int32_t split_log2,
+                            int32_t* dst, void* stream) {
+  if (n_entries < 0 || split_log2 < 0) return PBA_ERR_BAD_SHAPE;
+  if (split_log2 > 4) return PBA_ERR_UNSUPPORTED;
+  if (n_entries == 0) return PBA_OK;
+  if (!src || !dst) return PBA_ERR_NULL_ARG;
+  if ((n_entries << split_log2) / 256 + 1 > INT32_MAX) return PBA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    std::vector<int32_t> h;
+    if (!copy_to_host(h, src, n_entries, s)) return PBA_ERR_HIP;
+    for (int32_t a : h)
+      if (a >= 0 && (int64_t)a << split_log2 > INT32_MAX) return PBA_ERR_OUT_OF_RANGE;
+  }
+  return pba::launch_expand_tables(src, n_entries, split_log2, dst, s) == hipSuccess ? PBA_OK
+                                                                                     : PBA_ERR_HIP;
+}
+
+int pba_pack_block_tables(const int32_t* src, int32_t batch, int32_t width,
+                          const int64_t* row_offsets, int32_t* dst, void* stream) {
+  if (batch < 0 || width < 0) return PBA_ERR_BAD_SHAPE;
+  if (batch == 0 || width == 0) return PBA_OK;
+  if (batch > 65535) return PBA_ERR_UNSUPPORTED;
+  if (!src || !row_offsets || !dst) return PBA_ERR_NULL_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    std::vector<int64_t> offs;
+    if (!copy_to_host(offs, row_offsets, (int64_t)batch + 1, s)) return PBA_ERR_HIP;
+    if (offs[0] < 0) return PBA_ERR_OUT_OF_RANGE;
+    for (int32_t r = 0; r < batch; ++r)
+      if (offs[r + 1] < offs[r] || offs[r + 1] - offs[r] > width) return PBA_ERR_OUT_OF_RANGE;
+  }
+  return pba::launch_pack_tables(src, batch, width, row_offsets, dst, s) == hipSuccess
+             ? PBA_OK
+             : PBA_ERR_HIP;
 }
 
 }  // extern "C"
@@ -504,6 +582,8 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
   a.ws_u = ws.bytes ? reinterpret_cast<float*>(wsb + ws.u_off) : nullptr;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = pool->num_blocks;
+  a.split_log2 = pool->split_log2;
+  a.row_offsets = nullptr;
   a.log2P = log2_exact(pool->block_size);
   a.G = num_q_heads / pool->num_kv_heads;
   a.num_q_heads = num_q_heads;

@@ -46,6 +46,8 @@ struct DecodeArgs {
   float* ws_ml;  // [B][H_q][n_parts][2]: running max (log2 domain), sum
   float* ws_u;   // [B][H_q][n_parts][D]: unnormalised output
   int32_t* counters;  // [B][H_kv]: partitions finished; zero between calls
+  const int64_t* row_offsets;  // ragged tables: row r = tables[row_offsets[r] ..
+                               // row_offsets[r + 1]); nullptr for dense tables
   int32_t max_blocks;
   int32_t num_blocks;  // pool size: clamp for block ids read ahead of the length
   int32_t log2P;
@@ -56,6 +58,7 @@ struct DecodeArgs {
   int32_t part_tokens;
   int32_t n_parts;
   float scale_log2;  // scale * log2(e): scores live in the log2 domain
+  int32_t split_log2;  // kernel view of an allocator pool: tiles of P << split rows
 };
 
 // Shared-prefix decode: chunk-first items (int32 x 8 each: row0, nrows, tb,
@@ -67,6 +70,10 @@ struct SharedArgs {
   int32_t nz_items;  // grid z planes of chunk-first items: ceil(n_items / batch)
 };
 
+hipError_t launch_expand_tables(const int32_t* src, int64_t n_src, int split_log2, int32_t* dst,
+                                hipStream_t stream);
+hipError_t launch_pack_tables(const int32_t* src, int32_t batch, int32_t width,
+                              const int64_t* offsets, int32_t* dst, hipStream_t stream);
 hipError_t launch_kv_append(const AppendArgs& a, int esize, hipStream_t stream);
 hipError_t launch_block_copy(const CopyArgs& a, int64_t n_pairs, int kv_heads, hipStream_t stream);
 hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hipStream_t stream);

@@ -71,6 +71,18 @@ typedef enum pba_dtype { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
  * Requirements: block_size (P) in {16, 32, 64, 128, 256}; head_dim in
  * {64, 128}; k, v and every tile 16-byte aligned; a (block, head) tile of
  * P * head_dim elements must fit inside its stride.
+ *
+ * Kernel view of an allocator pool ("M5.3", 0x0AC): with split_log2 = s > 0
+ * the memory holds tiles of P_a = P << s rows (allocator blocks), and the
+ * descriptor exposes each as q = 2^s kernel blocks of P rows: kernel block b
+ * is rows [(b mod q) P, (b mod q + 1) P) of tile b >> s, so
+ *   K: k[(b >> s) * k_stride_block + h * k_stride_head + ((b mod q) P + o) * head_dim + c]
+ *   V: v[(b >> s) * v_stride_block + h * v_stride_head + c * P_a + (b mod q) P + o]
+ * num_blocks counts kernel blocks (a multiple of q), and block tables hold
+ * kernel ids (pba_expand_block_tables makes them from allocator ids).  Slot
+ * ids are the same in both views (b P + o = a P_a + i P + o).  Only the
+ * decode calls accept s > 0 (at most 4); kv_append and block_copy take the
+ * allocator view (s = 0, block_size P_a) of the same memory.
  */
 typedef struct pba_kv_pool {
   void* k;
@@ -80,7 +92,7 @@ typedef struct pba_kv_pool {
   int32_t block_size;    /* P: tokens per block (block_granularity)          */
   int32_t num_kv_heads;  /* H_kv                                             */
   int32_t head_dim;      /* d                                                */
-  int32_t reserved0;     /* must be 0                                        */
+  int32_t split_log2;    /* 0, or the kernel view of an allocator pool: see above */
   int64_t k_stride_block, k_stride_head;
   int64_t v_stride_block, v_stride_head;
 } pba_kv_pool;
@@ -164,6 +176,44 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
                      const int32_t* seq_lens, int32_t batch, float scale, float* out, float* lse,
                      int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                      void* stream);
+
+/*
+ * pba_paged_decode_ragged -- pba_paged_decode over a compact block table
+ * ("M5.3", 0x0AB): row r's entries are block_entries[row_offsets[r] ..
+ * row_offsets[r + 1]) (at least ceil(T_r / P) of them) instead of a dense
+ * [batch, max_blocks_per_seq] row.  row_offsets: device int64 [batch + 1],
+ * non-decreasing, from 0 or more; max_blocks_per_seq bounds every row's entry
+ * count and plans the partitions exactly as for the dense call (the same
+ * workspace size).  Validate mode checks the offsets and the visible entries.
+ * Each work-group reads its row's two offsets before its first table entry
+ * (one more scalar round trip than the dense call).
+ */
+int pba_paged_decode_ragged(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* block_entries, const int64_t* row_offsets,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
+                            float scale, float* out, float* lse, int32_t partition_tokens,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pba_expand_block_tables -- allocator ids to kernel ids ("M5.3", 0x0AC): for
+ * each of the n_entries input entries a, the q = 2^split_log2 outputs at
+ * positions q*i .. q*i + q - 1 are a*q .. a*q + q - 1, or -1 when a < 0
+ * (padding).  A dense [B, n] table becomes a dense [B, n q] one, a compact one
+ * a compact one with every offset times q.  dst: device int32 [n_entries * q].
+ * Ids times q must fit in int32 (validate mode: PBA_ERR_OUT_OF_RANGE).
+ */
+int pba_expand_block_tables(const int32_t* src, int64_t n_entries, int32_t split_log2,
+                            int32_t* dst, void* stream);
+
+/*
+ * pba_pack_block_tables -- dense [batch, width] table to a compact one
+ * ("M5.3", 0x0AB): dst[row_offsets[r] + j] = src[r, j] for
+ * j < row_offsets[r + 1] - row_offsets[r] (<= width; validate mode checks the
+ * offsets).  The caller computes the offsets (prefix sums of its rows' block
+ * counts) and sizes dst to row_offsets[batch] entries; batch <= 65535.
+ */
+int pba_pack_block_tables(const int32_t* src, int32_t batch, int32_t width,
+                          const int64_t* row_offsets, int32_t* dst, void* stream);
 
 /* Workspace bytes pba_paged_decode needs for these arguments (0 when one
  * partition per row suffices); returns 0 for arguments it would reject. */

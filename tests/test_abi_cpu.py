@@ -30,7 +30,7 @@ def _desc(**kw):
     import block_table_attention_amd as pba
 
     d = dict(k=0x10000, v=0x20000, dtype=1, num_blocks=8, block_size=16, num_kv_heads=2,
-             head_dim=128, reserved0=0, k_stride_block=2 * 16 * 128, k_stride_head=16 * 128,
+             head_dim=128, split_log2=0, k_stride_block=2 * 16 * 128, k_stride_head=16 * 128,
              v_stride_block=2 * 16 * 128, v_stride_head=16 * 128)
     d.update(kw)
     return pba.PoolDesc(**d)
@@ -52,7 +52,9 @@ NULL = None
     (dict(head_dim=96), -4),
     (dict(num_blocks=0), -3),
     (dict(num_kv_heads=0), -3),
-    (dict(reserved0=1), -3),
+    (dict(split_log2=-1), -3),
+    (dict(split_log2=5), -4),
+    (dict(split_log2=1, num_blocks=7), -3),       # kernel blocks not a multiple of q
     (dict(k=0), -1),
     (dict(k=0x10008), -4),
     (dict(k_stride_head=1024), -3),
@@ -274,3 +276,28 @@ def test_shared_decode_host_rejections():
     assert lib.pba_paged_decode_shared_workspace_bytes(
         ctypes.byref(_desc(dtype=0)), 8, 2, 4, ctypes.byref(plan())) == 0
     assert call(d, plan(), q=0x30008) == -4
+
+
+def test_kernel_view_host_rules():
+    """A kernel view (split_log2 > 0) is for the decode calls only: kv_append
+    and block_copy reject it before any launch; expansion and packing reject
+    bad sizes."""
+    import block_table_attention_amd as pba
+
+    lib = _lib()
+    # Tiles of 32 rows (the allocator view's strides) seen as 16-row kernel blocks.
+    view = _desc(split_log2=1, num_blocks=8, block_size=16, k_stride_head=32 * 128,
+                 v_stride_head=32 * 128, k_stride_block=2 * 32 * 128, v_stride_block=2 * 32 * 128)
+    assert lib.pba_kv_append(ctypes.byref(view), 0x30000, 4, 0x40000, 0x50000, NULL) == -4
+    assert lib.pba_block_copy(ctypes.byref(view), 0x30000, 0x30010, 4, NULL) == -4
+    need = lib.pba_paged_decode_workspace_bytes(ctypes.byref(view), 8, 2, 64, 256)
+    assert need > 0
+    assert lib.pba_expand_block_tables(0x1000, 4, 5, 0x2000, NULL) == -4
+    assert lib.pba_expand_block_tables(0x1000, -1, 1, 0x2000, NULL) == -3
+    assert lib.pba_expand_block_tables(NULL, 0, 1, NULL, NULL) == 0
+    assert lib.pba_expand_block_tables(NULL, 4, 1, 0x2000, NULL) == -1
+    assert lib.pba_pack_block_tables(0x1000, 70000, 4, 0x2000, 0x3000, NULL) == -4
+    assert lib.pba_pack_block_tables(0x1000, 2, -1, 0x2000, 0x3000, NULL) == -3
+    assert lib.pba_pack_block_tables(NULL, 2, 4, 0x2000, 0x3000, NULL) == -1
+    assert lib.pba_paged_decode_ragged(ctypes.byref(view), 0x30000, 8, 0x40000, NULL, 4, 0x50000,
+                                       2, ctypes.c_float(0.1), 0x60000, NULL, 0, NULL, 0, NULL) == -1
