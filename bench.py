@@ -61,6 +61,11 @@ def parse():
                     help="piece length of the shared-prefix plan")
     ap.add_argument("--shared-tiles", type=int, default=2, choices=[1, 2, 4],
                     help="16-column tiles per chunk-first item of the shared-prefix plan")
+    ap.add_argument("--tables", default="dense", choices=["dense", "ragged"],
+                    help="block tables as a dense [B, n_max] array or compact rows with offsets")
+    ap.add_argument("--kernel-block", type=int, default=0,
+                    help="decode through a kernel view of this many tokens per block (the "
+                         "allocator blocks split; tables expanded by the library)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--decode-only", action="store_true",
@@ -277,18 +282,43 @@ def run_workload(args, name, pba, torch, dev):
     q = dev_bits(qb)
     tab_d = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
     lens_d = torch.from_numpy(np.ascontiguousarray(lens_h)).to(dev)
+    # Table encodings of the plain path: a kernel view of the pool (tables
+    # expanded by the library) and/or compact rows with offsets.
+    dpool = pool
+    split = 0
+    row_offsets = None
+    table_cells = int(tab_d.numel())
+    expand_us = None
+    if host_plan is None and getattr(args, "kernel_block", 0):
+        dpool = pool.kernel_view(args.kernel_block)
+        split = dpool.split_log2
+        tab_a = tab_d
+        pba.expand_block_tables(tab_a, split)          # first launch loads the code
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tab_d = pba.expand_block_tables(tab_a, split)
+        e1.record()
+        torch.cuda.synchronize()
+        expand_us = round(e0.elapsed_time(e1) * 1e3, 2)
+    if host_plan is None and getattr(args, "tables", "dense") == "ragged":
+        n_r = -(-lens_h.astype(np.int64) // P) << split   # whole expanded groups
+        offs = np.zeros(len(n_r) + 1, dtype=np.int64)
+        offs[1:] = np.cumsum(n_r)
+        row_offsets = torch.from_numpy(offs).to(dev)
+        tab_d = pba.pack_block_tables(tab_d, row_offsets, int(offs[-1]))
+        table_cells = int(offs[-1])
     scale = 1.0 / math.sqrt(d)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
-    mb = plan.tables.shape[1]
+    mb = plan.tables.shape[1] << split
     # The bench is the caller: it knows the lengths and may pick the split.
     req_pt = args.partition_tokens
     if req_pt < 0:
         from block_table_attention_amd.blocks import suggest_partition_tokens
         req_pt = suggest_partition_tokens(plan.seq_lens, Hkv)
     if host_plan is None:
-        pt, n_parts = pba.paged_decode_plan(pool, Hq, B, mb, req_pt)
-        ws_bytes = pba.paged_decode_workspace_bytes(pool, Hq, B, mb, req_pt)
+        pt, n_parts = pba.paged_decode_plan(dpool, Hq, B, mb, req_pt)
+        ws_bytes = pba.paged_decode_workspace_bytes(dpool, Hq, B, mb, req_pt)
     else:
         splan = pba.SharedPlan.from_host(host_plan, dev)
         pt, n_parts = host_plan.partition_tokens, host_plan.max_slots
@@ -299,8 +329,11 @@ def run_workload(args, name, pba, torch, dev):
     torch.cuda.synchronize()
 
     def decode(st=stream):
-        if host_plan is None:
-            pba.paged_decode(pool, q, tab_d, lens_d, scale, out=out, lse=lse,
+        if host_plan is None and row_offsets is not None:
+            pba.paged_decode_ragged(dpool, q, tab_d, row_offsets, lens_d, mb, scale, out=out,
+                                    lse=lse, partition_tokens=req_pt, workspace=ws, stream=st)
+        elif host_plan is None:
+            pba.paged_decode(dpool, q, tab_d, lens_d, scale, out=out, lse=lse,
                              partition_tokens=req_pt, workspace=ws, stream=st)
         else:
             pba.paged_decode_shared(pool, q, tab_d, lens_d, splan, scale, out=out, lse=lse,
@@ -405,6 +438,10 @@ def run_workload(args, name, pba, torch, dev):
                    ("library plan" if req_pt == 0 else
                     ("caller (suggest_partition_tokens)" if args.partition_tokens < 0 else "fixed")),
                    "decode_path": path,
+                   "tables": "ragged" if row_offsets is not None else "dense",
+                   "table_cells": table_cells,
+                   "kernel_block": P >> split,
+                   "expand_us": expand_us,
                    "shared_plan": None if host_plan is None else
                    {"chunks": len(host_plan.chunks), "items": int(host_plan.items.shape[0]),
                     "max_slots": host_plan.max_slots,
