@@ -408,7 +408,8 @@ def run_workload(args, name, pba, torch, dev):
     kv_unique, kv_logical, alg_bytes = decode_bytes(plan, sh)
     traffic = (profiled_traffic(name if host_plan is None else f"shared_{name}")
                if args.partition_tokens < 0 and args.shared_partition_tokens == 1024
-               and args.shared_tiles == 2 else None)
+               and args.shared_tiles == 2 and args.tables == "dense"
+               and args.kernel_block == 0 else None)
     step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg_ms * 1e-3) / 1e9
     lens = plan.seq_lens
