@@ -24,6 +24,15 @@ What it computes, and where the pages define it:
 * ``ledgers`` -- block counts, tails, table cells, copy-on-write costs and the
   other byte/row ledgers the pages print.  "M5.3", sections 0x02, 0x05A, 0x09,
   0x0AB, 0x0BE, 0x0BI, 0x0D; "7. Memory Management and Local Model State".
+* ``shared`` -- shared-prefix execution reuse over a chunk tree: the
+  monolithic, Hydragen and ChunkAttention schedules and their row ledgers.
+  "M5.3", sections 0x0BA-0x0BE.
+* ``views`` -- kernel views of allocator blocks (P_a = q P_k) and compact
+  (ragged) block tables.  "M5.3", sections 0x0AB-0x0AC.
+* ``bundles`` -- cache groups with a layer axis in a declared axis order,
+  whole-bundle appends and copies, and the all-or-nothing multi-group
+  allocator with rollback.  "M5.3", sections 0x03B-0x03F, 0x04E-0x04F,
+  0x05B-0x05C.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values the pages
 print, closed forms, invariants, an independent library routine or brute force.
