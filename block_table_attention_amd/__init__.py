@@ -19,7 +19,8 @@ import torch
 __all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_plan",
            "paged_decode_ragged", "expand_block_tables", "pack_block_tables",
            "paged_decode_shared", "paged_decode_shared_workspace_bytes", "SharedPlan",
-           "paged_decode_workspace_bytes", "decode_workspace", "set_validate", "PBAError", "lib_path", "STATUS"]
+           "paged_decode_workspace_bytes", "decode_workspace", "KVGroup", "kv_append_bundle",
+           "block_copy_bundle", "set_validate", "PBAError", "lib_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -39,7 +40,9 @@ _lib = ctypes.CDLL(lib_path())
 PBA_F32, PBA_BF16 = 0, 1
 STATUS = {0: "PBA_OK", -1: "PBA_ERR_NULL_ARG", -2: "PBA_ERR_BAD_DTYPE", -3: "PBA_ERR_BAD_SHAPE",
           -4: "PBA_ERR_UNSUPPORTED", -5: "PBA_ERR_WORKSPACE_TOO_SMALL",
-          -6: "PBA_ERR_OUT_OF_RANGE", -7: "PBA_ERR_OVERLAP", -8: "PBA_ERR_HIP"}
+          -6: "PBA_ERR_OUT_OF_RANGE", -7: "PBA_ERR_OVERLAP", -8: "PBA_ERR_HIP",
+          -9: "PBA_ERR_HALF_BUNDLE"}
+MAX_GROUPS = 8
 _DTYPES = {torch.float32: PBA_F32, torch.bfloat16: PBA_BF16}
 
 
@@ -52,6 +55,11 @@ class PoolDesc(ctypes.Structure):
                 ("v_stride_head", ctypes.c_int64)]
 
 
+class GroupDesc(ctypes.Structure):
+    _fields_ = [("pool", PoolDesc), ("num_layers", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+                ("k_stride_layer", ctypes.c_int64), ("v_stride_layer", ctypes.c_int64)]
+
+
 class SharedPlanDesc(ctypes.Structure):
     _fields_ = [("num_items", ctypes.c_int32), ("max_slots", ctypes.c_int32),
                 ("partition_tokens", ctypes.c_int32), ("private_parts", ctypes.c_int32),
@@ -61,6 +69,7 @@ class SharedPlanDesc(ctypes.Structure):
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _P = ctypes.POINTER(PoolDesc)
 _SP = ctypes.POINTER(SharedPlanDesc)
+_GP = ctypes.POINTER(GroupDesc)
 _SIGS = {
     "pba_kv_append": (ctypes.c_int, [_P, _vp, _i64, _vp, _vp, _vp]),
     "pba_block_copy": (ctypes.c_int, [_P, _vp, _vp, _i64, _vp]),
@@ -76,6 +85,9 @@ _SIGS = {
     "pba_paged_decode_shared_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _SP]),
     "pba_paged_decode_shared": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float,
                                                _vp, _vp, _SP, _vp, _sz, _vp]),
+    "pba_group_layer_pool": (ctypes.c_int, [_GP, _i32, _P]),
+    "pba_kv_append_bundle": (ctypes.c_int, [_GP, _i32, _vp, _vp, _vp, _i64, _vp]),
+    "pba_block_copy_bundle": (ctypes.c_int, [_GP, _i32, _vp, _vp, _vp, _vp]),
     "pba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pba_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pba_version": (ctypes.c_int, []),
@@ -430,6 +442,139 @@ def pack_block_tables(tables: torch.Tensor, row_offsets: torch.Tensor, total: in
     _check("pba_pack_block_tables", _lib.pba_pack_block_tables(
         tables.data_ptr(), B, width, row_offsets.data_ptr(), out.data_ptr(), _stream(stream)))
     return out[:total]
+
+
+@dataclass(frozen=True)
+class KVGroup:
+    """One cache group of L layers with one block table per request.
+
+    layer_major: K [L, NB, H_kv, P, d] and V [L, NB, H_kv, d, P]; otherwise
+    block major: K [NB, L, H_kv, P, d] and V [NB, L, H_kv, d, P] (one block's
+    layers adjacent).  Tiles are dense as in ``KVPool``.
+    """
+
+    k: torch.Tensor
+    v: torch.Tensor
+    layer_major: bool = True
+
+    def __post_init__(self):
+        k, v = self.k, self.v
+        if k.dim() != 5 or v.dim() != 5:
+            raise ValueError("group K and V must be rank 5")
+        la, ba = (0, 1) if self.layer_major else (1, 0)
+        L, nb, h, p, d = k.shape[la], k.shape[ba], k.shape[2], k.shape[3], k.shape[4]
+        want_v = (L, nb, h, d, p) if self.layer_major else (nb, L, h, d, p)
+        if tuple(v.shape) != want_v or v.dtype != k.dtype or v.device != k.device:
+            raise ValueError(f"V must be {want_v} of K's dtype and device")
+        if k.dtype not in _DTYPES:
+            raise TypeError(f"pool dtype {k.dtype} not supported")
+        if k.stride(3) != d or k.stride(4) != 1 or v.stride(3) != p or v.stride(4) != 1:
+            raise ValueError("group tiles must be dense ([P][d] for K, [d][P] for V)")
+        pool = PoolDesc(k.data_ptr(), v.data_ptr(), _DTYPES[k.dtype], nb, p, h, d, 0,
+                        k.stride(ba), k.stride(2), v.stride(ba), v.stride(2))
+        desc = GroupDesc(pool, L, 0, k.stride(la), v.stride(la))
+        object.__setattr__(self, "_desc", desc)
+
+    @classmethod
+    def empty(cls, layers: int, num_blocks: int, block_size: int, num_kv_heads: int,
+              head_dim: int, dtype=torch.bfloat16, device="cuda", layer_major: bool = True):
+        lead = (layers, num_blocks) if layer_major else (num_blocks, layers)
+        k = torch.empty(lead + (num_kv_heads, block_size, head_dim), dtype=dtype, device=device)
+        v = torch.empty(lead + (num_kv_heads, head_dim, block_size), dtype=dtype, device=device)
+        return cls(k, v, layer_major)
+
+    @property
+    def num_layers(self) -> int:
+        return self._desc.num_layers
+
+    @property
+    def num_blocks(self) -> int:
+        return self._desc.pool.num_blocks
+
+    @property
+    def block_size(self) -> int:
+        return self._desc.pool.block_size
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self._desc.pool.num_kv_heads
+
+    @property
+    def head_dim(self) -> int:
+        return self._desc.pool.head_dim
+
+    @property
+    def dtype(self):
+        return self.k.dtype
+
+    def desc(self) -> GroupDesc:
+        return self._desc
+
+    def layer(self, layer: int) -> KVPool:
+        """Layer ``layer`` as a single-layer pool (views; no copy), for
+        paged_decode and the other single-layer calls."""
+        if not 0 <= layer < self.num_layers:
+            raise IndexError(layer)
+        if self.layer_major:
+            return KVPool(self.k[layer], self.v[layer])
+        return KVPool(self.k[:, layer], self.v[:, layer])
+
+    def layer_desc(self, layer: int) -> PoolDesc:
+        """The library's own layer descriptor (pba_group_layer_pool)."""
+        out = PoolDesc()
+        _check("pba_group_layer_pool", _lib.pba_group_layer_pool(ctypes.byref(self._desc), layer,
+                                                                 ctypes.byref(out)))
+        return out
+
+
+def _group_array(groups):
+    if not 1 <= len(groups) <= MAX_GROUPS:
+        raise ValueError(f"1 to {MAX_GROUPS} groups")
+    return (GroupDesc * len(groups))(*[g.desc() for g in groups])
+
+
+def kv_append_bundle(groups, slot_mappings, k_new, v_new, stream=None) -> None:
+    """Write token i into every layer of every group: group g's rows
+    k_new[g][i] / v_new[g][i] ([L_g, H_kv, d] each) at slot_mappings[g][i]
+    (int64; a token negative in every group is skipped)."""
+    G = len(groups)
+    if not (len(slot_mappings) == len(k_new) == len(v_new) == G):
+        raise ValueError("one slot mapping and one k_new/v_new per group")
+    n = slot_mappings[0].shape[0] if G else 0
+    for g, grp in enumerate(groups):
+        dev = grp.k.device
+        _require(slot_mappings[g], f"slot_mappings[{g}]", torch.int64, dev, 1)
+        _require(k_new[g], f"k_new[{g}]", grp.dtype, dev, 4)
+        _require(v_new[g], f"v_new[{g}]", grp.dtype, dev, 4)
+        shape = (n, grp.num_layers, grp.num_kv_heads, grp.head_dim)
+        if slot_mappings[g].shape[0] != n or tuple(k_new[g].shape) != shape or \
+                tuple(v_new[g].shape) != shape:
+            raise ValueError(f"group {g}: slots [n] and rows {shape} expected")
+    arr = _group_array(groups)
+    vp = ctypes.c_void_p * G
+    _check("pba_kv_append_bundle", _lib.pba_kv_append_bundle(
+        arr, G, vp(*[t.data_ptr() for t in slot_mappings]), vp(*[t.data_ptr() for t in k_new]),
+        vp(*[t.data_ptr() for t in v_new]), n, _stream(stream)))
+
+
+def block_copy_bundle(groups, src_blocks, dst_blocks, stream=None) -> None:
+    """Copy whole blocks src_blocks[g][k] -> dst_blocks[g][k] (int32) of every
+    layer of every group in one launch; the groups' pair counts may differ."""
+    G = len(groups)
+    if not (len(src_blocks) == len(dst_blocks) == G):
+        raise ValueError("one src/dst list per group")
+    for g, grp in enumerate(groups):
+        dev = grp.k.device
+        _require(src_blocks[g], f"src_blocks[{g}]", torch.int32, dev, 1)
+        _require(dst_blocks[g], f"dst_blocks[{g}]", torch.int32, dev, 1)
+        if src_blocks[g].shape != dst_blocks[g].shape:
+            raise ValueError(f"group {g}: src and dst lengths differ")
+    arr = _group_array(groups)
+    vp = ctypes.c_void_p * G
+    counts = (ctypes.c_int64 * G)(*[t.shape[0] for t in src_blocks])
+    _check("pba_block_copy_bundle", _lib.pba_block_copy_bundle(
+        arr, G, vp(*[t.data_ptr() for t in src_blocks]), vp(*[t.data_ptr() for t in dst_blocks]),
+        counts, _stream(stream)))
 
 
 def set_validate(on: bool) -> bool:

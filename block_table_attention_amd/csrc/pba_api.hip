@@ -11,6 +11,7 @@
 #include <unordered_set>
 #include <vector>
 
+#include "bundle_internal.h"
 #include "pba_internal.h"
 
 namespace {
@@ -29,6 +30,21 @@ int log2_exact(int x) {
 int esize_of(int dtype) { return dtype == PBA_BF16 ? 2 : 4; }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// True when the tiles of `tile` elements at sum_i idx_i * stride_i (idx_i <
+// count_i) are pairwise disjoint: taken by increasing stride, every axis with
+// more than one index strides at least over the span of the axes below it.
+bool tiles_disjoint(int64_t tile, std::vector<std::pair<int64_t, int64_t>> axes) {
+  std::sort(axes.begin(), axes.end());
+  int64_t span = tile;
+  for (const auto& a : axes) {
+    if (a.second <= 1) continue;
+    if (a.first < span) return false;
+    if (a.first > (INT64_MAX - span) / (a.second - 1)) return false;
+    span += a.first * (a.second - 1);
+  }
+  return true;
+}
 
 // Checks the pool descriptor; everything here is host-visible.
 int check_pool(const pba_kv_pool* pool) {
@@ -53,12 +69,43 @@ int check_pool(const pba_kv_pool* pool) {
     if (s < 0) return PBA_ERR_BAD_SHAPE;
     if ((s * es) % 16) return PBA_ERR_UNSUPPORTED;
   }
-  // A tile must fit in its stride, and the heads of one block in the block stride.
-  if (pool->num_kv_heads > 1 && (pool->k_stride_head < tile || pool->v_stride_head < tile))
-    return PBA_ERR_BAD_SHAPE;
-  if (tiles > 1 && (pool->k_stride_block < tile || pool->v_stride_block < tile))
+  // The (block, head) tiles of K, and of V, must not overlap.
+  if (!tiles_disjoint(tile, {{pool->k_stride_block, tiles}, {pool->k_stride_head, pool->num_kv_heads}}) ||
+      !tiles_disjoint(tile, {{pool->v_stride_block, tiles}, {pool->v_stride_head, pool->num_kv_heads}}))
     return PBA_ERR_BAD_SHAPE;
   if (!aligned16(pool->k) || !aligned16(pool->v)) return PBA_ERR_UNSUPPORTED;
+  return PBA_OK;
+}
+
+// Checks a cache group: its layer-0 pool (allocator view), the layer count and
+// strides, and that no two (layer, block, head) tiles of K, or of V, overlap.
+int check_group(const pba_kv_group* g) {
+  if (!g) return PBA_ERR_NULL_ARG;
+  if (g->pool.split_log2) return PBA_ERR_UNSUPPORTED;  // groups are allocator views
+  const int st = check_pool(&g->pool);
+  if (st) return st;
+  const pba_kv_pool& p = g->pool;
+  if (g->num_layers < 1 || g->reserved0 != 0 || g->k_stride_layer < 0 || g->v_stride_layer < 0)
+    return PBA_ERR_BAD_SHAPE;
+  const int es = esize_of(p.dtype);
+  if ((g->k_stride_layer * es) % 16 || (g->v_stride_layer * es) % 16) return PBA_ERR_UNSUPPORTED;
+  const int64_t tile = (int64_t)p.block_size * p.head_dim;
+  if (!tiles_disjoint(tile, {{g->k_stride_layer, g->num_layers}, {p.k_stride_block, p.num_blocks},
+                             {p.k_stride_head, p.num_kv_heads}}) ||
+      !tiles_disjoint(tile, {{g->v_stride_layer, g->num_layers}, {p.v_stride_block, p.num_blocks},
+                             {p.v_stride_head, p.num_kv_heads}}))
+    return PBA_ERR_BAD_SHAPE;
+  return PBA_OK;
+}
+
+int check_groups(const pba_kv_group* groups, int32_t num_groups) {
+  if (!groups) return PBA_ERR_NULL_ARG;
+  if (num_groups < 1) return PBA_ERR_BAD_SHAPE;
+  if (num_groups > PBA_MAX_GROUPS) return PBA_ERR_UNSUPPORTED;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const int st = check_group(&groups[g]);
+    if (st) return st;
+  }
   return PBA_OK;
 }
 
@@ -166,7 +213,7 @@ bool copy_to_host(std::vector<T>& dst, const T* src, int64_t n, hipStream_t stre
 
 extern "C" {
 
-int pba_version(void) { return 200; }
+int pba_version(void) { return 300; }
 
 int pba_set_validate(int on) { return g_validate.exchange(on ? 1 : 0); }
 
@@ -181,6 +228,7 @@ const char* pba_status_string(int status) {
     case PBA_ERR_OUT_OF_RANGE: return "block id, slot or sequence length out of range";
     case PBA_ERR_OVERLAP: return "duplicate slot or overlapping copy pairs";
     case PBA_ERR_HIP: return "HIP runtime error";
+    case PBA_ERR_HALF_BUNDLE: return "a token or copy would move some cache groups only";
     default: return "unknown status";
   }
 }
@@ -258,6 +306,150 @@ int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* d
   a.tile_bytes = (int64_t)pool->block_size * pool->head_dim * a.esize;
   return pba::launch_block_copy(a, n_pairs, pool->num_kv_heads, s) == hipSuccess ? PBA_OK
                                                                                  : PBA_ERR_HIP;
+}
+
+int pba_group_layer_pool(const pba_kv_group* group, int32_t layer, pba_kv_pool* out) {
+  const int st = check_group(group);
+  if (st) return st;
+  if (!out) return PBA_ERR_NULL_ARG;
+  if (layer < 0 || layer >= group->num_layers) return PBA_ERR_BAD_SHAPE;
+  const int es = esize_of(group->pool.dtype);
+  *out = group->pool;
+  out->k = static_cast<char*>(group->pool.k) + (int64_t)layer * group->k_stride_layer * es;
+  out->v = static_cast<char*>(group->pool.v) + (int64_t)layer * group->v_stride_layer * es;
+  return PBA_OK;
+}
+
+int pba_kv_append_bundle(const pba_kv_group* groups, int32_t num_groups,
+                         const int64_t* const* slot_mappings, const void* const* k_new,
+                         const void* const* v_new, int64_t n_tokens, void* stream) {
+  int st = check_groups(groups, num_groups);
+  if (st) return st;
+  if (n_tokens < 0) return PBA_ERR_BAD_SHAPE;
+  if (n_tokens == 0) return PBA_OK;
+  if (!slot_mappings || !k_new || !v_new) return PBA_ERR_NULL_ARG;
+  int64_t tasks_per_token = 0;  // K and V pieces of one token over every group
+  for (int32_t g = 0; g < num_groups; ++g) {
+    if (!slot_mappings[g] || !k_new[g] || !v_new[g]) return PBA_ERR_NULL_ARG;
+    if (!aligned16(k_new[g]) || !aligned16(v_new[g])) return PBA_ERR_UNSUPPORTED;
+    const pba_kv_pool& p = groups[g].pool;
+    tasks_per_token += 2LL * groups[g].num_layers * p.num_kv_heads * (p.head_dim * esize_of(p.dtype) / 16);
+  }
+  // Tokens per launch: every task index of a launch fits in int32.
+  const int64_t chunk = std::min<int64_t>(n_tokens, (INT32_MAX - 256) / tasks_per_token);
+  if (chunk < 1) return PBA_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    std::vector<std::vector<int64_t>> slots(num_groups);
+    for (int32_t g = 0; g < num_groups; ++g) {
+      if (!copy_to_host(slots[g], slot_mappings[g], n_tokens, s)) return PBA_ERR_HIP;
+      const int64_t limit = (int64_t)groups[g].pool.num_blocks * groups[g].pool.block_size;
+      std::unordered_set<int64_t> seen;
+      for (int64_t x : slots[g]) {
+        if (x < 0) continue;
+        if (x >= limit) return PBA_ERR_OUT_OF_RANGE;
+        if (!seen.insert(x).second) return PBA_ERR_OVERLAP;
+      }
+    }
+    for (int64_t i = 0; i < n_tokens; ++i) {
+      int skipped = 0;
+      for (int32_t g = 0; g < num_groups; ++g) skipped += slots[g][i] < 0;
+      if (skipped != 0 && skipped != num_groups) return PBA_ERR_HALF_BUNDLE;
+    }
+  }
+  for (int64_t t0 = 0; t0 < n_tokens; t0 += chunk) {
+    const int64_t n = std::min(chunk, n_tokens - t0);
+    pba::BundleAppendArgs a{};
+    a.n_groups = num_groups;
+    a.n = (int32_t)n;
+    int64_t task = 0;
+    for (int32_t g = 0; g < num_groups; ++g) {
+      const pba_kv_group& G = groups[g];
+      const pba_kv_pool& p = G.pool;
+      const int es = esize_of(p.dtype);
+      const int64_t row = (int64_t)G.num_layers * p.num_kv_heads * p.head_dim * es;  // bytes
+      pba::GroupAppend& A = a.g[g];
+      A.k = static_cast<char*>(p.k);
+      A.v = static_cast<char*>(p.v);
+      A.k_new = static_cast<const char*>(k_new[g]) + t0 * row;
+      A.v_new = static_cast<const char*>(v_new[g]) + t0 * row;
+      A.slots = slot_mappings[g] + t0;
+      A.k_sl = G.k_stride_layer;
+      A.k_sb = p.k_stride_block;
+      A.k_sh = p.k_stride_head;
+      A.v_sl = G.v_stride_layer;
+      A.v_sb = p.v_stride_block;
+      A.v_sh = p.v_stride_head;
+      A.layers = G.num_layers;
+      A.heads = p.num_kv_heads;
+      A.head_dim = p.head_dim;
+      A.log2P = log2_exact(p.block_size);
+      A.esize = es;
+      A.task0 = (int32_t)task;
+      A.per_kind = (int32_t)(n * G.num_layers * p.num_kv_heads * (p.head_dim * es / 16));
+      task += 2LL * A.per_kind;
+    }
+    a.total = (int32_t)task;
+    if (pba::launch_kv_append_bundle(a, s) != hipSuccess) return PBA_ERR_HIP;
+  }
+  return PBA_OK;
+}
+
+int pba_block_copy_bundle(const pba_kv_group* groups, int32_t num_groups,
+                          const int32_t* const* src_blocks, const int32_t* const* dst_blocks,
+                          const int64_t* n_pairs, void* stream) {
+  int st = check_groups(groups, num_groups);
+  if (st) return st;
+  if (!src_blocks || !dst_blocks || !n_pairs) return PBA_ERR_NULL_ARG;
+  int64_t total = 0;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    if (n_pairs[g] < 0) return PBA_ERR_BAD_SHAPE;
+    if (n_pairs[g] > 0 && (!src_blocks[g] || !dst_blocks[g])) return PBA_ERR_NULL_ARG;
+    total += n_pairs[g] * 2 * groups[g].num_layers * groups[g].pool.num_kv_heads;
+    if (total > INT32_MAX) return PBA_ERR_UNSUPPORTED;
+  }
+  if (total == 0) return PBA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (g_validate.load()) {
+    for (int32_t g = 0; g < num_groups; ++g) {
+      std::vector<int32_t> hs, hd;
+      if (!copy_to_host(hs, src_blocks[g], n_pairs[g], s) ||
+          !copy_to_host(hd, dst_blocks[g], n_pairs[g], s))
+        return PBA_ERR_HIP;
+      const int32_t nb = groups[g].pool.num_blocks;
+      std::unordered_set<int32_t> dsts, srcs(hs.begin(), hs.end());
+      for (int64_t i = 0; i < n_pairs[g]; ++i) {
+        if (hs[i] < 0 || hs[i] >= nb || hd[i] < 0 || hd[i] >= nb) return PBA_ERR_OUT_OF_RANGE;
+        if (!dsts.insert(hd[i]).second || srcs.count(hd[i])) return PBA_ERR_OVERLAP;
+      }
+    }
+  }
+  pba::BundleCopyArgs a{};
+  a.n_groups = num_groups;
+  int64_t wg = 0;
+  for (int32_t g = 0; g < num_groups; ++g) {
+    const pba_kv_group& G = groups[g];
+    const pba_kv_pool& p = G.pool;
+    const int es = esize_of(p.dtype);
+    pba::GroupCopy& C = a.g[g];
+    C.k = static_cast<char*>(p.k);
+    C.v = static_cast<char*>(p.v);
+    C.src = src_blocks[g];
+    C.dst = dst_blocks[g];
+    C.k_sl = G.k_stride_layer * es;
+    C.k_sb = p.k_stride_block * es;
+    C.k_sh = p.k_stride_head * es;
+    C.v_sl = G.v_stride_layer * es;
+    C.v_sb = p.v_stride_block * es;
+    C.v_sh = p.v_stride_head * es;
+    C.layers = G.num_layers;
+    C.heads = p.num_kv_heads;
+    C.tile16 = (int32_t)((int64_t)p.block_size * p.head_dim * es / 16);
+    C.wg0 = (int32_t)wg;
+    wg += n_pairs[g] * 2 * G.num_layers * p.num_kv_heads;
+  }
+  a.total = (int32_t)wg;
+  return pba::launch_block_copy_bundle(a, s) == hipSuccess ? PBA_OK : PBA_ERR_HIP;
 }
 
 int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,

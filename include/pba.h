@@ -46,7 +46,9 @@ typedef enum pba_status {
   PBA_ERR_WORKSPACE_TOO_SMALL = -5, /* workspace NULL or smaller than needed   */
   PBA_ERR_OUT_OF_RANGE = -6,        /* validate mode: bad id, slot or length   */
   PBA_ERR_OVERLAP = -7,             /* validate mode: duplicate slot / pair    */
-  PBA_ERR_HIP = -8                  /* a HIP runtime call failed               */
+  PBA_ERR_HIP = -8,                 /* a HIP runtime call failed               */
+  PBA_ERR_HALF_BUNDLE = -9          /* validate mode: a token or copy list that
+                                       would move some cache groups only       */
 } pba_status;
 
 typedef enum pba_dtype { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
@@ -129,6 +131,83 @@ int pba_kv_append(const pba_kv_pool* pool, const int64_t* slot_mapping, int64_t 
  */
 int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* dst,
                    int64_t n_pairs, void* stream);
+
+/*
+ * Cache groups with a layer axis ("M5.3", 0x03B: each cache group has its
+ * own pool and its own block table per request, and a token row of the group
+ * spans all of its layers; 0x03C-0x03E: the group-local layer index is one
+ * more coordinate of the stride rule; 0x04E: a bundle is one block of every
+ * group, P_g * B_row,g bytes in group g).
+ *
+ * A group holds num_layers consecutive layers.  `pool` describes layer 0
+ * (dtype, block count, P, kv heads, head_dim, block and head strides;
+ * split_log2 must be 0); layer l is the same description with k and v
+ * advanced by l * k_stride_layer and l * v_stride_layer elements:
+ *   K: k[l * k_stride_layer + b * k_stride_block + h * k_stride_head + o * head_dim + c]
+ *   V: v[l * v_stride_layer + b * v_stride_block + h * v_stride_head + c * P + o]
+ * Layer-major groups ([L][NB][H] tiles) and block-major groups ([NB][L][H]
+ * tiles: one block's layers adjacent) are both expressed by the strides.  The
+ * (layer, block, head) tiles must be pairwise disjoint: sorted by stride,
+ * every stride is at least the span of the axes below it (PBA_ERR_BAD_SHAPE).
+ * Strides are multiples of 16 bytes.
+ */
+typedef struct pba_kv_group {
+  pba_kv_pool pool;          /* layer 0 */
+  int32_t num_layers;        /* L >= 1 */
+  int32_t reserved0;         /* must be 0 */
+  int64_t k_stride_layer, v_stride_layer;
+} pba_kv_group;
+
+#define PBA_MAX_GROUPS 8
+
+/* The pba_kv_pool of layer `layer` of a group, for pba_paged_decode and the
+ * other single-layer calls.  Host only: checks the group and writes *out. */
+int pba_group_layer_pool(const pba_kv_group* group, int32_t layer, pba_kv_pool* out);
+
+/*
+ * pba_kv_append_bundle -- write new tokens into every layer of every cache
+ * group in one launch ("M5.3", 0x04E: the appended row is written in every
+ * group's destination; 0x05C step 6).
+ *
+ * For group g < num_groups and token i < n_tokens with s = slot_mappings[g][i]
+ * >= 0: block s div P_g, offset s mod P_g, and for every layer l and kv head h
+ * the row k_new[g][i, l, h, :] goes to K(l, block, h, offset, :) and
+ * v_new[g][i, l, h, :] to V(l, block, h, offset, :), bit exact.
+ *
+ *   groups         host array [num_groups], 1 <= num_groups <= PBA_MAX_GROUPS
+ *   slot_mappings  host array [num_groups] of device int64 [n_tokens]
+ *   k_new, v_new   host arrays [num_groups] of device
+ *                  [n_tokens, num_layers_g, num_kv_heads_g, head_dim_g] in the
+ *                  group's dtype, contiguous, 16-byte aligned
+ * A token is written to every group or, when its slot is negative in every
+ * group, to none; validate mode rejects a token skipped in some groups only
+ * (PBA_ERR_HALF_BUNDLE), a repeated slot within a group (PBA_ERR_OVERLAP) and
+ * a slot beyond a group's pool (PBA_ERR_OUT_OF_RANGE), before any launch.
+ */
+int pba_kv_append_bundle(const pba_kv_group* groups, int32_t num_groups,
+                         const int64_t* const* slot_mappings, const void* const* k_new,
+                         const void* const* v_new, int64_t n_tokens, void* stream);
+
+/*
+ * pba_block_copy_bundle -- the copies of one publication, every layer of
+ * every group, in one launch ("M5.3", 0x04C one fused block-copy launch over
+ * many pairs and layers; 0x05B-0x05C the tail bundle of every group is copied
+ * and all groups' replacements are published together).
+ *
+ * For group g and pair k < n_pairs[g]: block src_blocks[g][k] -> block
+ * dst_blocks[g][k], whole blocks (every layer, kv head, row; K and V).
+ *
+ *   src_blocks, dst_blocks  host arrays [num_groups] of device int32 [n_pairs[g]]
+ *   n_pairs                 host int64 [num_groups]; groups whose block sizes
+ *                           differ may copy different numbers of blocks
+ * Validate mode checks every group's pairs (ids in range: PBA_ERR_OUT_OF_RANGE;
+ * no block twice as a destination or as both source and destination within a
+ * group: PBA_ERR_OVERLAP) before anything is copied, so a rejected call moves
+ * no group.
+ */
+int pba_block_copy_bundle(const pba_kv_group* groups, int32_t num_groups,
+                          const int32_t* const* src_blocks, const int32_t* const* dst_blocks,
+                          const int64_t* n_pairs, void* stream);
 
 /*
  * pba_paged_decode -- one decode query row per request over its logical

@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     assert declared == sorted(pba.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pba.version() == 200
+    assert pba.version() == 300
 
 
 def _desc(**kw):

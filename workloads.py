@@ -43,7 +43,7 @@ import numpy as np
 
 SEED_BASE = 20261202
 WORKLOAD_INDEX = {"tiny": 1, "batch32": 2, "shared_prefix": 3, "lognormal": 4,
-                  "long16k": 5, "long64k": 5}
+                  "long16k": 5, "long64k": 5, "layers32": 6, "bundle": 7}
 
 # Per-component seed offsets.
 _K, _V, _Q, _POISON, _STRUCT, _ORDER = 1, 2, 3, 4, 5, 6
@@ -274,3 +274,94 @@ def pool_poison(w: Workload):
 
 def fifo_order(w: Workload) -> np.ndarray:
     return free_order(w.seed * 16 + _ORDER, w.shape.num_blocks)
+
+
+# ---------------------------------------------------------------------------
+# Cache groups with a layer axis
+# ---------------------------------------------------------------------------
+@dataclass(frozen=True)
+class GroupShape:
+    layers: int
+    block_size: int
+    num_blocks: int
+    layer_major: bool   # K [L, NB, H, P, d]; else block major K [NB, L, H, P, d]
+
+
+@dataclass
+class BundleWorkload:
+    """A request script over several cache groups (one block table per group
+    and request, one length per request); same action vocabulary as
+    ``Workload``."""
+
+    name: str
+    groups: List[GroupShape]
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    seed: int
+    actions: List[Tuple] = field(default_factory=list)
+    decode: List[int] = field(default_factory=list)
+
+    def n_writes(self) -> int:
+        return sum(a[2] if a[0] == "prefill" else 1 for a in self.actions
+                   if a[0] in ("prefill", "append"))
+
+    @property
+    def total_layers(self) -> int:
+        return sum(g.layers for g in self.groups)
+
+
+def bundle_rows(w: BundleWorkload, g: int):
+    """K and V bits [n_writes, L_g, H_kv, d] of group g, write w = token w."""
+    n = w.n_writes()
+    shape = (n, w.groups[g].layers, w.num_kv_heads, w.head_dim)
+    k = normal_bits(w.seed * 16 + _K + 100 * g, shape, w.dtype)
+    v = normal_bits(w.seed * 16 + _V + 100 * g, shape, w.dtype)
+    return k, v
+
+
+def bundle_q_bits(w: BundleWorkload) -> np.ndarray:
+    """Decode queries of every model layer: bits [total_layers, B, H_q, d]."""
+    return normal_bits(w.seed * 16 + _Q, (w.total_layers, len(w.decode), w.num_q_heads,
+                                         w.head_dim), w.dtype)
+
+
+def bundle_poison(w: BundleWorkload, g: int):
+    """Initial K and V bits of group g, flat, in the group's memory order."""
+    gs = w.groups[g]
+    n = gs.layers * gs.num_blocks * w.num_kv_heads * gs.block_size * w.head_dim
+    k = poison_bits(w.seed * 16 + _POISON + 100 * g, (n,), w.dtype)
+    v = poison_bits(w.seed * 16 + _POISON + 8 + 100 * g, (n,), w.dtype)
+    return k, v
+
+
+def bundle_fifo_orders(w: BundleWorkload) -> List[np.ndarray]:
+    return [free_order(w.seed * 16 + _ORDER + 100 * g, gs.num_blocks)
+            for g, gs in enumerate(w.groups)]
+
+
+def layers32(rep: int = 0, batch: int = 32, forks: int = 8, lo: int = 64,
+             hi: int = 2048) -> BundleWorkload:
+    """All 32 layers of one tensor-parallel rank of an 8-kv-head, 32-q-head,
+    d = 128 model at TP 2 (4 kv heads and 16 q heads per rank), in the pages'
+    two cache groups: layers 0-23 (block major) and 24-31 (layer major), both
+    with P = 16, bf16.  ``batch`` requests of U[lo, hi] tokens; ``forks`` of
+    them are forked, and the step appends one token to every request, so each
+    forked pair copies its shared tail bundle first."""
+    s = seed_for("layers32", rep)
+    lengths = uniform_lengths(s + _STRUCT, batch, lo, hi)
+    blocks = sum(-(-(int(T) + 1) // 16) for T in lengths) + forks
+    nb = int(math.ceil(1.25 * blocks))
+    w = BundleWorkload("layers32", [GroupShape(24, 16, nb, False), GroupShape(8, 16, nb, True)],
+                       16, 4, 128, "bf16", s)
+    for r in range(batch):
+        w.actions.append(("new",))
+        w.actions.append(("prefill", r, int(lengths[r]) - 1))
+    kids = list(range(batch, batch + forks))
+    for i in range(forks):
+        w.actions.append(("fork", i))
+    for r in list(range(batch)) + kids:
+        w.actions.append(("append", r))
+    w.decode = list(range(batch)) + kids
+    return w
