@@ -40,7 +40,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 WORKLOADS = ["long16k", "long64k", "batch32", "shared_prefix", "lognormal_p16",
-             "lognormal_p64", "lognormal_p256", "tiny"]
+             "lognormal_p64", "lognormal_p256", "tiny", "layers32"]
+BUNDLE_WORKLOADS = {"layers32"}
 
 
 def parse():
@@ -224,10 +225,16 @@ def main():
         return copy_calibration(args, pba, torch, dev)
     names = WORKLOADS if args.sweep else [args.workload]
     for name in names:
-        result = run_workload(args, name, pba, torch, dev)
-        if not (args.sweep or args.no_cpu_baseline):
-            w = make_workload(name)
-            result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, result["_kv_value_bytes"])
+        if name in BUNDLE_WORKLOADS:
+            result = run_bundle(args, name, pba, torch, dev)
+            if not (args.sweep or args.no_cpu_baseline):
+                result["cpu_baseline"] = cpu_baseline_bundle(make_workload(name), args.cpu_seconds,
+                                                             result["_kv_value_bytes"])
+        else:
+            result = run_workload(args, name, pba, torch, dev)
+            if not (args.sweep or args.no_cpu_baseline):
+                w = make_workload(name)
+                result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, result["_kv_value_bytes"])
         result.pop("_kv_value_bytes")
         print(json.dumps(result), flush=True)
 
@@ -474,6 +481,331 @@ def run_workload(args, name, pba, torch, dev):
     del pool, ws
     torch.cuda.empty_cache()
     return result
+
+
+# ---------------------------------------------------------------------------
+# Cache groups with a layer axis: the whole model's decode attention step.
+# ---------------------------------------------------------------------------
+@dataclass
+class BundlePlan:
+    setup: List[Tuple]          # ("copy", [(src, dst) per group]) | ("append", [slots per group], lo, hi)
+    step_copies: List[Tuple[np.ndarray, np.ndarray]]   # per group
+    step_slots: List[np.ndarray]                       # per group
+    step_rows: Tuple[int, int]
+    tables: List[np.ndarray]    # per group: int32 [B, max_blocks_g]
+    seq_lens: np.ndarray
+    n_writes: int
+
+
+def plan_bundle_script(w) -> BundlePlan:
+    """The BundleManager over the script; the step is its trailing appends."""
+    import workloads as wl
+    from block_table_attention_amd.blocks import BundleManager
+
+    G = len(w.groups)
+    m = BundleManager([g.num_blocks for g in w.groups], [g.block_size for g in w.groups],
+                      free_orders=wl.bundle_fifo_orders(w))
+    n_tail = 0
+    for act in reversed(w.actions):
+        if act[0] != "append":
+            break
+        n_tail += 1
+    first_step = len(w.actions) - n_tail
+    setup: List[Tuple] = []
+    step_src = [[] for _ in range(G)]
+    step_dst = [[] for _ in range(G)]
+    step_slots = [[] for _ in range(G)]
+    row = 0
+    step_lo = None
+    for i, act in enumerate(w.actions):
+        kind = act[0]
+        if kind == "new":
+            m.new_request()
+        elif kind == "fork":
+            m.fork(act[1])
+        elif kind == "release":
+            m.release(act[1])
+        else:
+            n = act[2] if kind == "prefill" else 1
+            slots, copies = m.append(act[1], n)
+            if i >= first_step:
+                step_lo = row if step_lo is None else step_lo
+                for g in range(G):
+                    step_src[g] += [c[0] for c in copies[g]]
+                    step_dst[g] += [c[1] for c in copies[g]]
+                    step_slots[g].append(slots[g])
+            else:
+                if any(copies):
+                    setup.append(("copy", [(np.array([c[0] for c in copies[g]], np.int32),
+                                            np.array([c[1] for c in copies[g]], np.int32))
+                                           for g in range(G)]))
+                setup.append(("append", slots, row, row + n))
+            row += n
+    step_lo = row if step_lo is None else step_lo
+    return BundlePlan(setup,
+                      [(np.array(step_src[g], np.int32), np.array(step_dst[g], np.int32))
+                       for g in range(G)],
+                      [np.concatenate(step_slots[g]) if step_slots[g] else np.zeros(0, np.int64)
+                       for g in range(G)],
+                      (step_lo, row), m.block_tables(w.decode), m.seq_lens(w.decode), row)
+
+
+def run_bundle(args, name, pba, torch, dev):
+    """One decode step of every layer: block_copy_bundle of the step's
+    copy-on-write bundles, kv_append_bundle of the step's tokens into every
+    layer of every group, then paged_decode of each layer through its group's
+    layer pool and block table."""
+    import workloads as wl
+
+    w = make_workload(name)
+    G = len(w.groups)
+    Hq, Hkv, d = w.num_q_heads, w.num_kv_heads, w.head_dim
+    t0 = time.time()
+    plan = plan_bundle_script(w)
+    rows = [wl.bundle_rows(w, g) for g in range(G)]
+    print(f"[bench] {name}: planned the script and drew {plan.n_writes} rows x "
+          f"{w.total_layers} layers in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+
+    def dev_bits(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    groups = []
+    for g, gs in enumerate(w.groups):
+        k0, v0 = wl.bundle_poison(w, g)
+        lead = (gs.layers, gs.num_blocks) if gs.layer_major else (gs.num_blocks, gs.layers)
+        k = dev_bits(k0).view(lead + (Hkv, gs.block_size, d))
+        v = dev_bits(v0).view(lead + (Hkv, d, gs.block_size))
+        groups.append(pba.KVGroup(k, v, gs.layer_major))
+        del k0, v0
+    rows_dev = [(dev_bits(k), dev_bits(v)) for k, v in rows]
+    del rows
+    for op in plan.setup:
+        if op[0] == "copy":
+            pba.block_copy_bundle(groups, [torch.from_numpy(s).to(dev) for s, _ in op[1]],
+                                  [torch.from_numpy(t).to(dev) for _, t in op[1]])
+        else:
+            pba.kv_append_bundle(groups, [torch.from_numpy(s).to(dev) for s in op[1]],
+                                 [r[0][op[2]:op[3]] for r in rows_dev],
+                                 [r[1][op[2]:op[3]] for r in rows_dev])
+    lo, hi = plan.step_rows
+    k_step = [r[0][lo:hi].contiguous() for r in rows_dev]
+    v_step = [r[1][lo:hi].contiguous() for r in rows_dev]
+    k_step_l = [[k[:, l].contiguous() for l in range(k.shape[1])] for k in k_step]
+    v_step_l = [[v[:, l].contiguous() for l in range(v.shape[1])] for v in v_step]
+    del rows_dev
+    slots = [torch.from_numpy(s).to(dev) for s in plan.step_slots]
+    csrc = [torch.from_numpy(s).to(dev) for s, _ in plan.step_copies]
+    cdst = [torch.from_numpy(t).to(dev) for _, t in plan.step_copies]
+    q_all = dev_bits(wl.bundle_q_bits(w))           # [layers, B, Hq, d]
+    B = len(plan.seq_lens)
+    lens_d = torch.from_numpy(plan.seq_lens).to(dev)
+    tabs = [torch.from_numpy(t).to(dev) for t in plan.tables]
+    layer_pools = [(g, grp.layer(l)) for g, grp in enumerate(groups) for l in range(grp.num_layers)]
+    scale = 1.0 / math.sqrt(d)
+    req_pt = args.partition_tokens
+    if req_pt < 0:
+        from block_table_attention_amd.blocks import suggest_partition_tokens
+        req_pt = suggest_partition_tokens(plan.seq_lens, Hkv)
+    mbs = [t.shape[1] for t in plan.tables]
+    ws_bytes = max(pba.paged_decode_workspace_bytes(lp, Hq, B, mbs[g], req_pt) for g, lp in layer_pools)
+    pt, n_parts = pba.paged_decode_plan(layer_pools[0][1], Hq, B, mbs[0], req_pt)
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.total_layers, B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.total_layers, B, Hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def decode_layer(i, st=stream):
+        g, lp = layer_pools[i]
+        pba.paged_decode(lp, q_all[i], tabs[g], lens_d, scale, out=out[i], lse=lse[i],
+                         partition_tokens=req_pt, workspace=ws, stream=st)
+
+    def copies(st=stream):
+        pba.block_copy_bundle(groups, csrc, cdst, stream=st)
+
+    def appends(st=stream):
+        pba.kv_append_bundle(groups, slots, k_step, v_step, stream=st)
+
+    def copies_per_layer(st=stream):
+        for g, grp in enumerate(groups):
+            if csrc[g].numel():
+                for l in range(grp.num_layers):
+                    pba.block_copy(grp.layer(l), csrc[g], cdst[g], stream=st)
+
+    def appends_per_layer(st=stream):
+        for g, grp in enumerate(groups):
+            for l in range(grp.num_layers):
+                pba.kv_append(layer_pools_by_group[g][l], slots[g], k_step_l[g][l], v_step_l[g][l],
+                              stream=st)
+
+    layer_pools_by_group = [[grp.layer(l) for l in range(grp.num_layers)] for grp in groups]
+
+    def step(evs=None, st=stream):
+        if evs is not None:
+            evs[0].record(st)
+        copies(st)
+        if evs is not None:
+            evs[1].record(st)
+        appends(st)
+        if evs is not None:
+            evs[2].record(st)
+        for i in range(len(layer_pools)):
+            decode_layer(i, st)
+        if evs is not None:
+            evs[3].record(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t_start = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / K
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    for i in range(K):
+        step(evs[i])
+    torch.cuda.synchronize()
+    copy_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    append_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    dec_all_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+
+    def burst(fn, reps):
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        b0.record(stream)
+        for _ in range(reps):
+            fn()
+        b1.record(stream)
+        torch.cuda.synchronize()
+        return b0.elapsed_time(b1) / reps
+
+    L = len(layer_pools)
+    dec_avg_ms = burst(lambda: [decode_layer(i) for i in range(L)], K) / L
+    copy_fused = burst(copies, K)
+    copy_split = burst(copies_per_layer, K)
+    app_fused = burst(appends, K)
+    app_split = burst(appends_per_layer, K)
+    print(f"[bench] {name}: {ms_per_step * 1e3:.1f} us/step; decode {dec_avg_ms * 1e3:.1f} us/layer; "
+          f"copy {copy_fused * 1e3:.1f} us fused vs {copy_split * 1e3:.1f} per layer; append "
+          f"{app_fused * 1e3:.1f} us fused vs {app_split * 1e3:.1f} per layer",
+          file=sys.stderr, flush=True)
+
+    # Bytes: one layer's decode reads every unique visible row of its group.
+    lens = plan.seq_lens
+    P = w.groups[0].block_size
+    row_layer = Hkv * d * 2 * 2
+    uniq = [int(np.unique(visible_slots(plan.tables[g], lens, w.groups[g].block_size)).size)
+            for g in range(G)]
+    kv_unique = sum(uniq[g] * row_layer * w.groups[g].layers for g in range(G))
+    kv_logical = int(lens.sum()) * row_layer * w.total_layers
+    small = B * Hq * d * 2 + B * Hq * d * 4 + B * Hq * 4 + B * 4
+    alg_layer = [uniq[g] * row_layer + small + int(sum(-(-int(T) // w.groups[g].block_size)
+                                                      for T in lens)) * 4 for g in range(G)]
+    alg_avg = sum(alg_layer[g] * w.groups[g].layers for g in range(G)) / w.total_layers
+    achieved = alg_avg / (dec_avg_ms * 1e-3) / 1e9
+    traffic = profiled_traffic(name) if args.partition_tokens < 0 else None
+    step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
+    n_copy = [int(s.numel()) for s in csrc]
+    bundle_bytes = sum(gs.layers * Hkv * gs.block_size * d * 2 * 2 for gs in w.groups)
+    result = {
+        "metric": "paged decode: KV GB/s achieved (% of HBM peak) + query rows/s at 1 GPU",
+        "value": round(step_kv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q rounded to bf16; seeded free-FIFO block placement)",
+        "config": {"workload": f"{name}: {w.total_layers} layers in {G} cache groups "
+                               f"({', '.join(f'{gs.layers} layers P={gs.block_size} ' + ('layer' if gs.layer_major else 'block') + '-major' for gs in w.groups)}), "
+                               f"batch {B}, context {int(lens.min())}..{int(lens.max())} "
+                               f"(sum {int(lens.sum())}), {Hq} q-heads / {Hkv} kv-heads, head_dim {d}, "
+                               f"bf16, {w.groups[0].num_blocks} blocks per group",
+                   "batch": B, "layers": w.total_layers, "groups": G,
+                   "context_min": int(lens.min()), "context_max": int(lens.max()),
+                   "context_sum": int(lens.sum()), "block_size": P, "num_q_heads": Hq,
+                   "num_kv_heads": Hkv, "head_dim": d, "partition_tokens": pt,
+                   "num_partitions": n_parts, "bundle_bytes": bundle_bytes,
+                   "step": f"block_copy_bundle({n_copy} pairs per group) + kv_append_bundle("
+                           f"{int(slots[0].numel())} tokens x {w.total_layers} layers) + "
+                           f"{w.total_layers} x paged_decode",
+                   "step_launch": "eager"},
+        "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "hbm_peak_frac_step": round(step_kv_gbs / HBM_PEAK_GBS, 4),
+        "decode_us": round(dec_avg_ms * 1e3, 2),
+        "decode_all_layers_us_in_step": round(float(dec_all_ms.mean()) * 1e3, 2),
+        "append_us": round(float(append_ms.mean()) * 1e3, 2),
+        "copy_us": round(float(copy_ms.mean()) * 1e3, 2),
+        "copy_bundle_us": round(copy_fused * 1e3, 2),
+        "copy_per_layer_calls_us": round(copy_split * 1e3, 2),
+        "append_bundle_us": round(app_fused * 1e3, 2),
+        "append_per_layer_calls_us": round(app_split * 1e3, 2),
+        "kv_unique_bytes": kv_unique,
+        "kv_logical_bytes": kv_logical,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": f"decode_bf16_kernel<{d}> (one launch per layer, merge fused in)",
+                     "algorithmic_bytes_per_launch": int(round(alg_avg))},
+        "_kv_value_bytes": kv_unique,
+    }
+    del groups, ws
+    torch.cuda.empty_cache()
+    return result
+
+
+def cpu_baseline_bundle(w, seconds, kv_bytes_total):
+    """The CPU oracle on a bounded sample: whole decode rows of layer 0 (a
+    single-layer oracle pool of the first group, replayed with that layer's
+    rows), scaled to the bytes of every layer."""
+    from threadpoolctl import threadpool_limits
+
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from harness import execute_bundle
+    import workloads as wl
+    from oracle import attention as att
+    from oracle.pool import BitPool
+
+    t0 = time.time()
+    ex = execute_bundle(w)
+    gs = w.groups[0]
+    k_rows, v_rows = wl.bundle_rows(w, 0)
+    H, d, P = w.num_kv_heads, w.head_dim, gs.block_size
+    pool = BitPool(np.zeros((gs.num_blocks, H, P, d), np.uint16),
+                   np.zeros((gs.num_blocks, H, d, P), np.uint16), w.dtype)
+    for op in ex.ops:
+        if op[0] == "append":
+            pool.kv_append(op[1][0], k_rows[op[2]:op[3], 0], v_rows[op[2]:op[3], 0])
+        elif op[1][0][0].size:
+            pool.block_copy(op[1][0][0], op[1][0][1])
+    del k_rows, v_rows
+    qb = wl.bundle_q_bits(w)[0]
+    scale = 1.0 / math.sqrt(d)
+    print(f"[bench] cpu oracle set-up {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    B = len(w.decode)
+    done = 0
+    with threadpool_limits(limits=1):
+        start = time.perf_counter()
+        r = 0
+        while True:
+            att.paged_decode(pool, qb, list(ex.tables[0]), ex.seq_lens, scale,
+                             rows=[(r, h) for h in range(H)])
+            done += 1
+            r = (r + 1) % B
+            if time.perf_counter() - start >= seconds:
+                break
+        el = time.perf_counter() - start
+    per_layer = kv_bytes_total / w.total_layers
+    return {"value": round(per_layer * done / B / el / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "rows_per_s": round(done / el, 3),
+            "sample": f"{done} whole decode rows of layer 0 (all {w.num_q_heads} q-heads) of the "
+                      f"same workload, binary64 numpy oracle, 1 BLAS thread, {el:.1f}s; bytes "
+                      f"per row scaled to one layer"}
 
 
 def cpu_baseline(w, seconds, kv_bytes_total):

@@ -107,6 +107,17 @@ class BlockManager:
         self._lens[rid] = T + n
         return slots, copies
 
+    def blocks_needed(self, rid: int, n: int) -> int:
+        """Free blocks ``append(rid, n)`` would take (fresh blocks plus a
+        copy-on-write destination)."""
+        if n <= 0:
+            return 0
+        P = self.block_size
+        table = self._tables[rid]
+        T = self._lens[rid]
+        cow = T % P != 0 and self._ref[table[-1]] > 1
+        return int(cow) + -(-(T + n) // P) - len(table)
+
     # -- views ----------------------------------------------------------------
     def table(self, rid: int) -> List[int]:
         return list(self._tables[rid])
@@ -145,6 +156,59 @@ class BlockManager:
         self._ref[b] -= 1
         if self._ref[b] == 0:
             self._free.append(b)
+
+
+class BundleManager:
+    """Block bookkeeping for several cache groups ("M5.3", 0x03B: one pool
+    and one block table per group; 0x04E-0x04F: an append reserves the blocks
+    of every group before any group changes, so it succeeds in all groups or
+    in none).  Group g has its own block size, pool size and free FIFO; a
+    request has one length and one table per group.
+
+    ``append`` returns, per group, the slots for ``kv_append_bundle`` and the
+    (src, dst) pairs for ``block_copy_bundle``; issue the copies first.
+    """
+
+    def __init__(self, num_blocks: Sequence[int], block_sizes: Sequence[int],
+                 free_orders: Optional[Sequence[Sequence[int]]] = None):
+        if len(num_blocks) != len(block_sizes) or not num_blocks:
+            raise ValueError("one pool size and block size per group")
+        self.groups = [BlockManager(n, p, None if free_orders is None else free_orders[g])
+                       for g, (n, p) in enumerate(zip(num_blocks, block_sizes))]
+
+    def new_request(self) -> int:
+        ids = {m.new_request() for m in self.groups}
+        assert len(ids) == 1
+        return ids.pop()
+
+    def fork(self, rid: int) -> int:
+        ids = {m.fork(rid) for m in self.groups}
+        assert len(ids) == 1
+        return ids.pop()
+
+    def release(self, rid: int) -> None:
+        for m in self.groups:
+            m.release(rid)
+
+    def append(self, rid: int, n: int = 1):
+        """Reserve positions T .. T+n-1 in every group: ([slots per group],
+        [copies per group]); raises OutOfBlocks with no group changed."""
+        for g, m in enumerate(self.groups):
+            need = m.blocks_needed(rid, n)
+            if need > m.n_free():
+                raise OutOfBlocks(f"group {g}: request {rid} needs {need} blocks, "
+                                  f"{m.n_free()} free")
+        out = [m.append(rid, n) for m in self.groups]
+        return [o[0] for o in out], [o[1] for o in out]
+
+    def length(self, rid: int) -> int:
+        return self.groups[0].length(rid)
+
+    def block_tables(self, rids: Sequence[int]) -> List[np.ndarray]:
+        return [m.block_tables(rids) for m in self.groups]
+
+    def seq_lens(self, rids: Sequence[int]) -> np.ndarray:
+        return self.groups[0].seq_lens(rids)
 
 
 def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 256) -> int:

@@ -156,3 +156,62 @@ def test_block_tables_padding():
     assert m.block_tables([a, b], width=5).shape == (2, 5)
     with pytest.raises(ValueError):
         m.block_tables([a, b], width=2)
+
+
+# ---------------------------------------------------------------------------
+# BundleManager: several cache groups, all-or-nothing appends
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", range(4))
+def test_bundle_manager_matches_oracle_bundle_allocator(seed):
+    """Random scripts over two groups (P 16 and 32 or 64): the caller-side
+    BundleManager and the oracle's BundleAllocator give the same tables,
+    slots and copies, group by group."""
+    from block_table_attention_amd.blocks import BundleManager
+    from oracle.bundles import BundleAllocator
+
+    rng = np.random.default_rng(300 + seed)
+    Ps = [16, int(rng.choice([32, 64]))]
+    NB = [300, 160]
+    orders = [rng.permutation(n).tolist() for n in NB]
+    m = BundleManager(NB, Ps, free_orders=orders)
+    a = BundleAllocator(NB, Ps, free_orders=orders)
+    live = []
+    for _ in range(80):
+        op = rng.integers(4) if live else 0
+        if op == 0:
+            assert m.new_request() == a.new_request()
+            live.append(len(a.tables) and max(a.tables))
+        elif op == 1:
+            r = live[int(rng.integers(len(live)))]
+            assert m.fork(r) == a.fork(r)
+            live.append(max(a.tables))
+        elif op == 2 and len(live) > 1:
+            r = live.pop(int(rng.integers(len(live))))
+            m.release(r)
+            a.release(r)
+        else:
+            r = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(1, 30))
+            n0 = len(a.trace)
+            want = [a.append(r) for _ in range(n)]
+            slots, copies = m.append(r, n)
+            for g in range(2):
+                assert slots[g].tolist() == [w[g] for w in want]
+                ocopies = [(op[2], op[3]) for op in a.trace[n0:] if op[0] == "copy" and op[1] == g]
+                assert copies[g] == ocopies
+        for g in range(2):
+            for r in live:
+                assert m.groups[g].table(r) == a.table(r, g)
+
+
+def test_bundle_manager_all_or_nothing():
+    from block_table_attention_amd.blocks import BundleManager, OutOfBlocks
+
+    m = BundleManager([8, 2], [16, 16])
+    r = m.new_request()
+    m.append(r, 32)                        # group 1 full
+    state = ([list(g._free) for g in m.groups], [g.table(r) for g in m.groups])
+    with pytest.raises(OutOfBlocks):
+        m.append(r, 1)
+    assert ([list(g._free) for g in m.groups], [g.table(r) for g in m.groups]) == state
+    assert m.length(r) == 32

@@ -135,3 +135,41 @@ def test_binding_shape_checks():
                               [torch.zeros(3, dtype=torch.int32)])
     with pytest.raises(ValueError):
         pba.KVGroup(g.k, g.v[:, :, :, :, :8])
+
+
+def test_bench_bundle_plan_matches_oracle():
+    """bench.py's multi-group plan (package BundleManager) equals the oracle
+    bundle allocator's trace on the 32-layer workload's script: tables,
+    lengths, and the multiset of every group's copies and writes."""
+    import numpy as np
+
+    import bench
+    import workloads as wl
+    from harness import execute_bundle
+
+    w = wl.layers32(batch=12, forks=4)
+    plan = bench.plan_bundle_script(w)
+    ex = execute_bundle(w)
+    for g in range(2):
+        assert np.array_equal(plan.tables[g], ex.tables[g])
+    assert np.array_equal(plan.seq_lens, ex.seq_lens)
+    assert plan.n_writes == ex.n_writes
+    for g in range(2):
+        mine, theirs = [], []
+        for op in plan.setup:
+            if op[0] == "copy":
+                mine += [("copy", int(s), int(d)) for s, d in zip(*op[1][g])]
+            else:
+                mine += [("write", int(s), r) for s, r in zip(op[1][g], range(op[2], op[3]))]
+        lo, hi = plan.step_rows
+        mine += [("copy", int(s), int(d)) for s, d in zip(*plan.step_copies[g])]
+        mine += [("write", int(s), r) for s, r in zip(plan.step_slots[g], range(lo, hi))]
+        for op in ex.ops:
+            if op[0] == "copy":
+                theirs += [("copy", int(s), int(d)) for s, d in zip(*op[1][g])]
+            else:
+                theirs += [("write", int(s), r) for s, r in zip(op[1][g], range(op[2], op[3]))]
+        assert sorted(mine) == sorted(theirs)
+    # Every forked pair copies its shared tail in both groups during the step.
+    n_fork_tails = sum(1 for T in ex.seq_lens[:4] if (int(T) - 1) % 16)
+    assert [len(c[0]) for c in plan.step_copies] == [n_fork_tails] * 2
