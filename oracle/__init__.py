@@ -33,6 +33,10 @@ What it computes, and where the pages define it:
   whole-bundle appends and copies, and the all-or-nothing multi-group
   allocator with rollback.  "M5.3", sections 0x03B-0x03F, 0x04E-0x04F,
   0x05B-0x05C.
+* ``vattention`` -- contiguous virtual K/V: the reservation, page and slot
+  address algebra, the four ledgers, the slot/page lifecycle with retention
+  and reclamation, and decode by request-slot index with no block table.
+  "M5.3", sections 0x06A-0x06F, 0x0BJ.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values the pages
 print, closed forms, invariants, an independent library routine or brute force.
