@@ -20,7 +20,8 @@ __all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_pl
            "paged_decode_ragged", "expand_block_tables", "pack_block_tables",
            "paged_decode_shared", "paged_decode_shared_workspace_bytes", "SharedPlan",
            "paged_decode_workspace_bytes", "decode_workspace", "KVGroup", "kv_append_bundle",
-           "block_copy_bundle", "set_validate", "PBAError", "lib_path", "STATUS"]
+           "block_copy_bundle", "VKVArena", "paged_decode_contiguous", "set_validate", "PBAError",
+           "lib_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -41,7 +42,7 @@ PBA_F32, PBA_BF16 = 0, 1
 STATUS = {0: "PBA_OK", -1: "PBA_ERR_NULL_ARG", -2: "PBA_ERR_BAD_DTYPE", -3: "PBA_ERR_BAD_SHAPE",
           -4: "PBA_ERR_UNSUPPORTED", -5: "PBA_ERR_WORKSPACE_TOO_SMALL",
           -6: "PBA_ERR_OUT_OF_RANGE", -7: "PBA_ERR_OVERLAP", -8: "PBA_ERR_HIP",
-          -9: "PBA_ERR_HALF_BUNDLE"}
+          -9: "PBA_ERR_HALF_BUNDLE", -10: "PBA_ERR_OUT_OF_MEMORY"}
 MAX_GROUPS = 8
 _DTYPES = {torch.float32: PBA_F32, torch.bfloat16: PBA_BF16}
 
@@ -58,6 +59,20 @@ class PoolDesc(ctypes.Structure):
 class GroupDesc(ctypes.Structure):
     _fields_ = [("pool", PoolDesc), ("num_layers", ctypes.c_int32), ("reserved0", ctypes.c_int32),
                 ("k_stride_layer", ctypes.c_int64), ("v_stride_layer", ctypes.c_int64)]
+
+
+class VkvConfig(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("num_slots", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int64), ("page_bytes", ctypes.c_int64),
+                ("num_handles", ctypes.c_int64)]
+
+
+class VkvLedgers(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "reserved_bytes", "pool_bytes", "mapped_bytes", "inactive_retained_bytes", "free_bytes",
+        "bundle_maps", "bundle_unmaps", "slot_bytes")]
 
 
 class SharedPlanDesc(ctypes.Structure):
@@ -88,6 +103,15 @@ _SIGS = {
     "pba_group_layer_pool": (ctypes.c_int, [_GP, _i32, _P]),
     "pba_kv_append_bundle": (ctypes.c_int, [_GP, _i32, _vp, _vp, _vp, _i64, _vp]),
     "pba_block_copy_bundle": (ctypes.c_int, [_GP, _i32, _vp, _vp, _vp, _vp]),
+    "pba_vkv_create": (ctypes.c_int, [ctypes.POINTER(VkvConfig), ctypes.POINTER(_vp)]),
+    "pba_vkv_destroy": (ctypes.c_int, [_vp]),
+    "pba_vkv_map": (ctypes.c_int, [_vp, _i32, _i64]),
+    "pba_vkv_free": (ctypes.c_int, [_vp, _i32, _i32]),
+    "pba_vkv_group": (ctypes.c_int, [_vp, _GP, ctypes.POINTER(_i32)]),
+    "pba_vkv_capacity": (ctypes.c_int, [_vp, _i32, ctypes.POINTER(_i64)]),
+    "pba_vkv_get_ledgers": (ctypes.c_int, [_vp, ctypes.POINTER(VkvLedgers)]),
+    "pba_paged_decode_contiguous": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32,
+                                                   ctypes.c_float, _vp, _vp, _i32, _vp, _sz, _vp]),
     "pba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pba_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pba_version": (ctypes.c_int, []),
@@ -184,6 +208,10 @@ class KVPool:
     def dtype(self):
         return self.k.dtype
 
+    @property
+    def device(self):
+        return self.k.device
+
     def desc(self) -> PoolDesc:
         return self._desc
 
@@ -200,7 +228,7 @@ def _require(t: torch.Tensor, name: str, dtype, device, ndim: int):
 def kv_append(pool: KVPool, slot_mapping: torch.Tensor, k_new: torch.Tensor,
               v_new: torch.Tensor, stream=None) -> None:
     """Write row i of k_new/v_new [n, H_kv, d] at slot_mapping[i] (int64; < 0 skips)."""
-    dev = pool.k.device
+    dev = pool.device
     _require(slot_mapping, "slot_mapping", torch.int64, dev, 1)
     _require(k_new, "k_new", pool.dtype, dev, 3)
     _require(v_new, "v_new", pool.dtype, dev, 3)
@@ -213,7 +241,7 @@ def kv_append(pool: KVPool, slot_mapping: torch.Tensor, k_new: torch.Tensor,
 
 def block_copy(pool: KVPool, src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
     """Copy whole physical blocks src[k] -> dst[k] (int32 ids), K and V."""
-    dev = pool.k.device
+    dev = pool.device
     _require(src, "src", torch.int32, dev, 1)
     _require(dst, "dst", torch.int32, dev, 1)
     if src.shape != dst.shape:
@@ -249,10 +277,10 @@ def decode_workspace(pool: KVPool, num_q_heads: int, batch: int, max_blocks_per_
                                         partition_tokens)
     if need == 0:
         return None
-    key = (pool.k.device, _stream(stream), need)
+    key = (pool.device, _stream(stream), need)
     ws = _WORKSPACES.get(key)
     if ws is None:
-        ws = torch.zeros(need, dtype=torch.uint8, device=pool.k.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=pool.device)
         _WORKSPACES[key] = ws
     return ws
 
@@ -268,7 +296,7 @@ def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
     supplied workspace must be zero-filled before its first use (the library
     keeps it zeroed afterwards); without one, a cached zeroed workspace is used.
     """
-    dev = pool.k.device
+    dev = pool.device
     _require(q, "q", pool.dtype, dev, 3)
     _require(block_tables, "block_tables", torch.int32, dev, 2)
     _require(seq_lens, "seq_lens", torch.int32, dev, 1)
@@ -346,7 +374,7 @@ def paged_decode_shared(pool: KVPool, q: torch.Tensor, block_tables: torch.Tenso
     """paged_decode with shared-prefix execution reuse: same arguments and
     results, the plan in place of ``partition_tokens``.  A caller supplied
     workspace must be zero-filled before its first use."""
-    dev = pool.k.device
+    dev = pool.device
     _require(q, "q", pool.dtype, dev, 3)
     _require(block_tables, "block_tables", torch.int32, dev, 2)
     _require(seq_lens, "seq_lens", torch.int32, dev, 1)
@@ -391,7 +419,7 @@ def paged_decode_ragged(pool: KVPool, q: torch.Tensor, block_entries: torch.Tens
                         stream=None):
     """paged_decode over a compact table: row r is block_entries[row_offsets[r] :
     row_offsets[r + 1]] (int32 entries, int64 offsets [B + 1])."""
-    dev = pool.k.device
+    dev = pool.device
     _require(q, "q", pool.dtype, dev, 3)
     _require(block_entries, "block_entries", torch.int32, dev, 1)
     _require(row_offsets, "row_offsets", torch.int64, dev, 1)
@@ -507,6 +535,10 @@ class KVGroup:
     def dtype(self):
         return self.k.dtype
 
+    @property
+    def device(self):
+        return self.k.device
+
     def desc(self) -> GroupDesc:
         return self._desc
 
@@ -542,7 +574,7 @@ def kv_append_bundle(groups, slot_mappings, k_new, v_new, stream=None) -> None:
         raise ValueError("one slot mapping and one k_new/v_new per group")
     n = slot_mappings[0].shape[0] if G else 0
     for g, grp in enumerate(groups):
-        dev = grp.k.device
+        dev = grp.device
         _require(slot_mappings[g], f"slot_mappings[{g}]", torch.int64, dev, 1)
         _require(k_new[g], f"k_new[{g}]", grp.dtype, dev, 4)
         _require(v_new[g], f"v_new[{g}]", grp.dtype, dev, 4)
@@ -564,7 +596,7 @@ def block_copy_bundle(groups, src_blocks, dst_blocks, stream=None) -> None:
     if not (len(src_blocks) == len(dst_blocks) == G):
         raise ValueError("one src/dst list per group")
     for g, grp in enumerate(groups):
-        dev = grp.k.device
+        dev = grp.device
         _require(src_blocks[g], f"src_blocks[{g}]", torch.int32, dev, 1)
         _require(dst_blocks[g], f"dst_blocks[{g}]", torch.int32, dev, 1)
         if src_blocks[g].shape != dst_blocks[g].shape:
@@ -575,6 +607,139 @@ def block_copy_bundle(groups, src_blocks, dst_blocks, stream=None) -> None:
     _check("pba_block_copy_bundle", _lib.pba_block_copy_bundle(
         arr, G, vp(*[t.data_ptr() for t in src_blocks]), vp(*[t.data_ptr() for t in dst_blocks]),
         counts, _stream(stream)))
+
+
+class RawPool:
+    """A single-layer pool over memory the library manages (a layer of a
+    VKVArena): the same calls as ``KVPool`` accept it."""
+
+    def __init__(self, desc: PoolDesc, dtype, device, owner=None):
+        self._desc = desc
+        self._ref = ctypes.byref(desc)
+        self.dtype = dtype
+        self.device = device
+        self._owner = owner       # keeps the arena alive
+
+    num_blocks = property(lambda self: self._desc.num_blocks)
+    block_size = property(lambda self: self._desc.block_size)
+    num_kv_heads = property(lambda self: self._desc.num_kv_heads)
+    head_dim = property(lambda self: self._desc.head_dim)
+
+    def desc(self) -> PoolDesc:
+        return self._desc
+
+
+class VKVArena:
+    """Contiguous virtual K/V for ``num_slots`` request slots of every layer
+    (pba_vkv_*): a virtual reservation whose pages are mapped on demand.
+
+    ``map(slot, tokens)`` backs a slot's first rows; ``free(slot, retain)``
+    ends its request; the arena acts as a cache group for kv_append_bundle /
+    block_copy_bundle, and ``layer(l)`` is the pool of one layer for
+    paged_decode_contiguous (slot index, no block table).  Token t of slot r
+    has slot id ``slot_ids(r, t)``.
+    """
+
+    def __init__(self, layers: int, slots: int, max_tokens: int, num_kv_heads: int,
+                 head_dim: int, block_size: int = 16, page_bytes: int = 2 << 20,
+                 num_handles: int = 0, dtype=torch.bfloat16, device=None):
+        self.device = torch.device("cuda", torch.cuda.current_device()) if device is None \
+            else torch.device(device)
+        self.dtype = dtype
+        cfg = VkvConfig(_DTYPES[dtype], layers, slots, num_kv_heads, head_dim, block_size,
+                        max_tokens, page_bytes, num_handles)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            _check("pba_vkv_create", _lib.pba_vkv_create(ctypes.byref(cfg), ctypes.byref(h)))
+        self._h = h
+        self._desc = GroupDesc()
+        bps = ctypes.c_int32()
+        _check("pba_vkv_group", _lib.pba_vkv_group(h, ctypes.byref(self._desc), ctypes.byref(bps)))
+        self.blocks_per_slot = bps.value
+        self.num_slots = slots
+        self.max_tokens = max_tokens
+
+    num_layers = property(lambda self: self._desc.num_layers)
+    num_blocks = property(lambda self: self._desc.pool.num_blocks)
+    block_size = property(lambda self: self._desc.pool.block_size)
+    num_kv_heads = property(lambda self: self._desc.pool.num_kv_heads)
+    head_dim = property(lambda self: self._desc.pool.head_dim)
+
+    def desc(self) -> GroupDesc:
+        return self._desc
+
+    def layer(self, layer: int) -> RawPool:
+        out = PoolDesc()
+        _check("pba_group_layer_pool", _lib.pba_group_layer_pool(ctypes.byref(self._desc), layer,
+                                                                 ctypes.byref(out)))
+        return RawPool(out, self.dtype, self.device, self)
+
+    def map(self, slot: int, tokens: int) -> None:
+        _check("pba_vkv_map", _lib.pba_vkv_map(self._h, slot, tokens))
+
+    def free(self, slot: int, retain: bool = True) -> None:
+        _check("pba_vkv_free", _lib.pba_vkv_free(self._h, slot, 1 if retain else 0))
+
+    def capacity(self, slot: int) -> int:
+        t = ctypes.c_int64()
+        _check("pba_vkv_capacity", _lib.pba_vkv_capacity(self._h, slot, ctypes.byref(t)))
+        return t.value
+
+    def ledgers(self) -> dict:
+        led = VkvLedgers()
+        _check("pba_vkv_get_ledgers", _lib.pba_vkv_get_ledgers(self._h, ctypes.byref(led)))
+        return {f: getattr(led, f) for f, _ in led._fields_}
+
+    def slot_ids(self, slot, tokens):
+        """Slot ids of (slot, token) pairs for the append calls (numpy or int)."""
+        return slot * self.blocks_per_slot * self.block_size + tokens
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _check("pba_vkv_destroy", _lib.pba_vkv_destroy(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def paged_decode_contiguous(pool, q: torch.Tensor, slot_index: torch.Tensor,
+                            blocks_per_slot: int, seq_lens: torch.Tensor,
+                            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                            lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                            partition_tokens: int = 0, workspace: Optional[torch.Tensor] = None,
+                            stream=None):
+    """Decode with a request-slot index (int32 [B]) in place of a block table:
+    row r reads rows [0, seq_lens[r]) of slot slot_index[r]."""
+    dev = pool.device
+    _require(q, "q", pool.dtype, dev, 3)
+    _require(slot_index, "slot_index", torch.int32, dev, 1)
+    _require(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, Hq, D = q.shape
+    if D != pool.head_dim or slot_index.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, slot_index, seq_lens and the pool")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    else:
+        _require(out, "out", torch.float32, dev, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _require(lse, "lse", torch.float32, dev, 2)
+    if workspace is None and B > 0:
+        workspace = decode_workspace(pool, Hq, B, blocks_per_slot, partition_tokens, stream)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pba_paged_decode_contiguous", _lib.pba_paged_decode_contiguous(
+        pool._ref, q.data_ptr(), Hq, slot_index.data_ptr(), blocks_per_slot, seq_lens.data_ptr(),
+        B, ctypes.c_float(scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
+        partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+    return out, lse
 
 
 def set_validate(on: bool) -> bool:

@@ -228,6 +228,7 @@ struct PoolView {
   int last_block;  // num_blocks - 1: clamp for ids read ahead of the length
   int log2P;
   int split;       // kernel view: allocator tiles hold P << split rows
+  int64_t base_block = 0;  // contiguous slots: block j of the row is base_block + j
 };
 
 // Kernel block pb of a (possibly split) pool: allocator tile pb >> split, its
@@ -241,12 +242,21 @@ __device__ __forceinline__ int row_of(const PoolView& pv, int64_t pb) {
 // P == 16).  Ids are clamped into the pool so that a lookup made before the
 // request length is known (or past it) only ever addresses pool memory; rows
 // past the length are masked out of the result regardless.
+// Contiguous slots (IMPLICIT): no table; block j of the row is base_block + j,
+// with j clamped below the row's last block so that no address past the
+// request's mapped rows is formed.
+template <bool IMPLICIT = false>
 __device__ __forceinline__ void chunk_blocks(const PoolView& pv, int t0, int64_t& pb0,
                                              int64_t& pb1) {
   const int j0 = min(t0 >> pv.log2P, pv.max_blocks - 1);
-  pb0 = min(max(pv.trow[j0], 0), pv.last_block);
-  pb1 = pb0;
-  if (pv.log2P == 4) pb1 = min(max(pv.trow[min(j0 + 1, pv.max_blocks - 1)], 0), pv.last_block);
+  if constexpr (IMPLICIT) {
+    pb0 = pv.base_block + j0;
+    pb1 = pv.log2P == 4 ? pv.base_block + min(j0 + 1, pv.max_blocks - 1) : pb0;
+  } else {
+    pb0 = min(max(pv.trow[j0], 0), pv.last_block);
+    pb1 = pb0;
+    if (pv.log2P == 4) pb1 = min(max(pv.trow[min(j0 + 1, pv.max_blocks - 1)], 0), pv.last_block);
+  }
 }
 
 template <int D>
@@ -287,7 +297,7 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
 // the loads of the wave's next chunk tn, each issued as soon as the registers
 // it overwrites are consumed.  Tokens at or past t_end are masked out;
 // columns at or past ncols carry no probability mass.
-template <int D>
+template <int D, bool IMPLICIT = false>
 __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, int tn, int t_end,
                                            int ncols, float scale_log2,
                                            const bf16x8 (&qf)[D / 32], u32x4 (&kf)[2][D / 32],
@@ -297,7 +307,11 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
   constexpr int MT = D / 16;
   constexpr int CH = 32;
   int64_t nb0, nb1;
-  chunk_blocks(pv, tn, nb0, nb1);
+  chunk_blocks<IMPLICIT>(pv, tn, nb0, nb1);
+  // A second block that starts at or past the end holds no visible row: its
+  // loads go to the first block instead (and are masked), so no block past
+  // the row's last one is ever read.
+  if (tn + 16 >= t_end) nb1 = nb0;
 
   // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
   f32x4 s[2];
@@ -375,7 +389,10 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
 // XCDs round-robin in linear order, so with the partition as the slowest axis
 // every XCD gets an even share of the first partitions (never empty) and of
 // the later ones (empty past a short request's end).
-template <int D, bool RAGGED>
+// MODE: kTablesDense, kTablesRagged, or kTablesContiguous (`tables` is the
+// request-slot index [batch] and `max_blocks` the blocks of one slot: row r
+// reads blocks slot*max_blocks + j, with no table).
+template <int D, int MODE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
     const void* __restrict__ kbase, const void* __restrict__ vbase, int32_t max_blocks,
@@ -403,27 +420,33 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   // trip before the first table read).
   int64_t toff = (int64_t)r * max_blocks;
   int nblk = max_blocks;
-  if constexpr (RAGGED) {
+  if constexpr (MODE == kTablesRagged) {
     const int64_t __attribute__((address_space(4)))* ro =
         (const int64_t __attribute__((address_space(4)))*)a.row_offsets;
     toff = ro[r];
     nblk = (int)(ro[r + 1] - toff);
     if (nblk < 1) return;  // an empty row (rejected in validate mode)
   }
-  const PoolView pv{(table_t*)(tables + toff),
-                    static_cast<const uint16_t*>(kbase),
-                    static_cast<const uint16_t*>(vbase),
-                    k_sb, k_sh, a.v_sb, a.v_sh, nblk, last_block, log2P, a.split_log2};
-
   // Start-up: the request length and this wave's first block-table entries
-  // come back in one scalar round trip; q and the first chunk's K and V are
-  // requested right after, and only by waves that have a chunk, so the
-  // work-groups of partitions past a short request's end, and waves past it,
-  // read nothing else.  Issue order q, K, V keeps the in-loop waits exact.
+  // (or its slot) come back in one scalar round trip; q and the first
+  // chunk's K and V are requested right after, and only by waves that have a
+  // chunk, so the work-groups of partitions past a short request's end, and
+  // waves past it, read nothing else.  Issue order q, K, V keeps the in-loop
+  // waits exact.
   const int T = seq_lens[r];
+  PoolView pv{(table_t*)(tables + toff),
+              static_cast<const uint16_t*>(kbase),
+              static_cast<const uint16_t*>(vbase),
+              k_sb, k_sh, a.v_sb, a.v_sh, nblk, last_block, log2P, a.split_log2};
+  constexpr bool IMPLICIT = MODE == kTablesContiguous;
+  if constexpr (IMPLICIT) {
+    const int slot = ((const int32_t __attribute__((address_space(4)))*)tables)[r];
+    pv.base_block = (int64_t)slot * max_blocks;
+    pv.max_blocks = max(1, (T + (1 << log2P) - 1) >> log2P);
+  }
   int t0 = p_begin + wave * CH;
   int64_t pb0, pb1;
-  chunk_blocks(pv, t0, pb0, pb1);
+  chunk_blocks<IMPLICIT>(pv, t0, pb0, pb1);
   // The bundle fields the first loads need are fetched with the length, not
   // after the test on it (which would add a scalar round trip).
   const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
@@ -431,6 +454,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   asm volatile("" ::"s"(qbase), "s"(num_q_heads), "s"(G), "s"(pv.v_sb), "s"(pv.v_sh),
                "s"(pv.split));
   if (p_begin >= T) return;  // empty partition: never counted, never read
+  if (t0 + 16 >= T) pb1 = pb0;  // no block past the row's last one is read
   const int p_end = min(T, p_begin + part_tokens);
   // This wave's chunks: p_begin + wave*CH + k*kWaves*CH for k < n_w.
   const int span = p_end - p_begin - wave * CH;
@@ -470,7 +494,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     // requested again (in bounds, served from L2), which keeps the number of
     // loads in flight the same on every iteration.
     const int tn = it + 1 < n_w ? t0 + kWaves * CH : t0;
-    chunk_step<D>(pv, h, t0, tn, T, G, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
+    chunk_step<D, IMPLICIT>(pv, h, t0, tn, T, G, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
   }
 
   // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n]: four
@@ -596,6 +620,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   if (n_w > 0) {
     int64_t pb0, pb1;
     chunk_blocks(pv, t0, pb0, pb1);
+    if (t0 + 16 >= te) pb1 = pb0;  // no block past the piece's last one is read
     const int cn = n < ncols ? n : 0;
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            ((int64_t)(row0 + trow0 + cn / G) * a.num_q_heads +
@@ -845,8 +870,10 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     DecodeArgs s = a;
     const int64_t rows = (int64_t)r0 * a.num_q_heads;
     s.q = static_cast<const char*>(a.q) + rows * head_dim * (dtype == PBA_BF16 ? 2 : 4);
-    if (a.row_offsets)
+    if (a.table_mode == kTablesRagged)
       s.row_offsets = a.row_offsets + r0;  // entries stay put: offsets are absolute
+    else if (a.table_mode == kTablesContiguous)
+      s.tables = a.tables + r0;            // one slot index per request
     else
       s.tables = a.tables + (int64_t)r0 * a.max_blocks;
     s.seq_lens = a.seq_lens + r0;
@@ -859,9 +886,14 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     const dim3 grid((unsigned)a.num_kv_heads, (unsigned)nb, (unsigned)a.n_parts);
     const dim3 block(kDecodeThreads);
     if (dtype == PBA_BF16) {
-      auto kern = a.row_offsets
-                      ? (head_dim == 128 ? decode_bf16_kernel<128, true> : decode_bf16_kernel<64, true>)
-                      : (head_dim == 128 ? decode_bf16_kernel<128, false> : decode_bf16_kernel<64, false>);
+      auto kern = a.table_mode == kTablesRagged
+                      ? (head_dim == 128 ? decode_bf16_kernel<128, kTablesRagged>
+                                         : decode_bf16_kernel<64, kTablesRagged>)
+                  : a.table_mode == kTablesContiguous
+                      ? (head_dim == 128 ? decode_bf16_kernel<128, kTablesContiguous>
+                                         : decode_bf16_kernel<64, kTablesContiguous>)
+                      : (head_dim == 128 ? decode_bf16_kernel<128, kTablesDense>
+                                         : decode_bf16_kernel<64, kTablesDense>);
       hipLaunchKernelGGL(kern, grid, block, 0, stream, s.tables, s.seq_lens, s.k, s.v,
                          s.max_blocks, s.part_tokens, s.log2P, s.num_blocks - 1,
                          (int32_t)s.k_sb, (int32_t)s.k_sh, s);

@@ -13,6 +13,7 @@
 
 #include "bundle_internal.h"
 #include "pba_internal.h"
+#include "vkv_internal.h"
 
 namespace {
 
@@ -229,6 +230,7 @@ const char* pba_status_string(int status) {
     case PBA_ERR_OVERLAP: return "duplicate slot or overlapping copy pairs";
     case PBA_ERR_HIP: return "HIP runtime error";
     case PBA_ERR_HALF_BUNDLE: return "a token or copy would move some cache groups only";
+    case PBA_ERR_OUT_OF_MEMORY: return "no free or reclaimable physical page in the arena";
     default: return "unknown status";
   }
 }
@@ -255,6 +257,7 @@ int pba_kv_append(const pba_kv_pool* pool, const int64_t* slot_mapping, int64_t 
       if (x >= limit) return PBA_ERR_OUT_OF_RANGE;
       if (!seen.insert(x).second) return PBA_ERR_OVERLAP;
     }
+    if ((st = pba::vkv_check_slot_ids(pool->k, slots.data(), n_tokens))) return st;
   }
   pba::AppendArgs a;
   a.k = pool->k;
@@ -292,6 +295,9 @@ int pba_block_copy(const pba_kv_pool* pool, const int32_t* src, const int32_t* d
         return PBA_ERR_OUT_OF_RANGE;
       if (!dsts.insert(hd[i]).second || srcs.count(hd[i])) return PBA_ERR_OVERLAP;
     }
+    if ((st = pba::vkv_check_blocks(pool->k, hs.data(), n_pairs)) ||
+        (st = pba::vkv_check_blocks(pool->k, hd.data(), n_pairs)))
+      return st;
   }
   pba::CopyArgs a;
   a.k = pool->k;
@@ -350,6 +356,7 @@ int pba_kv_append_bundle(const pba_kv_group* groups, int32_t num_groups,
         if (x >= limit) return PBA_ERR_OUT_OF_RANGE;
         if (!seen.insert(x).second) return PBA_ERR_OVERLAP;
       }
+      if ((st = pba::vkv_check_slot_ids(groups[g].pool.k, slots[g].data(), n_tokens))) return st;
     }
     for (int64_t i = 0; i < n_tokens; ++i) {
       int skipped = 0;
@@ -422,6 +429,9 @@ int pba_block_copy_bundle(const pba_kv_group* groups, int32_t num_groups,
         if (hs[i] < 0 || hs[i] >= nb || hd[i] < 0 || hd[i] >= nb) return PBA_ERR_OUT_OF_RANGE;
         if (!dsts.insert(hd[i]).second || srcs.count(hd[i])) return PBA_ERR_OVERLAP;
       }
+      if ((st = pba::vkv_check_blocks(groups[g].pool.k, hs.data(), n_pairs[g])) ||
+          (st = pba::vkv_check_blocks(groups[g].pool.k, hd.data(), n_pairs[g])))
+        return st;
     }
   }
   pba::BundleCopyArgs a{};
@@ -476,15 +486,18 @@ size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_h
                           pool->head_dim).bytes;
 }
 
-// Dense (row_offsets == nullptr: row r at r * max_blocks_per_seq) or ragged
-// (row r = block_tables[row_offsets[r] .. row_offsets[r + 1])) decode.
+// Dense (row r at r * max_blocks_per_seq), ragged (row r =
+// block_tables[row_offsets[r] .. row_offsets[r + 1])) or contiguous
+// (block_tables = slot index, max_blocks_per_seq = blocks per slot) decode.
 static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
                        const int32_t* block_tables, const int64_t* row_offsets,
                        int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
                        float scale, float* out, float* lse, int32_t partition_tokens,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       int mode = pba::kTablesDense) {
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
+  if (mode == pba::kTablesContiguous && pool->dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
   const int G = num_q_heads / pool->num_kv_heads;
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
@@ -503,7 +516,15 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
     std::vector<int32_t> lens, tab;
     std::vector<int64_t> offs;
     if (!copy_to_host(lens, seq_lens, batch, s)) return PBA_ERR_HIP;
-    if (row_offsets) {
+    if (mode == pba::kTablesContiguous) {
+      if (!copy_to_host(tab, block_tables, batch, s)) return PBA_ERR_HIP;
+      const int64_t n_slots = pool->num_blocks / max_blocks_per_seq;
+      const int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
+      for (int32_t r = 0; r < batch; ++r)
+        if (tab[r] < 0 || tab[r] >= n_slots || lens[r] < 1 || lens[r] > cap)
+          return PBA_ERR_OUT_OF_RANGE;
+      if ((st = pba::vkv_check_rows(pool->k, tab.data(), lens.data(), batch))) return st;
+    } else if (row_offsets) {
       if (!copy_to_host(offs, row_offsets, (int64_t)batch + 1, s)) return PBA_ERR_HIP;
       if (offs[0] < 0) return PBA_ERR_OUT_OF_RANGE;
       for (int32_t r = 0; r < batch; ++r)
@@ -514,7 +535,7 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
       if (!copy_to_host(tab, block_tables, (int64_t)batch * max_blocks_per_seq, s)) return PBA_ERR_HIP;
     }
     const int64_t cap = (int64_t)max_blocks_per_seq * pool->block_size;
-    for (int32_t r = 0; r < batch; ++r) {
+    for (int32_t r = 0; r < batch && mode != pba::kTablesContiguous; ++r) {
       const int64_t T = lens[r];
       if (T < 1 || T > cap) return PBA_ERR_OUT_OF_RANGE;
       const int64_t nb = (T + pool->block_size - 1) / pool->block_size;
@@ -524,6 +545,7 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
         const int32_t b = tab[(size_t)(base + j)];
         if (b < 0 || b >= pool->num_blocks) return PBA_ERR_OUT_OF_RANGE;
       }
+      if ((st = pba::vkv_check_blocks(pool->k, tab.data() + base, nb))) return st;
     }
   }
   pba::DecodeArgs a;
@@ -546,6 +568,9 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
   a.num_blocks = pool->num_blocks;
   a.split_log2 = pool->split_log2;
   a.row_offsets = row_offsets;
+  a.table_mode = mode == pba::kTablesContiguous ? mode
+                 : row_offsets                  ? pba::kTablesRagged
+                                                : pba::kTablesDense;
   a.log2P = log2_exact(pool->block_size);
   a.G = G;
   a.num_q_heads = num_q_heads;
@@ -576,6 +601,18 @@ int pba_paged_decode_ragged(const pba_kv_pool* pool, const void* q, int32_t num_
   return decode_impl(pool, q, num_q_heads, block_entries, row_offsets, max_blocks_per_seq,
                      seq_lens, batch, scale, out, lse, partition_tokens, workspace,
                      workspace_bytes, stream);
+}
+
+int pba_paged_decode_contiguous(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                                const int32_t* slot_index, int32_t blocks_per_slot,
+                                const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                                float* lse, int32_t partition_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (pool && blocks_per_slot > 0 && pool->num_blocks % blocks_per_slot) return PBA_ERR_BAD_SHAPE;
+  if (pool && pool->split_log2) return PBA_ERR_UNSUPPORTED;
+  return decode_impl(pool, q, num_q_heads, slot_index, nullptr, blocks_per_slot, seq_lens, batch,
+                     scale, out, lse, partition_tokens, workspace, workspace_bytes, stream,
+                     pba::kTablesContiguous);
 }
 
 int pba_expand_block_tables(const int32_t* src, int64_t n_entries, int32_t split_log2,
@@ -776,6 +813,7 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
   a.num_blocks = pool->num_blocks;
   a.split_log2 = pool->split_log2;
   a.row_offsets = nullptr;
+  a.table_mode = pba::kTablesDense;
   a.log2P = log2_exact(pool->block_size);
   a.G = num_q_heads / pool->num_kv_heads;
   a.num_q_heads = num_q_heads;

@@ -32,6 +32,13 @@ struct CopyArgs {
   int32_t esize;
 };
 
+// How a decode row finds its blocks: a dense table row, a ragged table row,
+// or no table (contiguous slots: `tables` holds one slot index per request and
+// `max_blocks` the blocks of a slot).
+constexpr int kTablesDense = 0;
+constexpr int kTablesRagged = 1;
+constexpr int kTablesContiguous = 2;
+
 // Decode: one work-group per (partition, kv head, request).  The decode kernel
 // takes k_sb and k_sh as int32 (the host rejects larger strides).
 struct DecodeArgs {
@@ -48,6 +55,7 @@ struct DecodeArgs {
   int32_t* counters;  // [B][H_kv]: partitions finished; zero between calls
   const int64_t* row_offsets;  // ragged tables: row r = tables[row_offsets[r] ..
                                // row_offsets[r + 1]); nullptr for dense tables
+  int32_t table_mode;  // kTablesDense / kTablesRagged / kTablesContiguous
   int32_t max_blocks;
   int32_t num_blocks;  // pool size: clamp for block ids read ahead of the length
   int32_t log2P;

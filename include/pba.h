@@ -47,8 +47,10 @@ typedef enum pba_status {
   PBA_ERR_OUT_OF_RANGE = -6,        /* validate mode: bad id, slot or length   */
   PBA_ERR_OVERLAP = -7,             /* validate mode: duplicate slot / pair    */
   PBA_ERR_HIP = -8,                 /* a HIP runtime call failed               */
-  PBA_ERR_HALF_BUNDLE = -9          /* validate mode: a token or copy list that
+  PBA_ERR_HALF_BUNDLE = -9,         /* validate mode: a token or copy list that
                                        would move some cache groups only       */
+  PBA_ERR_OUT_OF_MEMORY = -10       /* contiguous arena: no free or reclaimable
+                                       physical page for the request           */
 } pba_status;
 
 typedef enum pba_dtype { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
@@ -365,6 +367,94 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
                             const int32_t* seq_lens, int32_t batch, float scale, float* out,
                             float* lse, const pba_shared_plan* plan, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/*
+ * Contiguous virtual K/V ("M5.3", 0x06A-0x06F; vAttention): a second kernel
+ * boundary with no user block table.  One virtual reservation holds the K and
+ * V tensor of every layer for num_slots request slots; physical pages of
+ * page_bytes are created as HIP virtual-memory handles and mapped into a
+ * slot's range on demand, in page bundles (page q of the slot in every K and
+ * V tensor, mapped and made accessible together before the slot's frontier
+ * moves).
+ *
+ * Layout: tensor x = 2 * layer + (0: K, 1: V) starts at x * num_slots * R
+ * bytes from the reservation; slot r's range of a tensor is [r R, (r+1) R),
+ * R = page_bytes * ceil(ceil(max_tokens / P) * P * row / page_bytes) with
+ * row = num_kv_heads * head_dim * scalar bytes; inside it, token t sits in
+ * tile t / P (P rows of every head) in the library's K and V tile layouts.
+ * The arena is therefore also a cache group (pba_vkv_group) whose block j of
+ * slot r is block id r * blocks_per_slot + j, and token t of slot r has slot
+ * id r * blocks_per_slot * P + t for pba_kv_append / pba_kv_append_bundle.
+ *
+ * Rows may be written and read only below the slot's mapped frontier
+ * (pba_vkv_capacity); reading or writing past it touches unmapped memory.
+ * In validate mode the append, copy and decode calls on an arena's memory
+ * check the frontier (PBA_ERR_OUT_OF_RANGE).  Unmapping (pba_vkv_free without
+ * retain, reclamation in pba_vkv_map) first waits for the device to be idle.
+ */
+typedef struct pba_vkv_arena pba_vkv_arena;
+
+typedef struct pba_vkv_config {
+  int32_t dtype;         /* PBA_BF16 or PBA_F32 */
+  int32_t num_layers;    /* L: K and V tensors per layer */
+  int32_t num_slots;     /* B: request slots */
+  int32_t num_kv_heads;  /* H_kv */
+  int32_t head_dim;      /* 64 or 128 */
+  int32_t block_size;    /* P: rows of one tile, a power of two in 16..256 */
+  int64_t max_tokens;    /* T_max: rows reserved per slot */
+  int64_t page_bytes;    /* G: a multiple of the device's virtual-memory
+                            granularity and of P * row */
+  int64_t num_handles;   /* physical pages created up front (a multiple of 2L);
+                            0: pages are created when needed, without limit */
+} pba_vkv_config;
+
+typedef struct pba_vkv_ledgers {  /* 0x06A: the ledgers are separate quantities */
+  int64_t reserved_bytes;           /* M_VA: virtual reservation */
+  int64_t pool_bytes;               /* M_phys,pool: handles created */
+  int64_t mapped_bytes;             /* M_mapped: handles mapped into slots */
+  int64_t inactive_retained_bytes;  /* mapped into freed slots, kept for reuse */
+  int64_t free_bytes;               /* created, not mapped */
+  int64_t bundle_maps, bundle_unmaps;  /* page bundles mapped / unmapped so far */
+  int64_t slot_bytes;               /* R */
+} pba_vkv_ledgers;
+
+/* Reserve the arena on the current device; creates num_handles pages. */
+int pba_vkv_create(const pba_vkv_config* cfg, pba_vkv_arena** out);
+/* Wait for the device, unmap and release every page, free the reservation. */
+int pba_vkv_destroy(pba_vkv_arena* arena);
+/* Back the first `tokens` rows of the slot (0x06D: map before use).  A freed
+ * slot becomes active for a new request generation: its retained pages are
+ * reused as capacity, none of its old rows are valid (0x06E).  Pages come
+ * from free handles, then from the highest bundle of the lowest-numbered
+ * inactive slot; if the pool cannot supply them the call changes nothing and
+ * returns PBA_ERR_OUT_OF_MEMORY.  Synchronous on the host. */
+int pba_vkv_map(pba_vkv_arena* arena, int32_t slot, int64_t tokens);
+/* Mark the slot inactive; retain != 0 keeps its pages mapped (delayed
+ * reclamation), otherwise they are unmapped and return to the pool. */
+int pba_vkv_free(pba_vkv_arena* arena, int32_t slot, int32_t retain);
+/* The arena as a cache group (every layer) and the blocks of one slot. */
+int pba_vkv_group(const pba_vkv_arena* arena, pba_kv_group* out, int32_t* blocks_per_slot);
+/* Rows of the slot below its mapped frontier. */
+int pba_vkv_capacity(const pba_vkv_arena* arena, int32_t slot, int64_t* tokens);
+int pba_vkv_get_ledgers(const pba_vkv_arena* arena, pba_vkv_ledgers* out);
+
+/*
+ * pba_paged_decode_contiguous -- pba_paged_decode with a request-slot index
+ * in place of the block table ("M5.3", 0x06C: the kernel reads no block table,
+ * only the slot of each request, as FlashAttention's cache_batch_idx): row r
+ * reads rows [0, seq_lens[r]) of slot slot_index[r], i.e. blocks
+ * slot_index[r] * blocks_per_slot + j of `pool` (a layer of pba_vkv_group, or
+ * any pool laid out that way).  No block past the row's last one is
+ * addressed.  slot_index: device int32 [batch], in [0, num_blocks /
+ * blocks_per_slot); 1 <= seq_lens[r] <= blocks_per_slot * P (validate mode,
+ * which also checks arena frontiers).  Partitions are planned as for the dense
+ * call with max_blocks_per_seq = blocks_per_slot.  bf16 pools only.
+ */
+int pba_paged_decode_contiguous(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                                const int32_t* slot_index, int32_t blocks_per_slot,
+                                const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                                float* lse, int32_t partition_tokens, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* pba_status_string(int status);

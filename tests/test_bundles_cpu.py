@@ -173,3 +173,57 @@ def test_bench_bundle_plan_matches_oracle():
     # Every forked pair copies its shared tail in both groups during the step.
     n_fork_tails = sum(1 for T in ex.seq_lens[:4] if (int(T) - 1) % 16)
     assert [len(c[0]) for c in plan.step_copies] == [n_fork_tails] * 2
+
+
+# ---------------------------------------------------------------------------
+# Contiguous arenas and the slot-indexed decode: host-side rejections
+# ---------------------------------------------------------------------------
+def _vkv_cfg(**kw):
+    pba = _pba()
+    d = dict(dtype=1, num_layers=2, num_slots=4, num_kv_heads=2, head_dim=128, block_size=16,
+             max_tokens=300, page_bytes=65536, num_handles=0)
+    d.update(kw)
+    return pba.VkvConfig(**d)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=5), -2),
+    (dict(num_layers=0), -3),
+    (dict(num_slots=0), -3),
+    (dict(max_tokens=0), -3),
+    (dict(page_bytes=0), -3),
+    (dict(num_handles=-4), -3),
+    (dict(head_dim=96), -4),
+    (dict(block_size=8), -4),
+    (dict(block_size=48), -4),
+])
+def test_arena_config_rejections(kw, status):
+    """Rejected before any HIP call (these run without a GPU)."""
+    pba = _pba()
+    h = ctypes.c_void_p()
+    assert pba._lib.pba_vkv_create(ctypes.byref(_vkv_cfg(**kw)), ctypes.byref(h)) == status
+    assert not h.value
+    assert pba._lib.pba_vkv_create(NULL, ctypes.byref(h)) == -1
+    assert pba._lib.pba_vkv_map(NULL, 0, 1) == -1
+    assert pba._lib.pba_vkv_free(NULL, 0, 1) == -1
+    assert pba._lib.pba_vkv_destroy(NULL) == -1
+
+
+def test_contiguous_decode_host_rejections():
+    pba = _pba()
+    lib = pba._lib
+    d = pba.PoolDesc(0x10000, 0x20000, 1, 64, 16, 2, 128, 0, 2 * 16 * 128, 16 * 128,
+                     2 * 16 * 128, 16 * 128)
+    call = lambda desc, bps: lib.pba_paged_decode_contiguous(
+        ctypes.byref(desc), 0x30000, 8, 0x40000, bps, 0x50000, 2, ctypes.c_float(0.1), 0x60000,
+        NULL, 0, NULL, 0, NULL)
+    assert call(d, 5) == -3                    # 64 blocks are not whole slots of 5
+    assert call(d, 0) == -3
+    f32 = pba.PoolDesc(0x10000, 0x20000, 0, 64, 16, 2, 128, 0, 2 * 16 * 128, 16 * 128,
+                       2 * 16 * 128, 16 * 128)
+    assert call(f32, 8) == -4                  # bf16 only
+    split = pba.PoolDesc(0x10000, 0x20000, 1, 64, 16, 2, 128, 1, 2 * 32 * 128, 32 * 128,
+                         2 * 32 * 128, 32 * 128)
+    assert call(split, 8) == -4
+    assert lib.pba_paged_decode_contiguous(ctypes.byref(d), NULL, 8, NULL, 8, NULL, 0,
+                                           ctypes.c_float(0.1), NULL, NULL, 0, NULL, 0, NULL) == 0
