@@ -67,6 +67,12 @@ def parse():
     ap.add_argument("--kernel-block", type=int, default=0,
                     help="decode through a kernel view of this many tokens per block (the "
                          "allocator blocks split; tables expanded by the library)")
+    ap.add_argument("--kv", default="paged", choices=["paged", "contiguous", "contiguous-plain"],
+                    help="K/V layout: the paged pool (block tables), a contiguous virtual "
+                         "arena with pages mapped on demand (slot index, no block table), or "
+                         "the same contiguous layout in one ordinary device allocation")
+    ap.add_argument("--page-mib", type=float, default=2.0,
+                    help="physical page size of the contiguous arena, MiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--decode-only", action="store_true",
@@ -225,11 +231,18 @@ def main():
         return copy_calibration(args, pba, torch, dev)
     names = WORKLOADS if args.sweep else [args.workload]
     for name in names:
+        if args.kv.startswith("contiguous") and (name in BUNDLE_WORKLOADS or name == "tiny"):
+            continue          # the contiguous arena path covers the bf16 single-layer workloads
         if name in BUNDLE_WORKLOADS:
             result = run_bundle(args, name, pba, torch, dev)
             if not (args.sweep or args.no_cpu_baseline):
                 result["cpu_baseline"] = cpu_baseline_bundle(make_workload(name), args.cpu_seconds,
                                                              result["_kv_value_bytes"])
+        elif args.kv.startswith("contiguous"):
+            result = run_contiguous(args, name, pba, torch, dev)
+            if not (args.sweep or args.no_cpu_baseline):
+                w = make_workload(name)
+                result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, result["_kv_value_bytes"])
         else:
             result = run_workload(args, name, pba, torch, dev)
             if not (args.sweep or args.no_cpu_baseline):
@@ -755,6 +768,140 @@ def run_bundle(args, name, pba, torch, dev):
         "_kv_value_bytes": kv_unique,
     }
     del groups, ws
+    torch.cuda.empty_cache()
+    return result
+
+
+def run_contiguous(args, name, pba, torch, dev):
+    """The same decode batch over a contiguous virtual arena (vAttention
+    layout): one slot per request, pages mapped for each request's rows, no
+    block table.  A step is kv_append of the step's tokens (slot ids in the
+    arena) + paged_decode_contiguous.  The arena's rows are synthetic draws
+    written once (the decode's time does not depend on their values); requests
+    that share blocks in the paged pool each hold their own rows here."""
+    w = make_workload(name)
+    sh = w.shape
+    if sh.dtype != "bf16":
+        raise SystemExit(f"{name}: the contiguous decode is bf16 only")
+    Hq, Hkv, d = sh.num_q_heads, sh.num_kv_heads, sh.head_dim
+    plan = plan_script(w)
+    lens = plan.seq_lens.astype(np.int64)
+    B = len(lens)
+    P = 64 if sh.block_size >= 64 else sh.block_size
+    page = int(args.page_mib * (1 << 20))
+    virtual = args.kv == "contiguous"
+    if virtual:
+        arena = pba.VKVArena(1, B, int(lens.max()), Hkv, d, P, page, dtype=torch.bfloat16,
+                             device=dev)
+        t0 = time.perf_counter()
+        for r in range(B):
+            arena.map(r, int(lens[r]))
+        map_s = time.perf_counter() - t0
+        led = arena.ledgers()
+        bundles = led["bundle_maps"]
+        pool = arena.layer(0)
+        bps = arena.blocks_per_slot
+        slot_ids = arena.slot_ids
+    else:                     # the same layout in one device allocation, no VMM
+        bps = int(-(-int(lens.max()) // P))
+        pool = pba.KVPool.empty(B * bps, P, Hkv, d, torch.bfloat16, dev)
+        slot_ids = lambda r, t: r * bps * P + t
+        map_s, bundles, led = 0.0, 0, None
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    for r in range(B):            # rows 0 .. T-2; the step appends row T-1
+        n = int(lens[r]) - 1
+        if n <= 0:
+            continue
+        ids = torch.from_numpy(slot_ids(r, np.arange(n, dtype=np.int64))).to(dev)
+        k = torch.randn((n, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((n, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+        pba.kv_append(pool, ids, k, v)
+    step_ids = torch.from_numpy(slot_ids(np.arange(B, dtype=np.int64), lens - 1)).to(dev)
+    k_step = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    v_step = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+    slot_index = torch.arange(B, dtype=torch.int32, device=dev)
+    lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
+    req_pt = args.partition_tokens
+    if req_pt < 0:
+        from block_table_attention_amd.blocks import suggest_partition_tokens
+        req_pt = suggest_partition_tokens(lens, Hkv)
+    pt, n_parts = pba.paged_decode_plan(pool, Hq, B, bps, req_pt)
+    ws = torch.zeros(max(pba.paged_decode_workspace_bytes(pool, Hq, B, bps, req_pt), 16),
+                     dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(d)
+    stream = torch.cuda.current_stream()
+
+    def decode():
+        pba.paged_decode_contiguous(pool, q, slot_index, bps, lens_d, scale, out=out, lse=lse,
+                                    partition_tokens=req_pt, workspace=ws)
+
+    def step():
+        pba.kv_append(pool, step_ids, k_step, v_step)
+        decode()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    t_start = time.perf_counter()
+    for _ in range(K):
+        step()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t_start) * 1e3 / K
+    b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    b0.record(stream)
+    for _ in range(K):
+        decode()
+    b1.record(stream)
+    torch.cuda.synchronize()
+    dec_avg_ms = b0.elapsed_time(b1) / K
+    row = Hkv * d * 2 * 2
+    kv_bytes = int(lens.sum()) * row
+    alg = kv_bytes + B * Hq * d * 2 + B * Hq * d * 4 + B * Hq * 4 + B * 4 * 2
+    achieved = alg / (dec_avg_ms * 1e-3) / 1e9
+    step_gbs = kv_bytes / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] {name} {args.kv}: {ms_per_step * 1e3:.1f} us/step, decode burst "
+          f"{dec_avg_ms * 1e3:.1f} us/launch; mapped {bundles} page bundles in "
+          f"{map_s * 1e3:.1f} ms", file=sys.stderr, flush=True)
+    traffic = profiled_traffic(f"contig_{name}") if virtual and args.partition_tokens < 0 and \
+        args.page_mib == 2.0 else None
+    result = {
+        "metric": "paged decode: KV GB/s achieved (% of HBM peak) + query rows/s at 1 GPU",
+        "value": round(step_gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (N(0,1) K/V/q rounded to bf16, drawn on the device)",
+        "config": {"workload": f"{name} over a contiguous "
+                               f"{'virtual arena' if virtual else 'device buffer'}: batch {B}, context "
+                               f"{int(lens.min())}..{int(lens.max())} (sum {int(lens.sum())}), "
+                               f"tile {P} rows, {Hq} q-heads / {Hkv} kv-heads, head_dim {d}, "
+                               f"pages of {page >> 10} KiB",
+                   "kv_layout": args.kv, "batch": B, "context_sum": int(lens.sum()),
+                   "tile_rows": P, "blocks_per_slot": bps, "page_bytes": page,
+                   "partition_tokens": pt, "num_partitions": n_parts,
+                   "step": f"kv_append({B} tokens) + paged_decode_contiguous",
+                   "step_launch": "eager"},
+        "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "decode_us": round(dec_avg_ms * 1e3, 2),
+        "arena": None if not virtual else
+                 {"reserved_bytes": led["reserved_bytes"], "mapped_bytes": led["mapped_bytes"],
+                  "pool_bytes": led["pool_bytes"], "page_bundles_mapped": bundles,
+                  "map_ms_total": round(map_s * 1e3, 2),
+                  "map_us_per_bundle": round(map_s * 1e6 / max(bundles, 1), 1),
+                  "mapped_over_rows": round(led["mapped_bytes"] / kv_bytes, 4)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": f"decode_bf16_kernel<{d}, contiguous> (slot index, no block table)",
+                     "algorithmic_bytes_per_launch": alg},
+        "_kv_value_bytes": kv_bytes,
+    }
+    del pool
+    if virtual:
+        arena.close()
     torch.cuda.empty_cache()
     return result
 
