@@ -44,6 +44,18 @@ WORKLOADS = ["long16k", "long64k", "batch32", "shared_prefix", "lognormal_p16",
 BUNDLE_WORKLOADS = {"layers32"}
 
 
+AUTO = -2      # --partition-tokens auto: the caller's choice from the batch's lengths
+BALANCED = -1  # the library's balanced decomposition (PBA_PARTITIONS_BALANCED)
+
+
+def _partition_arg(v: str) -> int:
+    if v == "auto":
+        return AUTO
+    if v == "balanced":
+        return BALANCED
+    return int(v)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,9 +64,11 @@ def parse():
     ap.add_argument("--workload", default="long16k", choices=WORKLOADS)
     ap.add_argument("--sweep", action="store_true",
                     help="every workload in turn, one JSON line each (no cpu_baseline)")
-    ap.add_argument("--partition-tokens", type=int, default=-1,
-                    help="decode partition length; 0 = the library's plan; default: chosen "
-                         "from the batch's lengths by blocks.suggest_partition_tokens")
+    ap.add_argument("--partition-tokens", type=_partition_arg, default=AUTO,
+                    help="decode partitions: a length in tokens, 0 = the library's plan, "
+                         "'balanced' = the batch's chunks spread evenly over the CUs; default "
+                         "'auto': chosen from the batch's lengths by "
+                         "blocks.suggest_partition_tokens")
     ap.add_argument("--decode", default="auto", choices=["auto", "plain", "shared"],
                     help="decode entry point: paged_decode, paged_decode_shared (shared-prefix "
                          "execution reuse), or auto = shared when the batch shares chunks")
@@ -333,9 +347,9 @@ def run_workload(args, name, pba, torch, dev):
     mb = plan.tables.shape[1] << split
     # The bench is the caller: it knows the lengths and may pick the split.
     req_pt = args.partition_tokens
-    if req_pt < 0:
+    if req_pt == AUTO:
         from block_table_attention_amd.blocks import suggest_partition_tokens
-        req_pt = suggest_partition_tokens(plan.seq_lens, Hkv)
+        req_pt = suggest_partition_tokens(plan.seq_lens, Hkv, balanced_ok=sh.dtype == "bf16")
     if host_plan is None:
         pt, n_parts = pba.paged_decode_plan(dpool, Hq, B, mb, req_pt)
         ws_bytes = pba.paged_decode_workspace_bytes(dpool, Hq, B, mb, req_pt)
@@ -427,7 +441,7 @@ def run_workload(args, name, pba, torch, dev):
 
     kv_unique, kv_logical, alg_bytes = decode_bytes(plan, sh)
     traffic = (profiled_traffic(name if host_plan is None else f"shared_{name}")
-               if args.partition_tokens < 0 and args.shared_partition_tokens == 1024
+               if args.partition_tokens == AUTO and args.shared_partition_tokens == 1024
                and args.shared_tiles == 2 and args.tables == "dense"
                and args.kernel_block == 0 else None)
     step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
@@ -457,7 +471,9 @@ def run_workload(args, name, pba, torch, dev):
                    "partition_tokens": pt, "num_partitions": n_parts,
                    "partition_choice": "shared-prefix plan" if host_plan is not None else
                    ("library plan" if req_pt == 0 else
-                    ("caller (suggest_partition_tokens)" if args.partition_tokens < 0 else "fixed")),
+                    ("balanced" if req_pt == BALANCED else
+                     ("caller (suggest_partition_tokens)" if args.partition_tokens == AUTO
+                      else "fixed"))),
                    "decode_path": path,
                    "tables": "ragged" if row_offsets is not None else "dense",
                    "table_cells": table_cells,
@@ -616,7 +632,7 @@ def run_bundle(args, name, pba, torch, dev):
     layer_pools = [(g, grp.layer(l)) for g, grp in enumerate(groups) for l in range(grp.num_layers)]
     scale = 1.0 / math.sqrt(d)
     req_pt = args.partition_tokens
-    if req_pt < 0:
+    if req_pt == AUTO:
         from block_table_attention_amd.blocks import suggest_partition_tokens
         req_pt = suggest_partition_tokens(plan.seq_lens, Hkv)
     mbs = [t.shape[1] for t in plan.tables]
@@ -717,7 +733,7 @@ def run_bundle(args, name, pba, torch, dev):
                                                       for T in lens)) * 4 for g in range(G)]
     alg_avg = sum(alg_layer[g] * w.groups[g].layers for g in range(G)) / w.total_layers
     achieved = alg_avg / (dec_avg_ms * 1e-3) / 1e9
-    traffic = profiled_traffic(name) if args.partition_tokens < 0 else None
+    traffic = profiled_traffic(name) if args.partition_tokens == AUTO else None
     step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
     n_copy = [int(s.numel()) for s in csrc]
     bundle_bytes = sum(gs.layers * Hkv * gs.block_size * d * 2 * 2 for gs in w.groups)
@@ -824,7 +840,7 @@ def run_contiguous(args, name, pba, torch, dev):
     slot_index = torch.arange(B, dtype=torch.int32, device=dev)
     lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
     req_pt = args.partition_tokens
-    if req_pt < 0:
+    if req_pt == AUTO:
         from block_table_attention_amd.blocks import suggest_partition_tokens
         req_pt = suggest_partition_tokens(lens, Hkv)
     pt, n_parts = pba.paged_decode_plan(pool, Hq, B, bps, req_pt)
@@ -867,7 +883,7 @@ def run_contiguous(args, name, pba, torch, dev):
     print(f"[bench] {name} {args.kv}: {ms_per_step * 1e3:.1f} us/step, decode burst "
           f"{dec_avg_ms * 1e3:.1f} us/launch; mapped {bundles} page bundles in "
           f"{map_s * 1e3:.1f} ms", file=sys.stderr, flush=True)
-    traffic = profiled_traffic(f"contig_{name}") if virtual and args.partition_tokens < 0 and \
+    traffic = profiled_traffic(f"contig_{name}") if virtual and args.partition_tokens == AUTO and \
         args.page_mib == 2.0 else None
     result = {
         "metric": "paged decode: KV GB/s achieved (% of HBM peak) + query rows/s at 1 GPU",

@@ -44,6 +44,7 @@ STATUS = {0: "PBA_OK", -1: "PBA_ERR_NULL_ARG", -2: "PBA_ERR_BAD_DTYPE", -3: "PBA
           -6: "PBA_ERR_OUT_OF_RANGE", -7: "PBA_ERR_OVERLAP", -8: "PBA_ERR_HIP",
           -9: "PBA_ERR_HALF_BUNDLE", -10: "PBA_ERR_OUT_OF_MEMORY"}
 MAX_GROUPS = 8
+PARTITIONS_BALANCED = -1   # partition_tokens: balance the batch's chunks over the CUs
 _DTYPES = {torch.float32: PBA_F32, torch.bfloat16: PBA_BF16}
 
 

@@ -211,18 +211,24 @@ class BundleManager:
         return self.groups[0].seq_lens(rids)
 
 
-def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 256) -> int:
-    """A partition length for ``paged_decode`` chosen from the lengths the
-    caller knows (the library sees only the table width and the batch).
+PARTITIONS_BALANCED = -1   # the library's balanced decomposition (PBA_PARTITIONS_BALANCED)
+
+
+def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 256,
+                             balanced_ok: bool = True) -> int:
+    """A partition choice for ``paged_decode`` from the lengths the caller
+    knows (the library sees only the table width and the batch).
 
     Returns 0 (the library's own plan) unless the batch already gives every
     CU a (request, kv head) of its own and its longest request is far above
-    the mean; then the long requests are cut near twice the mean length, so
-    that they stop setting the kernel's duration while the short ones keep a
-    single partition.  Measured on MI355X: a lognormal batch of 128 requests
-    (median 100, max 8192 tokens) decodes in 62 us with 1024-token partitions
-    against 102 us unsplit; uniform or mildly ragged batches are fastest
-    unsplit.
+    the mean.  Such ragged batches get the balanced decomposition
+    (``PARTITIONS_BALANCED``: the batch's chunks spread evenly over the CUs)
+    when ``balanced_ok`` (bf16 pools, at most 2048 rows), else partitions of
+    about twice the mean length.  Measured on MI355X, lognormal batches of 128
+    requests (median 100, max 8192 tokens): 61 / 67 / 65 us at P = 16 / 64 /
+    256 balanced, 61 / 77 / 76 us with 1024-token partitions, 102 / 139 / 140
+    us unsplit; uniform or mildly ragged batches are fastest with the
+    library's plan.
     """
     lens = np.asarray(seq_lens, dtype=np.int64)
     if lens.size == 0 or lens.size * num_kv_heads < num_cus:
@@ -231,6 +237,8 @@ def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus
     longest = int(lens.max())
     if longest <= 4 * mean:
         return 0
+    if balanced_ok and lens.size <= 2048:
+        return PARTITIONS_BALANCED
     pt = int(-(-int(2 * mean) // 256) * 256)
     pt = max(512, pt)
     return 0 if pt >= longest else pt

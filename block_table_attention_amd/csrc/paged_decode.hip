@@ -297,9 +297,12 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
 // the loads of the wave's next chunk tn, each issued as soon as the registers
 // it overwrites are consumed.  Tokens at or past t_end are masked out;
 // columns at or past ncols carry no probability mass.
+// `pv`, `h` and `tn_end` describe the chunk being prefetched (the same row as
+// the current chunk, except in the balanced kernel, where the next chunk may
+// belong to another (request, kv head)); t0 and t_end describe the current one.
 template <int D, bool IMPLICIT = false>
 __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, int tn, int t_end,
-                                           int ncols, float scale_log2,
+                                           int tn_end, int ncols, float scale_log2,
                                            const bf16x8 (&qf)[D / 32], u32x4 (&kf)[2][D / 32],
                                            u32x4 (&vf)[D / 16], float& m_run, float& l_run,
                                            f32x4 (&acc)[D / 16], int n, int g) {
@@ -311,7 +314,7 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
   // A second block that starts at or past the end holds no visible row: its
   // loads go to the first block instead (and are masked), so no block past
   // the row's last one is ever read.
-  if (tn + 16 >= t_end) nb1 = nb0;
+  if (tn + 16 >= tn_end) nb1 = nb0;
 
   // Scores S^T = K Q^T: lane gets tokens 8g + 4a + i (i < 4) of head n.
   f32x4 s[2];
@@ -494,7 +497,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     // requested again (in bounds, served from L2), which keeps the number of
     // loads in flight the same on every iteration.
     const int tn = it + 1 < n_w ? t0 + kWaves * CH : t0;
-    chunk_step<D, IMPLICIT>(pv, h, t0, tn, T, G, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
+    chunk_step<D, IMPLICIT>(pv, h, t0, tn, T, T, G, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n,
+                            g);
   }
 
   // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n]: four
@@ -509,6 +513,371 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(&st.o[wave][n][16 * mt + 4 * g]) = acc[mt];
   __syncthreads();
   finish_workgroup<D>(a, st, r, h, part, T);
+}
+
+// ---------------------------------------------------------------------------
+// Balanced decode: the batch's chunks spread evenly over the chip
+// ---------------------------------------------------------------------------
+// The (request, kv head) segments of the batch -- ceil(T/32) chunks each --
+// are laid end to end, request major.  With C chunks and NG work-groups (one
+// per CU), work-group w owns chunks [w C / NG, (w+1) C / NG), and its wave i
+// the i-th quarter of that range.  A wave walks its range chunk by chunk with
+// the grid kernel's software pipeline, the prefetch crossing from one segment
+// into the next (the next segment's q is requested with it), so a ragged batch
+// keeps every CU streaming until the end instead of waiting on its longest
+// rows.
+// A segment inside one wave's range is written by that wave.  A segment cut
+// by wave boundaries leaves one partial state per wave; after the loops the
+// work-group merges the pieces of each such segment that lie in its range
+// (in range order): into the rows if the segment lies inside the work-group's
+// range, otherwise into one work-group piece, which is counted with one atomic
+// per (request, kv head); the work-group that brings the count to the number
+// of work-groups over the segment merges their pieces and resets the counter.
+// Row lengths and their chunk prefix sums live in LDS (at most kFlatMaxRows
+// rows; the host keeps the chunk total below 2^31).
+constexpr int kFlatMaxRows = kFlatMaxBatch;
+
+struct FlatShared {
+  int32_t pre[kFlatMaxRows + 1];  // chunks of every segment of rows < r
+  int32_t T[kFlatMaxRows];
+  int32_t scan[kDecodeThreads];
+  int32_t pend[kWaves][2];        // segment (r * H + h) of each wave's partial pieces, or -1
+};
+
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Unit that owns chunk c when C chunks are split into NU ranges
+// [floor(i C / NU), floor((i+1) C / NU)): the largest i with floor(i C / NU) <= c.
+__device__ __forceinline__ int64_t range_owner(int64_t c, int64_t C, int64_t NU) {
+  return ((c + 1) * NU + C - 1) / C - 1;
+}
+
+// Merge n pieces (slot_of(j), j < n, in order) of G columns into (M, L, O)
+// and either write the rows or store one piece at dst_slot.  All threads of
+// the work-group take part; each owns four consecutive dims of one column.
+template <int D, typename SlotOf>
+__device__ void flat_merge(const DecodeArgs& a, const FlatArgs& f, SlotOf slot_of, int n,
+                           int64_t row0, bool to_rows, int64_t dst_slot) {
+  constexpr int C4 = D / 4;
+  const int G = a.G;
+  for (int idx = threadIdx.x; idx < G * C4; idx += kDecodeThreads) {
+    const int cn = idx / C4;
+    const int c4 = idx - cn * C4;
+    float M = -INFINITY, L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    constexpr int TILE = 8;
+    for (int j0 = 0; j0 < n; j0 += TILE) {
+      float mt[TILE], lt[TILE];
+      f32x4 ut[TILE];
+#pragma unroll
+      for (int j = 0; j < TILE; ++j) {
+        const int64_t s = slot_of(min(j0 + j, n - 1));
+        mt[j] = ld_state(f.piece_ml + (s * G + cn) * 2);
+        lt[j] = ld_state(f.piece_ml + (s * G + cn) * 2 + 1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(f.piece_u + (s * G + cn) * D + 4 * c4 + e);
+      }
+#pragma unroll
+      for (int j = 0; j < TILE; ++j) {
+        if (j0 + j >= n || mt[j] == -INFINITY) continue;
+        const float Mn = fmaxf(M, mt[j]);
+        const float sa = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+        const float sb = fast_exp2(mt[j] - Mn);
+        L = L * sa + lt[j] * sb;
+        O = O * sa + ut[j] * sb;
+        M = Mn;
+      }
+    }
+    if (to_rows) {
+      const f32x4 res = L > 0.f ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+      *reinterpret_cast<f32x4*>(a.out + (row0 + cn) * D + 4 * c4) = res;
+      if (a.lse && c4 == 0) a.lse[row0 + cn] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st_state(f.piece_u + (dst_slot * G + cn) * D + 4 * c4 + e, O[e]);
+      if (c4 == 0) {
+        st_state(f.piece_ml + (dst_slot * G + cn) * 2, M);
+        st_state(f.piece_ml + (dst_slot * G + cn) * 2 + 1, L);
+      }
+    }
+  }
+}
+
+template <int D, int MODE>
+__global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
+    const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
+    const void* __restrict__ kbase, const void* __restrict__ vbase, int32_t max_blocks,
+    int32_t log2P, int32_t last_block, int32_t k_sb, int32_t k_sh, DecodeArgs a, FlatArgs f) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int CH = 32;
+  constexpr bool IMPLICIT = MODE == kTablesContiguous;
+
+  __shared__ FlatShared sh;
+  const int B = a.batch;
+  const int H = a.num_kv_heads;
+  const int G = a.G;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int P = 1 << log2P;
+
+  // Rows and their chunk counts; prefix sums over the batch.  A row with no
+  // visible token (rejected in validate mode) has no chunk and gets out = 0,
+  // lse = -inf from work-group 0: the identity state.
+  const int per = (B + kDecodeThreads - 1) / kDecodeThreads;
+  const int rb = min(B, tid * per), re = min(B, rb + per);
+  int local = 0;
+  for (int r = rb; r < re; ++r) {
+    const int T = seq_lens[r];
+    sh.T[r] = T;
+    if (T > 0) {
+      local += H * ((T + CH - 1) / CH);
+    } else if (blockIdx.x == 0) {
+      for (int i = 0; i < a.num_q_heads; ++i) {
+        const int64_t row = (int64_t)r * a.num_q_heads + i;
+        for (int c = 0; c < D; ++c) a.out[row * D + c] = 0.f;
+        if (a.lse) a.lse[row] = -INFINITY;
+      }
+    }
+  }
+  sh.scan[tid] = local;
+  if (tid < kWaves) sh.pend[tid][0] = sh.pend[tid][1] = -1;
+  __syncthreads();
+  for (int st = 1; st < kDecodeThreads; st <<= 1) {
+    const int v = tid >= st ? sh.scan[tid - st] : 0;
+    __syncthreads();
+    sh.scan[tid] += v;
+    __syncthreads();
+  }
+  {
+    int run = sh.scan[tid] - local;
+    for (int r = rb; r < re; ++r) {
+      sh.pre[r] = run;
+      const int T = sh.T[r];
+      if (T > 0) run += H * ((T + CH - 1) / CH);
+    }
+    if (tid == 0) sh.pre[B] = sh.scan[kDecodeThreads - 1];
+  }
+  __syncthreads();
+
+  // Ranges: this work-group's, then this wave's quarter of it.
+  const int wave = uni(tid >> 6);
+  const int64_t C = uni(sh.pre[B]);
+  const int64_t NG = min((int64_t)gridDim.x, C);
+  const int64_t wg = blockIdx.x;
+  if (wg >= NG) return;
+  const int64_t gb = wg * C / NG, ge = (wg + 1) * C / NG;
+  const int64_t cb = gb + (ge - gb) * wave / kWaves;
+  const int64_t ce = gb + (ge - gb) * (wave + 1) / kWaves;
+
+  // Reads of one row's table: dense rows at r * max_blocks; ragged rows from
+  // row_offsets; contiguous rows are a slot's blocks.
+  auto view = [&](int rr, int TT) {
+    int64_t toff = (int64_t)rr * max_blocks;
+    int nb = max_blocks;
+    if constexpr (MODE == kTablesRagged) {
+      const int64_t __attribute__((address_space(4)))* ro =
+          (const int64_t __attribute__((address_space(4)))*)a.row_offsets;
+      toff = ro[rr];
+      nb = (int)(ro[rr + 1] - toff);
+    } else if constexpr (MODE == kTablesContiguous) {
+      toff = (int64_t)((const int32_t __attribute__((address_space(4)))*)tables)[rr] * max_blocks;
+    }
+    PoolView pv{(table_t*)(tables + toff),
+                static_cast<const uint16_t*>(kbase),
+                static_cast<const uint16_t*>(vbase),
+                k_sb, k_sh, a.v_sb, a.v_sh, nb, last_block, log2P, a.split_log2};
+    if constexpr (IMPLICIT) {
+      pv.trow = nullptr;
+      pv.base_block = toff;
+      pv.max_blocks = max(1, (TT + P - 1) >> log2P);
+    }
+    return pv;
+  };
+  const uint16_t* qbase = static_cast<const uint16_t*>(a.q);
+  auto load_q = [&](u32x4 (&qr)[KK], int rr, int hh) {
+    const uint16_t* qrow =
+        qbase + ((int64_t)rr * a.num_q_heads + (int64_t)hh * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qr[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
+  };
+
+  if (cb < ce) {
+    // Segment cursor at cb: row r (the largest with pre[r] <= cb), head h, chunk k.
+    int r;
+    {
+      int lo = 0, hi = B - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (uni(sh.pre[mid]) <= cb) lo = mid; else hi = mid - 1;
+      }
+      r = uni(lo);
+    }
+    int T = uni(sh.T[r]);
+    int nch = (T + CH - 1) / CH;
+    const int off0 = (int)(cb - uni(sh.pre[r]));
+    int h = off0 / nch;
+    int k = off0 - h * nch;
+
+    PoolView pv = view(r, T);
+    u32x4 qraw[KK];
+    u32x4 kf[2][KK];
+    u32x4 vf[MT];
+    {
+      load_q(qraw, r, h);
+      int64_t pb0, pb1;
+      const int t0 = k * CH;
+      chunk_blocks<IMPLICIT>(pv, t0, pb0, pb1);
+      if (t0 + 16 >= T) pb1 = pb0;
+      __builtin_amdgcn_sched_barrier(0);
+      load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    bf16x8 qf[KK];
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[kk] = __builtin_bit_cast(bf16x8, n < G ? qraw[kk] : u32x4{0u, 0u, 0u, 0u});
+
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+    f32x4 acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool first_seg = true;
+    int k_first = k;  // first chunk of this wave's piece of the current segment
+    const int64_t wid = wg * kWaves + wave;
+
+    for (int64_t c = cb; c < ce; ++c) {
+      const bool last = c + 1 == ce;
+      const bool seg_end = last || k + 1 == nch;
+      const bool new_seg = !last && k + 1 == nch;
+      int r2 = r, h2 = h, k2 = k, T2 = T, nch2 = nch;
+      if (!last) {
+        if (k + 1 < nch) {
+          k2 = k + 1;
+        } else {
+          k2 = 0;
+          if (h + 1 < H) {
+            h2 = h + 1;
+          } else {
+            h2 = 0;
+            do {
+              ++r2;
+              T2 = uni(sh.T[r2]);
+            } while (T2 <= 0);
+            nch2 = (T2 + CH - 1) / CH;
+          }
+        }
+      }
+      const PoolView pvn = r2 == r ? pv : view(r2, T2);
+      u32x4 qnext[KK];
+      if (new_seg) load_q(qnext, r2, h2);
+      chunk_step<D, IMPLICIT>(pvn, h2, k * CH, k2 * CH, T, T2, G, a.scale_log2, qf, kf, vf,
+                              m_run, l_run, acc, n, g);
+      if (seg_end) {
+        float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+        l_tot += __shfl_xor(l_tot, 32, 64);
+        if (k_first == 0 && k + 1 == nch) {
+          // The whole segment is this wave's: write the rows.
+          const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
+          if (n < G) {
+            const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              *reinterpret_cast<f32x4*>(a.out + row * D + 16 * mt + 4 * g) = acc[mt] * inv;
+            if (a.lse && g == 0)
+              a.lse[row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+          }
+        } else {
+          const int64_t slot = wid * 2 + (first_seg ? 0 : 1);
+          if (n < G) {
+            float* u = f.piece_u + (slot * G + n) * D;
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) st_state(u + 16 * mt + 4 * g + i, acc[mt][i]);
+            if (g == 0) {
+              st_state(f.piece_ml + (slot * G + n) * 2, m_run);
+              st_state(f.piece_ml + (slot * G + n) * 2 + 1, l_tot);
+            }
+          }
+          if (lane == 0) sh.pend[wave][first_seg ? 0 : 1] = r * H + h;
+        }
+        m_run = -INFINITY;
+        l_run = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        first_seg = false;
+        k_first = 0;
+      }
+      if (new_seg) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk)
+          qf[kk] = __builtin_bit_cast(bf16x8, n < G ? qnext[kk] : u32x4{0u, 0u, 0u, 0u});
+      }
+      if (r2 != r) pv = pvn;
+      r = r2;
+      h = h2;
+      k = k2;
+      T = T2;
+      nch = nch2;
+    }
+  }
+  // Pieces: every wave's stores complete, then the work-group merges.
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  __shared__ int s_last;
+  // Distinct segments among the waves' pieces, in range order.
+  for (int qi = 0; qi < 2 * kWaves; ++qi) {
+    const int seg = uni(sh.pend[qi >> 1][qi & 1]);
+    if (seg < 0) continue;
+    // Only the first occurrence of a segment in range order handles it.
+    bool seen = false;
+    for (int qj = 0; qj < qi; ++qj) seen |= uni(sh.pend[qj >> 1][qj & 1]) == seg;
+    if (seen) continue;
+    const int pr = seg / H, ph = seg - pr * H;
+    const int pT = uni(sh.T[pr]);
+    const int pn = (pT + CH - 1) / CH;
+    const int64_t s0 = (int64_t)uni(sh.pre[pr]) + (int64_t)ph * pn;  // segment's first chunk
+    const int64_t s1 = s0 + pn;
+    // This work-group's wave pieces of the segment, in order: wave slot
+    // (wg * kWaves + w) * 2 + which, packed as 3-bit local indices 2w + which.
+    uint32_t packed = 0;
+    int np = 0;
+    for (int q2 = 0; q2 < 2 * kWaves; ++q2)
+      if (uni(sh.pend[q2 >> 1][q2 & 1]) == seg) packed |= (uint32_t)q2 << (3 * np++);
+    auto wave_slot = [&](int j) { return wg * 2 * kWaves + ((packed >> (3 * j)) & 7); };
+    const int64_t row0 = (int64_t)pr * a.num_q_heads + (int64_t)ph * G;
+    if (s0 >= gb && s1 <= ge) {  // inside this work-group's range: write the rows
+      flat_merge<D>(a, f, wave_slot, np, row0, true, 0);
+      continue;
+    }
+    // One work-group piece, then the count over the work-groups of the segment.
+    // Slot 0: the segment began before this range; slot 1: it ends after it.
+    const int64_t wslot = f.wg_slot0 + wg * 2 + (s0 < gb ? 0 : 1);
+    flat_merge<D>(a, f, wave_slot, np, row0, false, wslot);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+    const int64_t w0 = range_owner(s0, C, NG), w1 = range_owner(s1 - 1, C, NG);
+    const int nwg = (int)(w1 - w0 + 1);
+    int32_t* counter = a.counters + (int64_t)pr * H + ph;
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               nwg - 1;
+    __syncthreads();
+    if (!s_last) continue;
+    // Work-group w0 holds the segment's start (its slot 1); the others hold
+    // segments that began before their ranges (slot 0).
+    auto wg_slot = [&](int j) { return f.wg_slot0 + (w0 + j) * 2 + (j == 0 ? 1 : 0); };
+    flat_merge<D>(a, f, wg_slot, nwg, row0, true, 0);
+    if (tid == 0) *counter = 0;  // ready for the next call on this workspace
+    __syncthreads();
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -645,7 +1014,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int it = 0; it < n_w; ++it, t0 += stride) {
     const int tn = it + 1 < n_w ? t0 + stride : t0;
-    chunk_step<D>(pv, h, t0, tn, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
+    chunk_step<D>(pv, h, t0, tn, te, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
   }
 
   l_run += __shfl_xor(l_run, 16, 64);
@@ -905,6 +1274,26 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
+}
+
+hipError_t launch_paged_decode_flat(const DecodeArgs& a, const FlatArgs& f, int head_dim,
+                                    int n_wg, hipStream_t stream) {
+  const dim3 grid((unsigned)n_wg), block(kDecodeThreads);
+#define PBA_FLAT(DD, MM)                                                                         \
+  hipLaunchKernelGGL((decode_bf16_flat_kernel<DD, MM>), grid, block, 0, stream, a.tables,       \
+                     a.seq_lens, a.k, a.v, a.max_blocks, a.log2P, a.num_blocks - 1,            \
+                     (int32_t)a.k_sb, (int32_t)a.k_sh, a, f)
+  if (head_dim == 128) {
+    if (a.table_mode == kTablesRagged) PBA_FLAT(128, kTablesRagged);
+    else if (a.table_mode == kTablesContiguous) PBA_FLAT(128, kTablesContiguous);
+    else PBA_FLAT(128, kTablesDense);
+  } else {
+    if (a.table_mode == kTablesRagged) PBA_FLAT(64, kTablesRagged);
+    else if (a.table_mode == kTablesContiguous) PBA_FLAT(64, kTablesContiguous);
+    else PBA_FLAT(64, kTablesDense);
+  }
+#undef PBA_FLAT
+  return hipGetLastError();
 }
 
 hipError_t launch_paged_decode_shared(const DecodeArgs& a, const SharedArgs& sa, int head_dim,

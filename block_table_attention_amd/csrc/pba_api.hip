@@ -200,6 +200,42 @@ WsLayout workspace_layout(int32_t batch, int32_t kv_heads, int64_t rows, int32_t
   return w;
 }
 
+// The balanced decode (one 4-wave work-group per CU, the batch's chunks split
+// evenly over the waves) serves partition_tokens == PBA_PARTITIONS_BALANCED
+// for bf16 batches of at most kFlatMaxBatch rows; everything else uses the
+// grid of (kv head, request, partition).
+bool use_flat(const pba_kv_pool* pool, int32_t batch, int32_t partition_tokens,
+              int32_t max_blocks_per_seq) {
+  // Chunk counts are int32 in the kernel: B * H_kv * ceil(max T / 32) < 2^31.
+  const int64_t max_T = (int64_t)max_blocks_per_seq * pool->block_size;
+  const int64_t chunks = (int64_t)batch * pool->num_kv_heads * ((max_T + 31) / 32);
+  return partition_tokens == PBA_PARTITIONS_BALANCED && pool->dtype == PBA_BF16 && batch >= 1 &&
+         batch <= pba::kFlatMaxBatch && chunks < INT32_MAX;
+}
+
+// A balanced request that the balanced decode cannot serve falls back to the
+// library's own partition plan.
+int32_t grid_request(int32_t partition_tokens) {
+  return partition_tokens == PBA_PARTITIONS_BALANCED ? 0 : partition_tokens;
+}
+
+int flat_workgroups() { return device_cu_count(); }
+
+// Balanced-decode workspace: [counters int32 B*H_kv | pad][piece (m, l) |
+// pad][piece u], two piece slots per wave then two per work-group, G columns
+// each.
+int64_t flat_slots() { return 2 * (int64_t)flat_workgroups() * (pba::kDecodeThreads / 64 + 1); }
+
+WsLayout flat_layout(int32_t batch, int32_t kv_heads, int32_t G, int head_dim) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t pieces = (size_t)flat_slots() * G;
+  WsLayout w;
+  w.ml_off = up((size_t)batch * kv_heads * sizeof(int32_t));
+  w.u_off = w.ml_off + up(pieces * 2 * sizeof(float));
+  w.bytes = w.u_off + pieces * head_dim * sizeof(float);
+  return w;
+}
+
 template <typename T>
 bool copy_to_host(std::vector<T>& dst, const T* src, int64_t n, hipStream_t stream) {
   dst.resize((size_t)n);
@@ -468,8 +504,13 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
   int32_t pt = 0, np = 0;
-  st = plan_partitions(pool, batch > 0 ? batch : 1, max_blocks_per_seq, partition_tokens, &pt, &np);
-  if (st) return st;
+  if (use_flat(pool, batch, partition_tokens, max_blocks_per_seq)) {
+    np = flat_workgroups() * pba::kDecodeThreads / 64;  // waves the batch is spread over
+  } else {
+    st = plan_partitions(pool, batch > 0 ? batch : 1, max_blocks_per_seq,
+                         grid_request(partition_tokens), &pt, &np);
+    if (st) return st;
+  }
   if (partition_tokens_out) *partition_tokens_out = pt;
   if (num_partitions_out) *num_partitions_out = np;
   return PBA_OK;
@@ -482,6 +523,9 @@ size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_h
   if (pba_paged_decode_plan(pool, num_q_heads, batch, max_blocks_per_seq, partition_tokens, &pt,
                             &np))
     return 0;
+  if (use_flat(pool, batch, partition_tokens, max_blocks_per_seq))
+    return flat_layout(batch, pool->num_kv_heads, num_q_heads / pool->num_kv_heads,
+                       pool->head_dim).bytes;
   return workspace_layout(batch, pool->num_kv_heads, (int64_t)batch * num_q_heads, np,
                           pool->head_dim).bytes;
 }
@@ -502,12 +546,17 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
   if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
+  const bool flat = use_flat(pool, batch, partition_tokens, max_blocks_per_seq);
   int32_t pt = 0, np = 0;
-  st = plan_partitions(pool, batch, max_blocks_per_seq, partition_tokens, &pt, &np);
-  if (st) return st;
+  if (!flat) {
+    st = plan_partitions(pool, batch, max_blocks_per_seq, grid_request(partition_tokens), &pt,
+                         &np);
+    if (st) return st;
+  }
   const int64_t rows = (int64_t)batch * num_q_heads;
   if (rows > INT32_MAX) return PBA_ERR_UNSUPPORTED;
-  const WsLayout ws = workspace_layout(batch, pool->num_kv_heads, rows, np, pool->head_dim);
+  const WsLayout ws = flat ? flat_layout(batch, pool->num_kv_heads, G, pool->head_dim)
+                           : workspace_layout(batch, pool->num_kv_heads, rows, np, pool->head_dim);
   const size_t need = ws.bytes;
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return PBA_ERR_WORKSPACE_TOO_SMALL;
@@ -579,6 +628,15 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
   a.part_tokens = pt;
   a.n_parts = np;
   a.scale_log2 = scale * 1.4426950408889634f;
+  if (flat) {
+    pba::FlatArgs f;
+    f.piece_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
+    f.piece_u = reinterpret_cast<float*>(wsb + ws.u_off);
+    f.wg_slot0 = 2 * (int64_t)flat_workgroups() * (pba::kDecodeThreads / 64);
+    return pba::launch_paged_decode_flat(a, f, pool->head_dim, flat_workgroups(), s) == hipSuccess
+               ? PBA_OK
+               : PBA_ERR_HIP;
+  }
   return pba::launch_paged_decode(a, pool->dtype, pool->head_dim, s) == hipSuccess ? PBA_OK
                                                                                   : PBA_ERR_HIP;
 }

@@ -78,6 +78,17 @@ struct SharedArgs {
   int32_t nz_items;  // grid z planes of chunk-first items: ceil(n_items / batch)
 };
 
+// Balanced decode: partial states of segments cut by range boundaries, two
+// slots per wave followed by two per work-group ([slots][G][2], [slots][G][D]).
+struct FlatArgs {
+  float* piece_ml;
+  float* piece_u;
+  int64_t wg_slot0;  // first work-group slot: 2 * waves
+};
+constexpr int kFlatMaxBatch = 2048;  // rows the balanced decode takes (LDS prefix sums)
+
+hipError_t launch_paged_decode_flat(const DecodeArgs& a, const FlatArgs& f, int head_dim,
+                                    int n_wg, hipStream_t stream);
 hipError_t launch_expand_tables(const int32_t* src, int64_t n_src, int split_log2, int32_t* dst,
                                 hipStream_t stream);
 hipError_t launch_pack_tables(const int32_t* src, int32_t batch, int32_t width,

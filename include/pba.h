@@ -55,6 +55,10 @@ typedef enum pba_status {
 
 typedef enum pba_dtype { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
 
+/* partition_tokens value of the decode calls: balance the batch's work over
+ * the CUs instead of cutting rows into equal partitions. */
+#define PBA_PARTITIONS_BALANCED (-1)
+
 /*
  * The K/V pool of one layer (one cache group): a fixed set of physical blocks
  * of P token rows each.  Element (block b, kv head h, in-block token o, dim c):
@@ -236,9 +240,14 @@ int pba_block_copy_bundle(const pba_kv_group* groups, int32_t num_groups,
  *   lse           device float32 [batch, num_q_heads], or NULL
  *   partition_tokens  0: the library splits each row into partitions of its
  *                 choice (sized so that all work-groups are resident at once);
- *                 otherwise the partition length in tokens, a positive
- *                 multiple of 256.  Partitions are reduced by the log-sum-exp
- *                 merge; an empty partition is the identity.
+ *                 PBA_PARTITIONS_BALANCED: the batch's 32-token chunks, laid
+ *                 end to end, are split evenly over one work-group per CU,
+ *                 whatever the row lengths (bf16 batches of at most 2048 rows;
+ *                 otherwise as 0) -- for ragged batches, where equal
+ *                 partitions leave most work-groups empty; otherwise the
+ *                 partition length in tokens, a positive multiple of 256.
+ *                 Partitions are reduced by the log-sum-exp merge; an empty
+ *                 partition is the identity.
  *   workspace     device scratch of at least
  *                 pba_paged_decode_workspace_bytes(...) bytes, 16-byte aligned
  *                 (NULL allowed when that is 0).  Its first 4 * batch *

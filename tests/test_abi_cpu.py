@@ -145,10 +145,28 @@ def test_workspace_and_plan():
     assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, 1, 129, 512, ctypes.byref(pt), ctypes.byref(npart)) == 0
     assert npart.value == 5
     # Automatic plans: partitions are multiples of 256 and cover the table.
-    for B, mb in [(1, 1), (8, 256), (32, 129), (1, 4096), (128, 512)]:
-        assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, B, mb, 0, ctypes.byref(pt), ctypes.byref(npart)) == 0
+    # PBA_PARTITIONS_BALANCED falls back to them where the balanced decode
+    # does not apply (fp32 pools, batches over 2048 rows).
+    f32 = _desc(dtype=0)
+    for desc, B, mb, req in [(d, 1, 1, 0), (d, 8, 256, 0), (d, 32, 129, 0), (d, 1, 4096, 0),
+                             (d, 128, 512, 0), (f32, 8, 256, -1), (d, 4096, 8, -1)]:
+        assert lib.pba_paged_decode_plan(ctypes.byref(desc), 8, B, mb, req, ctypes.byref(pt),
+                                         ctypes.byref(npart)) == 0
         assert pt.value % 128 == 0 and pt.value * npart.value >= mb * 16
         assert pt.value * (npart.value - 1) < mb * 16
+    # The balanced decode: one 4-wave work-group per CU (256 CUs when no device
+    # is visible); workspace = counters + two piece states per wave and two per
+    # work-group.
+    for B, mb in [(1, 1), (8, 256), (2048, 4)]:
+        assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, B, mb, -1, ctypes.byref(pt),
+                                         ctypes.byref(npart)) == 0
+        waves = npart.value
+        assert pt.value == 0 and waves % 4 == 0 and waves >= 4
+        G, slots = 4, 2 * waves + 2 * (waves // 4)
+        expect = up(B * 2 * 4) + up(slots * G * 2 * 4) + slots * G * 128 * 4
+        assert lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, B, mb, -1) == expect
+    assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, 2, 64, -2, ctypes.byref(pt),
+                                     ctypes.byref(npart)) == -3
     assert lib.pba_status_string(-5).decode().startswith("workspace")
     assert pba.STATUS[-6] == "PBA_ERR_OUT_OF_RANGE"
 

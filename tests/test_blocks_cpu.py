@@ -215,3 +215,16 @@ def test_bundle_manager_all_or_nothing():
         m.append(r, 1)
     assert ([list(g._free) for g in m.groups], [g.table(r) for g in m.groups]) == state
     assert m.length(r) == 32
+
+
+def test_partition_suggestion():
+    from block_table_attention_amd.blocks import PARTITIONS_BALANCED, suggest_partition_tokens
+
+    uniform = [16384] * 8
+    assert suggest_partition_tokens(uniform, 8) == 0                 # 64 units < 256 CUs
+    assert suggest_partition_tokens([1000] * 64, 8) == 0             # not ragged
+    ragged = [100] * 127 + [8192]
+    assert suggest_partition_tokens(ragged, 8) == PARTITIONS_BALANCED
+    pt = suggest_partition_tokens(ragged, 8, balanced_ok=False)
+    assert pt % 256 == 0 and 512 <= pt < 8192
+    assert suggest_partition_tokens([100] * 4000 + [8192], 8) > 0    # too many rows to balance
