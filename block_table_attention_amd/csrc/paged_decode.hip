@@ -546,59 +546,48 @@ struct FlatShared {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Unit that owns chunk c when C chunks are split into NU ranges
-// [floor(i C / NU), floor((i+1) C / NU)): the largest i with floor(i C / NU) <= c.
-__device__ __forceinline__ int64_t range_owner(int64_t c, int64_t C, int64_t NU) {
-  return ((c + 1) * NU + C - 1) / C - 1;
-}
-
-// Merge n pieces (slot_of(j), j < n, in order) of G columns into (M, L, O)
-// and either write the rows or store one piece at dst_slot.  All threads of
-// the work-group take part; each owns four consecutive dims of one column.
+// Merge n pieces (slot_of(j), j < n, in order) of column cn, dims 4 c4 ..
+// 4 c4 + 3, into (M, L, O) and write the rows, or store one piece at
+// dst_slot.  The loads of a tile of pieces are all issued before any is used.
 template <int D, typename SlotOf>
-__device__ void flat_merge(const DecodeArgs& a, const FlatArgs& f, SlotOf slot_of, int n,
-                           int64_t row0, bool to_rows, int64_t dst_slot) {
-  constexpr int C4 = D / 4;
+__device__ void flat_merge_item(const DecodeArgs& a, const FlatArgs& f, SlotOf slot_of, int n,
+                                int64_t row0, int cn, int c4, bool to_rows, int64_t dst_slot) {
   const int G = a.G;
-  for (int idx = threadIdx.x; idx < G * C4; idx += kDecodeThreads) {
-    const int cn = idx / C4;
-    const int c4 = idx - cn * C4;
-    float M = -INFINITY, L = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    constexpr int TILE = 8;
-    for (int j0 = 0; j0 < n; j0 += TILE) {
-      float mt[TILE], lt[TILE];
-      f32x4 ut[TILE];
+  float M = -INFINITY, L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  constexpr int TILE = 8;
+  for (int j0 = 0; j0 < n; j0 += TILE) {
+    float mt[TILE], lt[TILE];
+    f32x4 ut[TILE];
 #pragma unroll
-      for (int j = 0; j < TILE; ++j) {
-        const int64_t s = slot_of(min(j0 + j, n - 1));
-        mt[j] = ld_state(f.piece_ml + (s * G + cn) * 2);
-        lt[j] = ld_state(f.piece_ml + (s * G + cn) * 2 + 1);
+    for (int j = 0; j < TILE; ++j) {
+      const int64_t s = slot_of(min(j0 + j, n - 1));
+      mt[j] = ld_state(f.piece_ml + (s * G + cn) * 2);
+      lt[j] = ld_state(f.piece_ml + (s * G + cn) * 2 + 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(f.piece_u + (s * G + cn) * D + 4 * c4 + e);
-      }
-#pragma unroll
-      for (int j = 0; j < TILE; ++j) {
-        if (j0 + j >= n || mt[j] == -INFINITY) continue;
-        const float Mn = fmaxf(M, mt[j]);
-        const float sa = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
-        const float sb = fast_exp2(mt[j] - Mn);
-        L = L * sa + lt[j] * sb;
-        O = O * sa + ut[j] * sb;
-        M = Mn;
-      }
+      for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(f.piece_u + (s * G + cn) * D + 4 * c4 + e);
     }
-    if (to_rows) {
-      const f32x4 res = L > 0.f ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-      *reinterpret_cast<f32x4*>(a.out + (row0 + cn) * D + 4 * c4) = res;
-      if (a.lse && c4 == 0) a.lse[row0 + cn] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) st_state(f.piece_u + (dst_slot * G + cn) * D + 4 * c4 + e, O[e]);
-      if (c4 == 0) {
-        st_state(f.piece_ml + (dst_slot * G + cn) * 2, M);
-        st_state(f.piece_ml + (dst_slot * G + cn) * 2 + 1, L);
-      }
+    for (int j = 0; j < TILE; ++j) {
+      if (j0 + j >= n || mt[j] == -INFINITY) continue;
+      const float Mn = fmaxf(M, mt[j]);
+      const float sa = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+      const float sb = fast_exp2(mt[j] - Mn);
+      L = L * sa + lt[j] * sb;
+      O = O * sa + ut[j] * sb;
+      M = Mn;
+    }
+  }
+  if (to_rows) {
+    const f32x4 res = L > 0.f ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(a.out + (row0 + cn) * D + 4 * c4) = res;
+    if (a.lse && c4 == 0) a.lse[row0 + cn] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_state(f.piece_u + (dst_slot * G + cn) * D + 4 * c4 + e, O[e]);
+    if (c4 == 0) {
+      st_state(f.piece_ml + (dst_slot * G + cn) * 2, M);
+      st_state(f.piece_ml + (dst_slot * G + cn) * 2 + 1, L);
     }
   }
 }
@@ -672,6 +661,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   const int64_t gb = wg * C / NG, ge = (wg + 1) * C / NG;
   const int64_t cb = gb + (ge - gb) * wave / kWaves;
   const int64_t ce = gb + (ge - gb) * (wave + 1) / kWaves;
+  // Work-group owning chunk c: the largest w with floor(w C / NG) <= c.
+  auto wg_owner = [&](int64_t c) -> int64_t { return ((c + 1) * NG + C - 1) / C - 1; };
 
   // Reads of one row's table: dense rows at r * max_blocks; ragged rows from
   // row_offsets; contiguous rows are a slot's blocks.
@@ -828,55 +819,105 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       nch = nch2;
     }
   }
-  // Pieces: every wave's stores complete, then the work-group merges.
+  // Pieces: every wave's stores complete, then the work-group merges.  All
+  // cut segments of the range go through each step together: (1) merge each
+  // segment's wave pieces -- into the rows if it lies inside this range, else
+  // into one work-group piece; (2) count the work-group pieces; (3) the last
+  // work-group of a segment merges its work-group pieces into the rows.
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
-  __shared__ int s_last;
-  // Distinct segments among the waves' pieces, in range order.
-  for (int qi = 0; qi < 2 * kWaves; ++qi) {
-    const int seg = uni(sh.pend[qi >> 1][qi & 1]);
-    if (seg < 0) continue;
-    // Only the first occurrence of a segment in range order handles it.
-    bool seen = false;
-    for (int qj = 0; qj < qi; ++qj) seen |= uni(sh.pend[qj >> 1][qj & 1]) == seg;
-    if (seen) continue;
-    const int pr = seg / H, ph = seg - pr * H;
-    const int pT = uni(sh.T[pr]);
-    const int pn = (pT + CH - 1) / CH;
-    const int64_t s0 = (int64_t)uni(sh.pre[pr]) + (int64_t)ph * pn;  // segment's first chunk
-    const int64_t s1 = s0 + pn;
-    // This work-group's wave pieces of the segment, in order: wave slot
-    // (wg * kWaves + w) * 2 + which, packed as 3-bit local indices 2w + which.
-    uint32_t packed = 0;
-    int np = 0;
-    for (int q2 = 0; q2 < 2 * kWaves; ++q2)
-      if (uni(sh.pend[q2 >> 1][q2 & 1]) == seg) packed |= (uint32_t)q2 << (3 * np++);
+  __shared__ int s_seg[2 * kWaves];
+  __shared__ uint32_t s_packed[2 * kWaves];  // wave pieces: 3-bit local slots 2w + which
+  __shared__ int s_np[2 * kWaves];
+  __shared__ int s_last[2 * kWaves];
+  __shared__ int64_t s_w0[2 * kWaves];
+  __shared__ int s_nseg;
+  if (tid == 0) {
+    int ns = 0;
+    for (int qi = 0; qi < 2 * kWaves; ++qi) {
+      const int seg = sh.pend[qi >> 1][qi & 1];
+      if (seg < 0) continue;
+      int at = 0;
+      while (at < ns && s_seg[at] != seg) ++at;
+      if (at == ns) {
+        s_seg[ns] = seg;
+        s_packed[ns] = 0;
+        s_np[ns] = 0;
+        ++ns;
+      }
+      s_packed[at] |= (uint32_t)qi << (3 * s_np[at]);
+      ++s_np[at];
+    }
+    s_nseg = ns;
+  }
+  __syncthreads();
+  const int nseg = uni(s_nseg);
+  if (nseg == 0) return;
+  constexpr int C4 = D / 4;
+  const int items = G * C4;
+  // A segment's rows, its first chunk and the work-groups over it.
+  auto seg_info = [&](int si, int& pr, int& ph, int64_t& s0, int64_t& s1) {
+    const int seg = s_seg[si];
+    pr = seg / H;
+    ph = seg - pr * H;
+    const int pn = (sh.T[pr] + CH - 1) / CH;
+    s0 = (int64_t)sh.pre[pr] + (int64_t)ph * pn;
+    s1 = s0 + pn;
+  };
+  for (int idx = tid; idx < nseg * items; idx += kDecodeThreads) {
+    const int si = idx / items;
+    const int cn = (idx - si * items) / C4;
+    const int c4 = idx - si * items - cn * C4;
+    int pr, ph;
+    int64_t s0, s1;
+    seg_info(si, pr, ph, s0, s1);
+    const uint32_t packed = s_packed[si];
     auto wave_slot = [&](int j) { return wg * 2 * kWaves + ((packed >> (3 * j)) & 7); };
     const int64_t row0 = (int64_t)pr * a.num_q_heads + (int64_t)ph * G;
-    if (s0 >= gb && s1 <= ge) {  // inside this work-group's range: write the rows
-      flat_merge<D>(a, f, wave_slot, np, row0, true, 0);
-      continue;
-    }
-    // One work-group piece, then the count over the work-groups of the segment.
-    // Slot 0: the segment began before this range; slot 1: it ends after it.
+    const bool inside = s0 >= gb && s1 <= ge;
+    // Work-group slot 0: the segment began before this range; 1: it ends after it.
     const int64_t wslot = f.wg_slot0 + wg * 2 + (s0 < gb ? 0 : 1);
-    flat_merge<D>(a, f, wave_slot, np, row0, false, wslot);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    const int64_t w0 = range_owner(s0, C, NG), w1 = range_owner(s1 - 1, C, NG);
-    const int nwg = (int)(w1 - w0 + 1);
-    int32_t* counter = a.counters + (int64_t)pr * H + ph;
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               nwg - 1;
-    __syncthreads();
-    if (!s_last) continue;
+    flat_merge_item<D>(a, f, wave_slot, s_np[si], row0, cn, c4, inside, wslot);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  if (tid < nseg) {
+    int pr, ph;
+    int64_t s0, s1;
+    seg_info(tid, pr, ph, s0, s1);
+    int last = 0;
+    if (!(s0 >= gb && s1 <= ge)) {
+      const int64_t w0 = wg_owner(s0);
+      const int nwg = (int)(wg_owner(s1 - 1) - w0 + 1);
+      last = __hip_atomic_fetch_add(a.counters + (int64_t)pr * H + ph, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == nwg - 1
+                 ? nwg
+                 : 0;
+      s_w0[tid] = w0;
+    }
+    s_last[tid] = last;  // the number of work-group pieces when this one merges
+  }
+  __syncthreads();
+  for (int idx = tid; idx < nseg * items; idx += kDecodeThreads) {
+    const int si = idx / items;
+    if (!s_last[si]) continue;
+    const int cn = (idx - si * items) / C4;
+    const int c4 = idx - si * items - cn * C4;
+    int pr, ph;
+    int64_t s0, s1;
+    seg_info(si, pr, ph, s0, s1);
+    const int64_t w0 = s_w0[si];
     // Work-group w0 holds the segment's start (its slot 1); the others hold
     // segments that began before their ranges (slot 0).
     auto wg_slot = [&](int j) { return f.wg_slot0 + (w0 + j) * 2 + (j == 0 ? 1 : 0); };
-    flat_merge<D>(a, f, wg_slot, nwg, row0, true, 0);
-    if (tid == 0) *counter = 0;  // ready for the next call on this workspace
-    __syncthreads();
+    const int64_t row0 = (int64_t)pr * a.num_q_heads + (int64_t)ph * G;
+    flat_merge_item<D>(a, f, wg_slot, s_last[si], row0, cn, c4, true, 0);
+  }
+  if (tid < nseg && s_last[tid]) {
+    int pr, ph;
+    int64_t s0, s1;
+    seg_info(tid, pr, ph, s0, s1);
+    a.counters[(int64_t)pr * H + ph] = 0;  // ready for the next call on this workspace
   }
 }
 

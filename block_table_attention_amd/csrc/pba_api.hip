@@ -219,7 +219,7 @@ int32_t grid_request(int32_t partition_tokens) {
   return partition_tokens == PBA_PARTITIONS_BALANCED ? 0 : partition_tokens;
 }
 
-int flat_workgroups() { return device_cu_count(); }
+int flat_workgroups() { return device_cu_count(); }  // one work-group per CU
 
 // Balanced-decode workspace: [counters int32 B*H_kv | pad][piece (m, l) |
 // pad][piece u], two piece slots per wave then two per work-group, G columns
