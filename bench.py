@@ -352,8 +352,11 @@ def run_workload(args, name, pba, torch, dev):
         req_pt = suggest_partition_tokens(plan.seq_lens, Hkv, balanced_ok=sh.dtype == "bf16")
     if host_plan is None:
         pt, n_parts = pba.paged_decode_plan(dpool, Hq, B, mb, req_pt)
+        # The balanced path reports no partition size, only its wave count.
+        flat = req_pt == BALANCED and pt == 0
         ws_bytes = pba.paged_decode_workspace_bytes(dpool, Hq, B, mb, req_pt)
     else:
+        flat = False
         splan = pba.SharedPlan.from_host(host_plan, dev)
         pt, n_parts = host_plan.partition_tokens, host_plan.max_slots
         ws_bytes = pba.paged_decode_shared_workspace_bytes(pool, Hq, B, mb, splan)
@@ -474,7 +477,7 @@ def run_workload(args, name, pba, torch, dev):
                     ("balanced" if req_pt == BALANCED else
                      ("caller (suggest_partition_tokens)" if args.partition_tokens == AUTO
                       else "fixed"))),
-                   "decode_path": path,
+                   "decode_path": "balanced" if flat else path,
                    "tables": "ragged" if row_offsets is not None else "dense",
                    "table_cells": table_cells,
                    "kernel_block": P >> split,
@@ -503,7 +506,9 @@ def run_workload(args, name, pba, torch, dev):
                      "traffic": traffic,
                      "kernel": (f"decode_bf16_shared_kernel<{d}> (chunk-first + sequence-first, "
                                 "merge fused in)") if host_plan is not None else
-                               f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in)",
+                               (f"decode_bf16_flat_kernel<{d}> (balanced chunk ranges, cut rows "
+                                "merged in)" if flat else
+                                f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in)"),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "_kv_value_bytes": kv_unique,
     }

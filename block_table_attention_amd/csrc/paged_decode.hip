@@ -300,12 +300,19 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
 // `pv`, `h` and `tn_end` describe the chunk being prefetched (the same row as
 // the current chunk, except in the balanced kernel, where the next chunk may
 // belong to another (request, kv head)); t0 and t_end describe the current one.
+// vmode (balanced kernel, blocks of 64 or more tokens): the V rows of a
+// 64-token half-tile share 128-byte lines, which a wave that walks its chunks
+// in order would read one chunk apart (the line may leave the L2 in between).
+//   0: load the V of chunk tn;
+//   1: also load the V of chunk tn + 32 (same block) into vf2;
+//   2: chunk tn's V is already in vf2 (loaded with the previous chunk).
 template <int D, bool IMPLICIT = false>
 __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, int tn, int t_end,
                                            int tn_end, int ncols, float scale_log2,
                                            const bf16x8 (&qf)[D / 32], u32x4 (&kf)[2][D / 32],
                                            u32x4 (&vf)[D / 16], float& m_run, float& l_run,
-                                           f32x4 (&acc)[D / 16], int n, int g) {
+                                           f32x4 (&acc)[D / 16], int n, int g,
+                                           u32x4 (*vf2)[D / 16] = nullptr, int vmode = 0) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
   constexpr int CH = 32;
@@ -385,7 +392,13 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
     acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi, acc[mt], 0, 0, 0);
     acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo, acc[mt], 0, 0, 0);
   }
-  load_v<D>(vf, pv, h, tn, nb0, nb1, n, g);
+  if (vmode == 2) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) vf[mt] = (*vf2)[mt];
+  } else {
+    load_v<D>(vf, pv, h, tn, nb0, nb1, n, g);
+    if (vmode == 1) load_v<D>(*vf2, pv, h, tn + CH, nb0, nb0, n, g);
+  }
 }
 
 // Grid: x = kv head, y = request, z = partition.  Work-groups reach the
@@ -546,33 +559,49 @@ struct FlatShared {
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Merge n pieces (slot_of(j), j < n, in order) of column cn, dims 4 c4 ..
-// 4 c4 + 3, into (M, L, O) and write the rows, or store one piece at
-// dst_slot.  The loads of a tile of pieces are all issued before any is used.
+// Pieces are stored in the accumulator order of the MFMA tiles, columns
+// fastest: value (dim 16 mt + 4 q + i, column cn) of slot s sits at
+//   s G D + ((mt 4 + i) 4 + q) G + cn,
+// so a wave's store of one accumulator register covers 4 G consecutive floats
+// and a merge load of 64 consecutive items covers whole 4 G-float runs.  The
+// stores and loads are device coherent (they bypass the XCD's L2); without
+// this order each would fill a quarter of every 64-byte write or read.
+__device__ __forceinline__ int64_t piece_at(int64_t s, int G, int D, int mt, int i, int q, int cn) {
+  return s * G * D + (int64_t)((mt * 4 + i) * 4 + q) * G + cn;
+}
+
+// Merge n pieces (slot_of(j), j < n, in order) of item j (column j % G, dims
+// 16 mt + 4 q .. + 3 with q = (j / G) % 4, mt = j / (4 G)) into (M, L, O) and
+// write the rows, or store one piece at dst_slot.  The loads of a tile of
+// pieces are all issued before any is used.
 template <int D, typename SlotOf>
 __device__ void flat_merge_item(const DecodeArgs& a, const FlatArgs& f, SlotOf slot_of, int n,
-                                int64_t row0, int cn, int c4, bool to_rows, int64_t dst_slot) {
+                                int64_t row0, int item, bool to_rows, int64_t dst_slot) {
   const int G = a.G;
+  const int cn = item % G;
+  const int rq = item / G;
+  const int q = rq & 3;
+  const int mt = rq >> 2;
   float M = -INFINITY, L = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
   constexpr int TILE = 8;
   for (int j0 = 0; j0 < n; j0 += TILE) {
-    float mt[TILE], lt[TILE];
+    float mt_[TILE], lt[TILE];
     f32x4 ut[TILE];
 #pragma unroll
     for (int j = 0; j < TILE; ++j) {
       const int64_t s = slot_of(min(j0 + j, n - 1));
-      mt[j] = ld_state(f.piece_ml + (s * G + cn) * 2);
+      mt_[j] = ld_state(f.piece_ml + (s * G + cn) * 2);
       lt[j] = ld_state(f.piece_ml + (s * G + cn) * 2 + 1);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(f.piece_u + (s * G + cn) * D + 4 * c4 + e);
+      for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(f.piece_u + piece_at(s, G, D, mt, e, q, cn));
     }
 #pragma unroll
     for (int j = 0; j < TILE; ++j) {
-      if (j0 + j >= n || mt[j] == -INFINITY) continue;
-      const float Mn = fmaxf(M, mt[j]);
+      if (j0 + j >= n || mt_[j] == -INFINITY) continue;
+      const float Mn = fmaxf(M, mt_[j]);
       const float sa = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
-      const float sb = fast_exp2(mt[j] - Mn);
+      const float sb = fast_exp2(mt_[j] - Mn);
       L = L * sa + lt[j] * sb;
       O = O * sa + ut[j] * sb;
       M = Mn;
@@ -580,12 +609,12 @@ __device__ void flat_merge_item(const DecodeArgs& a, const FlatArgs& f, SlotOf s
   }
   if (to_rows) {
     const f32x4 res = L > 0.f ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-    *reinterpret_cast<f32x4*>(a.out + (row0 + cn) * D + 4 * c4) = res;
-    if (a.lse && c4 == 0) a.lse[row0 + cn] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    *reinterpret_cast<f32x4*>(a.out + (row0 + cn) * D + 16 * mt + 4 * q) = res;
+    if (a.lse && rq == 0) a.lse[row0 + cn] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) st_state(f.piece_u + (dst_slot * G + cn) * D + 4 * c4 + e, O[e]);
-    if (c4 == 0) {
+    for (int e = 0; e < 4; ++e) st_state(f.piece_u + piece_at(dst_slot, G, D, mt, e, q, cn), O[e]);
+    if (rq == 0) {
       st_state(f.piece_ml + (dst_slot * G + cn) * 2, M);
       st_state(f.piece_ml + (dst_slot * G + cn) * 2 + 1, L);
     }
@@ -717,6 +746,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     u32x4 qraw[KK];
     u32x4 kf[2][KK];
     u32x4 vf[MT];
+    u32x4 vf2[MT];
+    // Chunk pairs (2j, 2j + 1) of one segment share V lines when the kernel
+    // block holds 64 tokens or more: the even chunk's load brings both.
+    const bool pairs = log2P >= 6;
+    bool have2 = false;  // vf2 holds the V of the chunk after the one in vf
     {
       load_q(qraw, r, h);
       int64_t pb0, pb1;
@@ -727,6 +761,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
       __builtin_amdgcn_sched_barrier(0);
       load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
+      if (pairs && !(k & 1) && k + 1 < nch && cb + 1 < ce) {
+        load_v<D>(vf2, pv, h, t0 + CH, pb0, pb0, n, g);
+        have2 = true;
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
     bf16x8 qf[KK];
@@ -768,8 +806,18 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       const PoolView pvn = r2 == r ? pv : view(r2, T2);
       u32x4 qnext[KK];
       if (new_seg) load_q(qnext, r2, h2);
+      // The prefetched chunk (k2): its V came with the previous load, or it
+      // starts a pair whose second chunk this wave also reads.
+      int vmode = 0;
+      if (have2) {
+        vmode = 2;
+        have2 = false;
+      } else if (pairs && !last && !(k2 & 1) && k2 + 1 < nch2 && c + 2 < ce) {
+        vmode = 1;
+        have2 = true;
+      }
       chunk_step<D, IMPLICIT>(pvn, h2, k * CH, k2 * CH, T, T2, G, a.scale_log2, qf, kf, vf,
-                              m_run, l_run, acc, n, g);
+                              m_run, l_run, acc, n, g, &vf2, vmode);
       if (seg_end) {
         float l_tot = l_run + __shfl_xor(l_run, 16, 64);
         l_tot += __shfl_xor(l_tot, 32, 64);
@@ -787,11 +835,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
         } else {
           const int64_t slot = wid * 2 + (first_seg ? 0 : 1);
           if (n < G) {
-            float* u = f.piece_u + (slot * G + n) * D;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-              for (int i = 0; i < 4; ++i) st_state(u + 16 * mt + 4 * g + i, acc[mt][i]);
+              for (int i = 0; i < 4; ++i)
+                st_state(f.piece_u + piece_at(slot, G, D, mt, i, g, n), acc[mt][i]);
             if (g == 0) {
               st_state(f.piece_ml + (slot * G + n) * 2, m_run);
               st_state(f.piece_ml + (slot * G + n) * 2 + 1, l_tot);
@@ -866,8 +914,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   };
   for (int idx = tid; idx < nseg * items; idx += kDecodeThreads) {
     const int si = idx / items;
-    const int cn = (idx - si * items) / C4;
-    const int c4 = idx - si * items - cn * C4;
+    const int item = idx - si * items;
     int pr, ph;
     int64_t s0, s1;
     seg_info(si, pr, ph, s0, s1);
@@ -877,7 +924,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     const bool inside = s0 >= gb && s1 <= ge;
     // Work-group slot 0: the segment began before this range; 1: it ends after it.
     const int64_t wslot = f.wg_slot0 + wg * 2 + (s0 < gb ? 0 : 1);
-    flat_merge_item<D>(a, f, wave_slot, s_np[si], row0, cn, c4, inside, wslot);
+    flat_merge_item<D>(a, f, wave_slot, s_np[si], row0, item, inside, wslot);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
@@ -901,8 +948,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   for (int idx = tid; idx < nseg * items; idx += kDecodeThreads) {
     const int si = idx / items;
     if (!s_last[si]) continue;
-    const int cn = (idx - si * items) / C4;
-    const int c4 = idx - si * items - cn * C4;
+    const int item = idx - si * items;
     int pr, ph;
     int64_t s0, s1;
     seg_info(si, pr, ph, s0, s1);
@@ -911,7 +957,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     // segments that began before their ranges (slot 0).
     auto wg_slot = [&](int j) { return f.wg_slot0 + (w0 + j) * 2 + (j == 0 ? 1 : 0); };
     const int64_t row0 = (int64_t)pr * a.num_q_heads + (int64_t)ph * G;
-    flat_merge_item<D>(a, f, wg_slot, s_last[si], row0, cn, c4, true, 0);
+    flat_merge_item<D>(a, f, wg_slot, s_last[si], row0, item, true, 0);
   }
   if (tid < nseg && s_last[tid]) {
     int pr, ph;
