@@ -540,22 +540,17 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
 // keeps every CU streaming until the end instead of waiting on its longest
 // rows.
 // A segment inside one wave's range is written by that wave.  A segment cut
-// by wave boundaries leaves one partial state per wave; after the loops the
-// work-group merges the pieces of each such segment that lie in its range
-// (in range order): into the rows if the segment lies inside the work-group's
-// range, otherwise into one work-group piece, which is counted with one atomic
-// per (request, kv head); the work-group that brings the count to the number
-// of work-groups over the segment merges their pieces and resets the counter.
-// Row lengths and their chunk prefix sums live in LDS (at most kFlatMaxRows
-// rows; the host keeps the chunk total below 2^31).
-constexpr int kFlatMaxRows = kFlatMaxBatch;
-
-struct FlatShared {
-  int32_t pre[kFlatMaxRows + 1];  // chunks of every segment of rows < r
-  int32_t T[kFlatMaxRows];
-  int32_t scan[kDecodeThreads];
-  int32_t pend[kWaves][2];        // segment (r * H + h) of each wave's partial pieces, or -1
-};
+// by wave boundaries leaves one partial state per wave, in LDS; after the
+// loops the work-group merges the pieces of each such segment that lie in its
+// range (in range order): into the rows if the segment lies inside the
+// work-group's range, otherwise into one work-group piece in memory, which is
+// counted with one atomic per (request, kv head); the work-group that brings
+// the count to the number of work-groups over the segment merges their pieces
+// and resets the counter.
+// Dynamic LDS (flat_lds_bytes): row lengths T[B] and their chunk prefix sums
+// pre[B + 1] (the host keeps the chunk total below 2^31), the waves' chunk
+// totals, the segment of each wave piece (r * H + h, or -1), and the wave
+// pieces themselves in the accumulator order of piece_at.
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -621,6 +616,49 @@ __device__ void flat_merge_item(const DecodeArgs& a, const FlatArgs& f, SlotOf s
   }
 }
 
+// Merge the n wave pieces of item `item` held in LDS (local slots packed 3
+// bits each, in range order) and write the rows, or store one work-group
+// piece at dst_slot in memory.
+template <int D>
+__device__ void lds_merge_item(const DecodeArgs& a, const FlatArgs& f, const float* l_ml,
+                               const float* l_u, uint32_t packed, int n, int64_t row0, int item,
+                               bool to_rows, int64_t dst_slot) {
+  const int G = a.G;
+  const int cn = item % G;
+  const int rq = item / G;
+  const int q = rq & 3;
+  const int mt = rq >> 2;
+  float M = -INFINITY, L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < n; ++j) {
+    const int ls = (packed >> (3 * j)) & 7;
+    const float m = l_ml[(ls * G + cn) * 2];
+    if (m == -INFINITY) continue;
+    const float l = l_ml[(ls * G + cn) * 2 + 1];
+    f32x4 u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = l_u[piece_at(ls, G, D, mt, e, q, cn)];
+    const float Mn = fmaxf(M, m);
+    const float sa = M == -INFINITY ? 0.f : fast_exp2(M - Mn);
+    const float sb = fast_exp2(m - Mn);
+    L = L * sa + l * sb;
+    O = O * sa + u * sb;
+    M = Mn;
+  }
+  if (to_rows) {
+    const f32x4 res = L > 0.f ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+    *reinterpret_cast<f32x4*>(a.out + (row0 + cn) * D + 16 * mt + 4 * q) = res;
+    if (a.lse && rq == 0) a.lse[row0 + cn] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) st_state(f.piece_u + piece_at(dst_slot, G, D, mt, e, q, cn), O[e]);
+    if (rq == 0) {
+      st_state(f.piece_ml + (dst_slot * G + cn) * 2, M);
+      st_state(f.piece_ml + (dst_slot * G + cn) * 2 + 1, L);
+    }
+  }
+}
+
 template <int D, int MODE>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
@@ -632,7 +670,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   constexpr int CH = 32;
   constexpr bool IMPLICIT = MODE == kTablesContiguous;
 
-  __shared__ FlatShared sh;
+  extern __shared__ __align__(16) int32_t flat_lds[];
   const int B = a.batch;
   const int H = a.num_kv_heads;
   const int G = a.G;
@@ -641,6 +679,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   const int n = lane & 15;
   const int g = lane >> 4;
   const int P = 1 << log2P;
+  const int wave = uni(tid >> 6);
+  int32_t* const s_T = flat_lds;                 // [B]
+  int32_t* const s_pre = s_T + B;                // [B + 1]
+  int32_t* const s_wsum = s_pre + B + 1;         // [kWaves]
+  int32_t* const s_pend = s_wsum + kWaves;       // [2 kWaves]
+  float* const l_ml = reinterpret_cast<float*>(flat_lds + flat_head_words(B));
+  float* const l_u = l_ml + 2 * kWaves * G * 2;
 
   // Rows and their chunk counts; prefix sums over the batch.  A row with no
   // visible token (rejected in validate mode) has no chunk and gets out = 0,
@@ -650,7 +695,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   int local = 0;
   for (int r = rb; r < re; ++r) {
     const int T = seq_lens[r];
-    sh.T[r] = T;
+    s_T[r] = T;
     if (T > 0) {
       local += H * ((T + CH - 1) / CH);
     } else if (blockIdx.x == 0) {
@@ -661,29 +706,31 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       }
     }
   }
-  sh.scan[tid] = local;
-  if (tid < kWaves) sh.pend[tid][0] = sh.pend[tid][1] = -1;
-  __syncthreads();
-  for (int st = 1; st < kDecodeThreads; st <<= 1) {
-    const int v = tid >= st ? sh.scan[tid - st] : 0;
-    __syncthreads();
-    sh.scan[tid] += v;
-    __syncthreads();
+  // Inclusive scan of the thread totals: within each wave by shuffles, then
+  // over the waves' totals.
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
   }
+  if (lane == 63) s_wsum[wave] = incl;
+  if (tid < 2 * kWaves) s_pend[tid] = -1;
+  __syncthreads();
   {
-    int run = sh.scan[tid] - local;
+    int run = incl - local;
+    for (int w = 0; w < wave; ++w) run += s_wsum[w];
     for (int r = rb; r < re; ++r) {
-      sh.pre[r] = run;
-      const int T = sh.T[r];
+      s_pre[r] = run;
+      const int T = s_T[r];
       if (T > 0) run += H * ((T + CH - 1) / CH);
     }
-    if (tid == 0) sh.pre[B] = sh.scan[kDecodeThreads - 1];
+    if (tid == kDecodeThreads - 1) s_pre[B] = run;
   }
   __syncthreads();
 
   // Ranges: this work-group's, then this wave's quarter of it.
-  const int wave = uni(tid >> 6);
-  const int64_t C = uni(sh.pre[B]);
+  const int64_t C = uni(s_pre[B]);
   const int64_t NG = min((int64_t)gridDim.x, C);
   const int64_t wg = blockIdx.x;
   if (wg >= NG) return;
@@ -732,13 +779,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       int lo = 0, hi = B - 1;
       while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if (uni(sh.pre[mid]) <= cb) lo = mid; else hi = mid - 1;
+        if (uni(s_pre[mid]) <= cb) lo = mid; else hi = mid - 1;
       }
       r = uni(lo);
     }
-    int T = uni(sh.T[r]);
+    int T = uni(s_T[r]);
     int nch = (T + CH - 1) / CH;
-    const int off0 = (int)(cb - uni(sh.pre[r]));
+    const int off0 = (int)(cb - uni(s_pre[r]));
     int h = off0 / nch;
     int k = off0 - h * nch;
 
@@ -779,7 +826,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     bool first_seg = true;
     int k_first = k;  // first chunk of this wave's piece of the current segment
-    const int64_t wid = wg * kWaves + wave;
 
     for (int64_t c = cb; c < ce; ++c) {
       const bool last = c + 1 == ce;
@@ -797,7 +843,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
             h2 = 0;
             do {
               ++r2;
-              T2 = uni(sh.T[r2]);
+              T2 = uni(s_T[r2]);
             } while (T2 <= 0);
             nch2 = (T2 + CH - 1) / CH;
           }
@@ -833,19 +879,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
               a.lse[row] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
           }
         } else {
-          const int64_t slot = wid * 2 + (first_seg ? 0 : 1);
+          // A cut segment: this wave's piece goes to its LDS slot.
+          const int ls = wave * 2 + (first_seg ? 0 : 1);
           if (n < G) {
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                st_state(f.piece_u + piece_at(slot, G, D, mt, i, g, n), acc[mt][i]);
+              for (int i = 0; i < 4; ++i) l_u[piece_at(ls, G, D, mt, i, g, n)] = acc[mt][i];
             if (g == 0) {
-              st_state(f.piece_ml + (slot * G + n) * 2, m_run);
-              st_state(f.piece_ml + (slot * G + n) * 2 + 1, l_tot);
+              l_ml[(ls * G + n) * 2] = m_run;
+              l_ml[(ls * G + n) * 2 + 1] = l_tot;
             }
           }
-          if (lane == 0) sh.pend[wave][first_seg ? 0 : 1] = r * H + h;
+          if (lane == 0) s_pend[ls] = r * H + h;
         }
         m_run = -INFINITY;
         l_run = 0.f;
@@ -867,12 +913,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       nch = nch2;
     }
   }
-  // Pieces: every wave's stores complete, then the work-group merges.  All
-  // cut segments of the range go through each step together: (1) merge each
-  // segment's wave pieces -- into the rows if it lies inside this range, else
-  // into one work-group piece; (2) count the work-group pieces; (3) the last
-  // work-group of a segment merges its work-group pieces into the rows.
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  // Pieces: every wave's LDS pieces are written, then the work-group merges.
+  // All cut segments of the range go through each step together: (1) merge
+  // each segment's wave pieces -- into the rows if it lies inside this range,
+  // else into one work-group piece in memory; (2) count the work-group pieces;
+  // (3) the last work-group of a segment merges its work-group pieces into
+  // the rows.
   __syncthreads();
   __shared__ int s_seg[2 * kWaves];
   __shared__ uint32_t s_packed[2 * kWaves];  // wave pieces: 3-bit local slots 2w + which
@@ -883,7 +929,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   if (tid == 0) {
     int ns = 0;
     for (int qi = 0; qi < 2 * kWaves; ++qi) {
-      const int seg = sh.pend[qi >> 1][qi & 1];
+      const int seg = s_pend[qi];
       if (seg < 0) continue;
       int at = 0;
       while (at < ns && s_seg[at] != seg) ++at;
@@ -908,8 +954,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     const int seg = s_seg[si];
     pr = seg / H;
     ph = seg - pr * H;
-    const int pn = (sh.T[pr] + CH - 1) / CH;
-    s0 = (int64_t)sh.pre[pr] + (int64_t)ph * pn;
+    const int pn = (s_T[pr] + CH - 1) / CH;
+    s0 = (int64_t)s_pre[pr] + (int64_t)ph * pn;
     s1 = s0 + pn;
   };
   for (int idx = tid; idx < nseg * items; idx += kDecodeThreads) {
@@ -918,13 +964,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     int pr, ph;
     int64_t s0, s1;
     seg_info(si, pr, ph, s0, s1);
-    const uint32_t packed = s_packed[si];
-    auto wave_slot = [&](int j) { return wg * 2 * kWaves + ((packed >> (3 * j)) & 7); };
     const int64_t row0 = (int64_t)pr * a.num_q_heads + (int64_t)ph * G;
     const bool inside = s0 >= gb && s1 <= ge;
     // Work-group slot 0: the segment began before this range; 1: it ends after it.
-    const int64_t wslot = f.wg_slot0 + wg * 2 + (s0 < gb ? 0 : 1);
-    flat_merge_item<D>(a, f, wave_slot, s_np[si], row0, item, inside, wslot);
+    const int64_t wslot = wg * 2 + (s0 < gb ? 0 : 1);
+    lds_merge_item<D>(a, f, l_ml, l_u, s_packed[si], s_np[si], row0, item, inside, wslot);
   }
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
@@ -955,7 +999,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     const int64_t w0 = s_w0[si];
     // Work-group w0 holds the segment's start (its slot 1); the others hold
     // segments that began before their ranges (slot 0).
-    auto wg_slot = [&](int j) { return f.wg_slot0 + (w0 + j) * 2 + (j == 0 ? 1 : 0); };
+    auto wg_slot = [&](int j) { return (w0 + j) * 2 + (j == 0 ? 1 : 0); };
     const int64_t row0 = (int64_t)pr * a.num_q_heads + (int64_t)ph * G;
     flat_merge_item<D>(a, f, wg_slot, s_last[si], row0, item, true, 0);
   }
@@ -1366,8 +1410,9 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
 hipError_t launch_paged_decode_flat(const DecodeArgs& a, const FlatArgs& f, int head_dim,
                                     int n_wg, hipStream_t stream) {
   const dim3 grid((unsigned)n_wg), block(kDecodeThreads);
+  const unsigned lds = (unsigned)flat_lds_bytes(a.batch, a.G, head_dim);
 #define PBA_FLAT(DD, MM)                                                                         \
-  hipLaunchKernelGGL((decode_bf16_flat_kernel<DD, MM>), grid, block, 0, stream, a.tables,       \
+  hipLaunchKernelGGL((decode_bf16_flat_kernel<DD, MM>), grid, block, lds, stream, a.tables,     \
                      a.seq_lens, a.k, a.v, a.max_blocks, a.log2P, a.num_blocks - 1,            \
                      (int32_t)a.k_sb, (int32_t)a.k_sh, a, f)
   if (head_dim == 128) {

@@ -202,15 +202,20 @@ WsLayout workspace_layout(int32_t batch, int32_t kv_heads, int64_t rows, int32_t
 
 // The balanced decode (one 4-wave work-group per CU, the batch's chunks split
 // evenly over the waves) serves partition_tokens == PBA_PARTITIONS_BALANCED
-// for bf16 batches of at most kFlatMaxBatch rows; everything else uses the
+// for bf16 batches of at most kFlatMaxBatch rows whose LDS (row prefix sums
+// and the waves' pieces) fits in kFlatMaxLds bytes; everything else uses the
 // grid of (kv head, request, partition).
-bool use_flat(const pba_kv_pool* pool, int32_t batch, int32_t partition_tokens,
-              int32_t max_blocks_per_seq) {
+bool use_flat(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
+              int32_t partition_tokens, int32_t max_blocks_per_seq) {
+  if (partition_tokens != PBA_PARTITIONS_BALANCED || pool->dtype != PBA_BF16 || batch < 1 ||
+      batch > pba::kFlatMaxBatch)
+    return false;
   // Chunk counts are int32 in the kernel: B * H_kv * ceil(max T / 32) < 2^31.
   const int64_t max_T = (int64_t)max_blocks_per_seq * pool->block_size;
   const int64_t chunks = (int64_t)batch * pool->num_kv_heads * ((max_T + 31) / 32);
-  return partition_tokens == PBA_PARTITIONS_BALANCED && pool->dtype == PBA_BF16 && batch >= 1 &&
-         batch <= pba::kFlatMaxBatch && chunks < INT32_MAX;
+  const int G = num_q_heads / pool->num_kv_heads;
+  return chunks < INT32_MAX &&
+         pba::flat_lds_bytes(batch, G, pool->head_dim) <= pba::kFlatMaxLds;
 }
 
 // A balanced request that the balanced decode cannot serve falls back to the
@@ -222,9 +227,9 @@ int32_t grid_request(int32_t partition_tokens) {
 int flat_workgroups() { return device_cu_count(); }  // one work-group per CU
 
 // Balanced-decode workspace: [counters int32 B*H_kv | pad][piece (m, l) |
-// pad][piece u], two piece slots per wave then two per work-group, G columns
-// each.
-int64_t flat_slots() { return 2 * (int64_t)flat_workgroups() * (pba::kDecodeThreads / 64 + 1); }
+// pad][piece u], two work-group piece slots per work-group, G columns each
+// (the waves' pieces stay in LDS).
+int64_t flat_slots() { return 2 * (int64_t)flat_workgroups(); }
 
 WsLayout flat_layout(int32_t batch, int32_t kv_heads, int32_t G, int head_dim) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
@@ -504,7 +509,7 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
   int32_t pt = 0, np = 0;
-  if (use_flat(pool, batch, partition_tokens, max_blocks_per_seq)) {
+  if (use_flat(pool, num_q_heads, batch, partition_tokens, max_blocks_per_seq)) {
     np = flat_workgroups() * pba::kDecodeThreads / 64;  // waves the batch is spread over
   } else {
     st = plan_partitions(pool, batch > 0 ? batch : 1, max_blocks_per_seq,
@@ -523,7 +528,7 @@ size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_h
   if (pba_paged_decode_plan(pool, num_q_heads, batch, max_blocks_per_seq, partition_tokens, &pt,
                             &np))
     return 0;
-  if (use_flat(pool, batch, partition_tokens, max_blocks_per_seq))
+  if (use_flat(pool, num_q_heads, batch, partition_tokens, max_blocks_per_seq))
     return flat_layout(batch, pool->num_kv_heads, num_q_heads / pool->num_kv_heads,
                        pool->head_dim).bytes;
   return workspace_layout(batch, pool->num_kv_heads, (int64_t)batch * num_q_heads, np,
@@ -546,7 +551,7 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
   if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
-  const bool flat = use_flat(pool, batch, partition_tokens, max_blocks_per_seq);
+  const bool flat = use_flat(pool, num_q_heads, batch, partition_tokens, max_blocks_per_seq);
   int32_t pt = 0, np = 0;
   if (!flat) {
     st = plan_partitions(pool, batch, max_blocks_per_seq, grid_request(partition_tokens), &pt,
@@ -632,7 +637,6 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
     pba::FlatArgs f;
     f.piece_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
     f.piece_u = reinterpret_cast<float*>(wsb + ws.u_off);
-    f.wg_slot0 = 2 * (int64_t)flat_workgroups() * (pba::kDecodeThreads / 64);
     return pba::launch_paged_decode_flat(a, f, pool->head_dim, flat_workgroups(), s) == hipSuccess
                ? PBA_OK
                : PBA_ERR_HIP;

@@ -78,14 +78,14 @@ struct SharedArgs {
   int32_t nz_items;  // grid z planes of chunk-first items: ceil(n_items / batch)
 };
 
-// Balanced decode: partial states of segments cut by range boundaries, two
-// slots per wave followed by two per work-group ([slots][G][2], [slots][G][D]).
+// Balanced decode: partial states of segments cut by work-group range
+// boundaries, two slots per work-group ([slots][G][2], [slots][G][D]).
 struct FlatArgs {
   float* piece_ml;
   float* piece_u;
-  int64_t wg_slot0;  // first work-group slot: 2 * waves
 };
-constexpr int kFlatMaxBatch = 2048;  // rows the balanced decode takes (LDS prefix sums)
+constexpr int kFlatMaxBatch = 2048;        // rows the balanced decode takes
+constexpr int64_t kFlatMaxLds = 64 * 1024;  // its dynamic LDS, bytes
 
 hipError_t launch_paged_decode_flat(const DecodeArgs& a, const FlatArgs& f, int head_dim,
                                     int n_wg, hipStream_t stream);
@@ -105,6 +105,16 @@ hipError_t launch_paged_decode_shared(const DecodeArgs& a, const SharedArgs& sa,
 #define PBA_DECODE_WAVES 4
 #endif
 constexpr int kDecodeThreads = 64 * PBA_DECODE_WAVES;
+
+// Dynamic LDS of the balanced decode (4-byte words): T[B], pre[B + 1], the
+// waves' chunk totals and piece segments, then the waves' pieces,
+// (m, l)[2 waves][G][2] and u[2 waves][G * D].
+constexpr int64_t flat_head_words(int B) {
+  return (2 * (int64_t)B + 1 + 3 * PBA_DECODE_WAVES + 3) / 4 * 4;
+}
+constexpr int64_t flat_lds_bytes(int B, int G, int D) {
+  return 4 * (flat_head_words(B) + 2 * PBA_DECODE_WAVES * (int64_t)G * (2 + D));
+}
 inline int decode_granule(int dtype) { return (dtype == PBA_BF16 ? 32 : 64) * PBA_DECODE_WAVES; }
 
 }  // namespace pba

@@ -242,8 +242,11 @@ int pba_block_copy_bundle(const pba_kv_group* groups, int32_t num_groups,
  *                 choice (sized so that all work-groups are resident at once);
  *                 PBA_PARTITIONS_BALANCED: the batch's 32-token chunks, laid
  *                 end to end, are split evenly over one work-group per CU,
- *                 whatever the row lengths (bf16 batches of at most 2048 rows;
- *                 otherwise as 0) -- for ragged batches, where equal
+ *                 whatever the row lengths (bf16 batches of at most 2048 rows
+ *                 whose work-group state -- eight partial states of G x
+ *                 (head_dim + 2) floats and the rows' prefix sums -- fits in
+ *                 64 KiB of LDS, i.e. not G = 16 at head_dim 128; otherwise
+ *                 as 0) -- for ragged batches, where equal
  *                 partitions leave most work-groups empty; otherwise the
  *                 partition length in tokens, a positive multiple of 256.
  *                 Partitions are reduced by the log-sum-exp merge; an empty

@@ -155,16 +155,27 @@ def test_workspace_and_plan():
         assert pt.value % 128 == 0 and pt.value * npart.value >= mb * 16
         assert pt.value * (npart.value - 1) < mb * 16
     # The balanced decode: one 4-wave work-group per CU (256 CUs when no device
-    # is visible); workspace = counters + two piece states per wave and two per
-    # work-group.
+    # is visible); workspace = counters + two piece states per work-group (the
+    # waves' pieces stay in LDS).
     for B, mb in [(1, 1), (8, 256), (2048, 4)]:
         assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, B, mb, -1, ctypes.byref(pt),
                                          ctypes.byref(npart)) == 0
         waves = npart.value
         assert pt.value == 0 and waves % 4 == 0 and waves >= 4
-        G, slots = 4, 2 * waves + 2 * (waves // 4)
+        G, slots = 4, 2 * (waves // 4)
         expect = up(B * 2 * 4) + up(slots * G * 2 * 4) + slots * G * 128 * 4
         assert lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 8, B, mb, -1) == expect
+    # Its LDS holds 8 wave pieces of G x (head_dim + 2) floats and the row
+    # prefix sums, at most 64 KiB: G = 16 at head_dim 128 takes the grid plan,
+    # head_dim 64 stays balanced up to 2048 rows.
+    assert lib.pba_paged_decode_plan(ctypes.byref(d), 32, 8, 64, -1, ctypes.byref(pt),
+                                     ctypes.byref(npart)) == 0
+    assert pt.value > 0
+    d64 = _desc(head_dim=64, k_stride_block=2 * 16 * 64, k_stride_head=16 * 64,
+                v_stride_block=2 * 16 * 64, v_stride_head=16 * 64)
+    assert lib.pba_paged_decode_plan(ctypes.byref(d64), 32, 2048, 4, -1, ctypes.byref(pt),
+                                     ctypes.byref(npart)) == 0
+    assert pt.value == 0
     assert lib.pba_paged_decode_plan(ctypes.byref(d), 8, 2, 64, -2, ctypes.byref(pt),
                                      ctypes.byref(npart)) == -3
     assert lib.pba_status_string(-5).decode().startswith("workspace")
