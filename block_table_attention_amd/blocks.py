@@ -225,7 +225,7 @@ def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus
     (``PARTITIONS_BALANCED``: the batch's chunks spread evenly over the CUs)
     when ``balanced_ok`` (bf16 pools, at most 2048 rows), else partitions of
     about twice the mean length.  Measured on MI355X, lognormal batches of 128
-    requests (median 100, max 8192 tokens): 52 / 53 / 54 us at P = 16 / 64 /
+    requests (median 100, max 8192 tokens): 50 / 49 / 50 us at P = 16 / 64 /
     256 balanced, 61 / 77 / 76 us with 1024-token partitions, 102 / 139 / 140
     us unsplit; uniform or mildly ragged batches are fastest with the
     library's plan.

@@ -306,12 +306,16 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
 //   0: load the V of chunk tn;
 //   1: also load the V of chunk tn + 32 (same block) into vf2;
 //   2: chunk tn's V is already in vf2 (loaded with the previous chunk).
+// pf = false: the wave's last chunk, nothing to prefetch.  The loop exits
+// right after it, so every iteration that reaches the next one has the same
+// loads in flight (the waits in the loop stay exact), and the wave's final
+// waits do not cover reloads of a chunk it no longer needs.
 template <int D, bool IMPLICIT = false>
 __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, int tn, int t_end,
                                            int tn_end, int ncols, float scale_log2,
                                            const bf16x8 (&qf)[D / 32], u32x4 (&kf)[2][D / 32],
                                            u32x4 (&vf)[D / 16], float& m_run, float& l_run,
-                                           f32x4 (&acc)[D / 16], int n, int g,
+                                           f32x4 (&acc)[D / 16], int n, int g, bool pf = true,
                                            u32x4 (*vf2)[D / 16] = nullptr, int vmode = 0) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
@@ -333,7 +337,7 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
       s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[at][kk]),
                                                        qf[kk], s[at], 0, 0, 0);
   }
-  load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
+  if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
 
   const int tbase = t0 + 8 * g;  // token of k-slot j = 0 of this lane
   float x[8];
@@ -395,7 +399,7 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
   if (vmode == 2) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) vf[mt] = (*vf2)[mt];
-  } else {
+  } else if (pf) {
     load_v<D>(vf, pv, h, tn, nb0, nb1, n, g);
     if (vmode == 1) load_v<D>(*vf2, pv, h, tn + CH, nb0, nb0, n, g);
   }
@@ -506,12 +510,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int it = 0; it < n_w; ++it, t0 += kWaves * CH) {
-    // Next chunk of this wave; on the last iteration the current chunk is
-    // requested again (in bounds, served from L2), which keeps the number of
-    // loads in flight the same on every iteration.
-    const int tn = it + 1 < n_w ? t0 + kWaves * CH : t0;
+    // Next chunk of this wave (none after the last).
+    const bool more = it + 1 < n_w;
+    const int tn = more ? t0 + kWaves * CH : t0;
     chunk_step<D, IMPLICIT>(pv, h, t0, tn, T, T, G, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n,
-                            g);
+                            g, more);
   }
 
   // Wave state -> LDS.  acc[mt][i] is O^T[dim 16mt + 4g + i][head n]: four
@@ -532,9 +535,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
 // Balanced decode: the batch's chunks spread evenly over the chip
 // ---------------------------------------------------------------------------
 // The (request, kv head) segments of the batch -- ceil(T/32) chunks each --
-// are laid end to end, request major.  With C chunks and NG work-groups (one
-// per CU), work-group w owns chunks [w C / NG, (w+1) C / NG), and its wave i
-// the i-th quarter of that range.  A wave walks its range chunk by chunk with
+// are laid end to end, request major, on a cost axis: a chunk spans
+// kChunkUnits and every segment seg_cost more in front of its chunks (its
+// fixed cost: the q load, a new table row, the epilogue, the pieces), so
+// waves over many short segments get fewer chunks.  With V units and NG
+// work-groups (one per CU), work-group w owns the chunks that start in
+// [w V / NG, (w+1) V / NG), and its wave i those in the i-th quarter of that
+// range.  seg_cost = 0 splits the chunk count evenly.  A wave walks its range chunk by chunk with
 // the grid kernel's software pipeline, the prefetch crossing from one segment
 // into the next (the next segment's q is requested with it), so a ragged batch
 // keeps every CU streaming until the end instead of waiting on its longest
@@ -731,14 +738,58 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
 
   // Ranges: this work-group's, then this wave's quarter of it.
   const int64_t C = uni(s_pre[B]);
+  // NG <= C: every work-group range spans at least kChunkUnits, so no range
+  // between two chunks of one segment is empty (the merge counts every
+  // work-group between a segment's first and last chunk).
   const int64_t NG = min((int64_t)gridDim.x, C);
   const int64_t wg = blockIdx.x;
   if (wg >= NG) return;
-  const int64_t gb = wg * C / NG, ge = (wg + 1) * C / NG;
-  const int64_t cb = gb + (ge - gb) * wave / kWaves;
-  const int64_t ce = gb + (ge - gb) * (wave + 1) / kWaves;
-  // Work-group owning chunk c: the largest w with floor(w C / NG) <= c.
-  auto wg_owner = [&](int64_t c) -> int64_t { return ((c + 1) * NG + C - 1) / C - 1; };
+  const int64_t A = f.seg_cost;
+  const int64_t V = kChunkUnits * C + A * H * B;
+  // Start of row r on the cost axis, and the position of chunk k of head h of
+  // row r (nch chunks per head).
+  auto vpre = [&](int r) -> int64_t { return kChunkUnits * (int64_t)s_pre[r] + A * H * r; };
+  auto chunk_pos = [&](int r, int h, int k, int nch) -> int64_t {
+    return vpre(r) + h * (kChunkUnits * (int64_t)nch + A) + A + kChunkUnits * (int64_t)k;
+  };
+  // The largest row r with mul pre[r] + add r <= x (a nondecreasing key that
+  // row 0 meets): a binary search over groups of 64 rows, then one compare
+  // per lane and a ballot, so the dependent LDS reads number log2(B / 64) + 1.
+  auto last_row_le = [&](int64_t mul, int64_t add, int64_t x) -> int {
+    int glo = 0, ghi = (B - 1) >> 6;
+    while (glo < ghi) {
+      const int mid = (glo + ghi + 1) >> 1;
+      if (mul * uni(s_pre[64 * mid]) + add * (64 * mid) <= x) glo = mid; else ghi = mid - 1;
+    }
+    const int rr = 64 * glo + lane;
+    const bool ok = rr < B && mul * (int64_t)s_pre[min(rr, B)] + add * rr <= x;
+    return uni(64 * glo + (int)__popcll(__ballot(ok)) - 1);
+  };
+  // The first chunk that starts at or after position x (C past the end).
+  auto first_chunk = [&](int64_t x) -> int64_t {
+    if (x >= V) return C;
+    const int r = last_row_le(kChunkUnits, A * H, x);
+    const int T = uni(s_T[r]);
+    const int64_t nch = T > 0 ? (T + CH - 1) / CH : 0;
+    const int64_t span = kChunkUnits * nch + A;
+    const int64_t rel = x - vpre(r);
+    const int64_t base = uni(s_pre[r]);
+    const int64_t hh = span > 0 ? rel / span : H;
+    if (hh >= H) return base + H * nch;
+    const int64_t off = rel - hh * span;
+    const int64_t k = off <= A ? 0 : (off - A + kChunkUnits - 1) / kChunkUnits;
+    return k >= nch ? base + (hh + 1) * nch : base + hh * nch + k;
+  };
+  const int64_t x0 = wg * V / NG, x1 = (wg + 1) * V / NG;
+  const int64_t cb = first_chunk(x0 + (x1 - x0) * wave / kWaves);
+  const int64_t ce = first_chunk(x0 + (x1 - x0) * (wave + 1) / kWaves);
+  // The work-group's chunks [gb, ge): the first wave's start, the last one's end.
+  __shared__ int64_t s_gbe[2];
+  if (lane == 0 && wave == 0) s_gbe[0] = cb;
+  if (lane == 0 && wave == kWaves - 1) s_gbe[1] = ce;
+  // Work-group owning the chunk at position p: the largest w with
+  // floor(w V / NG) <= p.
+  auto wg_owner = [&](int64_t p) -> int64_t { return ((p + 1) * NG + V - 1) / V - 1; };
 
   // Reads of one row's table: dense rows at r * max_blocks; ragged rows from
   // row_offsets; contiguous rows are a slot's blocks.
@@ -774,15 +825,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
 
   if (cb < ce) {
     // Segment cursor at cb: row r (the largest with pre[r] <= cb), head h, chunk k.
-    int r;
-    {
-      int lo = 0, hi = B - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (uni(s_pre[mid]) <= cb) lo = mid; else hi = mid - 1;
-      }
-      r = uni(lo);
-    }
+    int r = last_row_le(1, 0, cb);
     int T = uni(s_T[r]);
     int nch = (T + CH - 1) / CH;
     const int off0 = (int)(cb - uni(s_pre[r]));
@@ -863,7 +906,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
         have2 = true;
       }
       chunk_step<D, IMPLICIT>(pvn, h2, k * CH, k2 * CH, T, T2, G, a.scale_log2, qf, kf, vf,
-                              m_run, l_run, acc, n, g, &vf2, vmode);
+                              m_run, l_run, acc, n, g, !last, &vf2, vmode);
       if (seg_end) {
         float l_tot = l_run + __shfl_xor(l_run, 16, 64);
         l_tot += __shfl_xor(l_tot, 32, 64);
@@ -949,7 +992,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
   if (nseg == 0) return;
   constexpr int C4 = D / 4;
   const int items = G * C4;
-  // A segment's rows, its first chunk and the work-groups over it.
+  // This work-group's chunks [gb, ge).
+  const int64_t gb = s_gbe[0], ge = s_gbe[1];
+  // A segment's rows and its chunks [s0, s1).
   auto seg_info = [&](int si, int& pr, int& ph, int64_t& s0, int64_t& s1) {
     const int seg = s_seg[si];
     pr = seg / H;
@@ -978,8 +1023,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     seg_info(tid, pr, ph, s0, s1);
     int last = 0;
     if (!(s0 >= gb && s1 <= ge)) {
-      const int64_t w0 = wg_owner(s0);
-      const int nwg = (int)(wg_owner(s1 - 1) - w0 + 1);
+      // The work-groups over the segment: owners of its first and last chunk.
+      const int pn = (int)(s1 - s0);
+      const int64_t w0 = wg_owner(chunk_pos(pr, ph, 0, pn));
+      const int nwg = (int)(wg_owner(chunk_pos(pr, ph, pn - 1, pn)) - w0 + 1);
       last = __hip_atomic_fetch_add(a.counters + (int64_t)pr * H + ph, 1, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT) == nwg - 1
                  ? nwg
@@ -1144,8 +1191,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int it = 0; it < n_w; ++it, t0 += stride) {
-    const int tn = it + 1 < n_w ? t0 + stride : t0;
-    chunk_step<D>(pv, h, t0, tn, te, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g);
+    const bool more = it + 1 < n_w;
+    const int tn = more ? t0 + stride : t0;
+    chunk_step<D>(pv, h, t0, tn, te, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g,
+                  more);
   }
 
   l_run += __shfl_xor(l_run, 16, 64);

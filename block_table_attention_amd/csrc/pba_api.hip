@@ -226,6 +226,14 @@ int32_t grid_request(int32_t partition_tokens) {
 
 int flat_workgroups() { return device_cu_count(); }  // one work-group per CU
 
+// Fixed cost of one (request, kv head) segment in the balanced decode, in
+// units of 1/kChunkUnits of a 32-token chunk, by kernel block size.  Per-wave
+// loop times grow with the segments a wave crosses (about a third of a chunk
+// each at 64+ token blocks); on lognormal batches (128 requests, median 100
+// tokens) half a chunk at 64+ token blocks and three eighths at 16 and 32
+// gave the shortest kernels, 4-10% below an even split of the chunks.
+int32_t flat_seg_cost(int kernel_block) { return kernel_block >= 64 ? 4 : 3; }
+
 // Balanced-decode workspace: [counters int32 B*H_kv | pad][piece (m, l) |
 // pad][piece u], two work-group piece slots per work-group, G columns each
 // (the waves' pieces stay in LDS).
@@ -637,6 +645,7 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
     pba::FlatArgs f;
     f.piece_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
     f.piece_u = reinterpret_cast<float*>(wsb + ws.u_off);
+    f.seg_cost = flat_seg_cost(pool->block_size);  // the kernel block
     return pba::launch_paged_decode_flat(a, f, pool->head_dim, flat_workgroups(), s) == hipSuccess
                ? PBA_OK
                : PBA_ERR_HIP;

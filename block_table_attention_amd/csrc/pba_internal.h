@@ -83,7 +83,9 @@ struct SharedArgs {
 struct FlatArgs {
   float* piece_ml;
   float* piece_u;
+  int32_t seg_cost;  // fixed cost of a (request, kv head) segment, in kChunkUnits per chunk
 };
+constexpr int kChunkUnits = 8;  // cost of one 32-token chunk on the balancing axis
 constexpr int kFlatMaxBatch = 2048;        // rows the balanced decode takes
 constexpr int64_t kFlatMaxLds = 64 * 1024;  // its dynamic LDS, bytes
 
