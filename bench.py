@@ -904,6 +904,7 @@ def run_contiguous(args, name, pba, torch, dev):
                    "kv_layout": args.kv, "batch": B, "context_sum": int(lens.sum()),
                    "tile_rows": P, "blocks_per_slot": bps, "page_bytes": page,
                    "partition_tokens": pt, "num_partitions": n_parts,
+                   "decode_path": "balanced" if req_pt == BALANCED and pt == 0 else "plain",
                    "step": f"kv_append({B} tokens) + paged_decode_contiguous",
                    "step_launch": "eager"},
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
@@ -916,7 +917,9 @@ def run_contiguous(args, name, pba, torch, dev):
                   "mapped_over_rows": round(led["mapped_bytes"] / kv_bytes, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": f"decode_bf16_kernel<{d}, contiguous> (slot index, no block table)",
+                     "kernel": (f"decode_bf16_flat_kernel<{d}, contiguous> (slot index, balanced "
+                                "chunk ranges)" if req_pt == BALANCED and pt == 0 else
+                                f"decode_bf16_kernel<{d}, contiguous> (slot index, no block table)"),
                      "algorithmic_bytes_per_launch": alg},
         "_kv_value_bytes": kv_bytes,
     }
