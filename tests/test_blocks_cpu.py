@@ -228,3 +228,11 @@ def test_partition_suggestion():
     pt = suggest_partition_tokens(ragged, 8, balanced_ok=False)
     assert pt % 256 == 0 and 512 <= pt < 8192
     assert suggest_partition_tokens([100] * 4000 + [8192], 8) > 0    # too many rows to balance
+    # Mildly ragged batches over half the CUs: 512-token partitions (1024 from
+    # 4096 tokens on); under half the CUs, short or uniform: the library plan.
+    mild = list(range(101, 2029, 48))                                # 41 rows, 101..2021
+    assert suggest_partition_tokens(mild, 4) == 512                  # 164 units > 128
+    assert suggest_partition_tokens(mild[:30], 4) == 0               # 120 units < 128
+    assert suggest_partition_tokens([x * 4 for x in mild], 8) == 1024
+    assert suggest_partition_tokens([x // 2 for x in mild], 8) == 0  # longest < 1536
+    assert suggest_partition_tokens([2000] * 40, 8) == 0             # uniform
