@@ -82,13 +82,54 @@ __device__ __forceinline__ float ld_state(const float* p) {
 // Final merge of the partition states of one (request, kv head):
 //   O = sum_p w_p u_p / L,  w_p = 2^(m_p - M),  M = max_p m_p,  L = sum_p w_p l_p,
 // partitions in index order, TILE at a time with a running (M, L, O).
-// A thread owns dims j, j + D/4, j + D/2, j + 3D/4 of one head, so it needs
-// only that head's (m, l), and each load or store instruction of a wave covers
-// whole runs of consecutive dims.  Every load of a tile is issued before any
-// is used and none
-// sits under a lane-dependent branch (partition indices are clamped in bounds
-// and the surplus ignored), so a tile costs one memory round trip and the
-// merge needs no LDS and no barrier.
+// A thread owns dims c, c + D/4, c + D/2, c + 3D/4 of one q-head row, so it
+// needs only that row's (m, l), and each load or store instruction of a wave
+// covers whole runs of consecutive dims.  Every load of a tile is issued
+// before any is used and none sits under a lane-dependent branch (partition
+// indices are clamped in bounds and the surplus ignored), so a tile costs one
+// memory round trip and the merge needs no LDS and no barrier.
+template <int D, int TILE>
+__device__ __forceinline__ void merge_dims(const DecodeArgs& a, int64_t row, int c, int np_r) {
+  constexpr int C4 = D / 4;
+  const float* ml = a.ws_ml + row * a.n_parts * 2;
+  const float* uu = a.ws_u + row * a.n_parts * D + c;
+  float M = -INFINITY, L = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = 0; p0 < np_r; p0 += TILE) {
+    float mt[TILE], lt[TILE];
+    f32x4 ut[TILE];
+#pragma unroll
+    for (int j = 0; j < TILE; ++j) {
+      const int64_t pp = min(p0 + j, np_r - 1);
+      mt[j] = ld_state(ml + 2 * pp);
+      lt[j] = ld_state(ml + 2 * pp + 1);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(uu + pp * D + C4 * e);
+    }
+    float Mt = M;
+#pragma unroll
+    for (int j = 0; j < TILE; ++j)
+      if (p0 + j < np_r) Mt = fmaxf(Mt, mt[j]);
+    if (Mt == -INFINITY) continue;  // only empty states so far: identity
+    const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mt);
+    L *= sc;
+    O *= sc;
+#pragma unroll
+    for (int j = 0; j < TILE; ++j) {
+      if (p0 + j < np_r && mt[j] != -INFINITY) {
+        const float w = fast_exp2(mt[j] - Mt);
+        L += w * lt[j];
+        O += w * ut[j];
+      }
+    }
+    M = Mt;
+  }
+  const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) a.out[row * D + c + C4 * e] = res[e];
+  if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+}
+
 template <int D, int TILE>
 __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
   constexpr int C4 = D / 4;
@@ -96,45 +137,24 @@ __device__ void merge_partitions(const DecodeArgs& a, int r, int h, int np_r) {
   const int64_t row0 = (int64_t)r * a.num_q_heads + (int64_t)h * G;
   for (int idx = threadIdx.x; idx < G * C4; idx += kDecodeThreads) {
     const int n = idx / C4;
-    const int c = idx - n * C4;  // dims c + C4 * e, e < 4
-    const int64_t row = row0 + n;
-    const float* ml = a.ws_ml + row * a.n_parts * 2;
-    const float* uu = a.ws_u + row * a.n_parts * D + c;
-    float M = -INFINITY, L = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    for (int p0 = 0; p0 < np_r; p0 += TILE) {
-      float mt[TILE], lt[TILE];
-      f32x4 ut[TILE];
-#pragma unroll
-      for (int j = 0; j < TILE; ++j) {
-        const int64_t pp = min(p0 + j, np_r - 1);
-        mt[j] = ld_state(ml + 2 * pp);
-        lt[j] = ld_state(ml + 2 * pp + 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ut[j][e] = ld_state(uu + pp * D + C4 * e);
-      }
-      float Mt = M;
-#pragma unroll
-      for (int j = 0; j < TILE; ++j)
-        if (p0 + j < np_r) Mt = fmaxf(Mt, mt[j]);
-      if (Mt == -INFINITY) continue;  // only empty states so far: identity
-      const float sc = (M == -INFINITY) ? 0.f : fast_exp2(M - Mt);
-      L *= sc;
-      O *= sc;
-#pragma unroll
-      for (int j = 0; j < TILE; ++j) {
-        if (p0 + j < np_r && mt[j] != -INFINITY) {
-          const float w = fast_exp2(mt[j] - Mt);
-          L += w * lt[j];
-          O += w * ut[j];
-        }
-      }
-      M = Mt;
-    }
-    const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) a.out[row * D + c + C4 * e] = res[e];
-    if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+    merge_dims<D, TILE>(a, row0 + n, idx - n * C4, np_r);
+  }
+}
+
+// The final merges of nm requests of kv head h at once (rows[k] with nps[k]
+// partitions): one pass of the whole work-group, so the rows' load round
+// trips overlap instead of following one another.
+template <int D, int TILE>
+__device__ void merge_rows(const DecodeArgs& a, const int* rows, const int* nps, int nm, int h) {
+  constexpr int C4 = D / 4;
+  const int G = a.G;
+  const int per = G * C4;
+  for (int idx = threadIdx.x; idx < nm * per; idx += kDecodeThreads) {
+    const int k = idx / per;
+    const int rem = idx - k * per;
+    const int n = rem / C4;
+    merge_dims<D, TILE>(a, (int64_t)rows[k] * a.num_q_heads + (int64_t)h * G + n, rem - n * C4,
+                        nps[k]);
   }
 }
 
@@ -1265,11 +1285,32 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     s_last[threadIdx.x] = last;
   }
   __syncthreads();
-  for (int i = 0; i < nrows; ++i) {
-    if (!s_last[i]) continue;
-    merge_row<D>(a, row0 + i, h, s_slots[i]);
-    if (threadIdx.x == 0) a.counters[(int64_t)(row0 + i) * a.num_kv_heads + h] = 0;
+  // The rows this work-group completed, merged together.
+  __shared__ int s_mrow[kMaxItemRows];
+  __shared__ int s_mnp[kMaxItemRows];
+  __shared__ int s_nm, s_maxnp;
+  if (threadIdx.x == 0) {
+    int nm = 0, mx = 0;
+    for (int i = 0; i < nrows; ++i) {
+      if (!s_last[i]) continue;
+      s_mrow[nm] = row0 + i;
+      s_mnp[nm] = s_slots[i];
+      mx = max(mx, s_slots[i]);
+      ++nm;
+    }
+    s_nm = nm;
+    s_maxnp = mx;
   }
+  __syncthreads();
+  const int nm = s_nm;
+  if (nm == 0) return;
+  if (s_maxnp <= 4)
+    merge_rows<D, 4>(a, s_mrow, s_mnp, nm, h);
+  else if (s_maxnp <= 8)
+    merge_rows<D, 8>(a, s_mrow, s_mnp, nm, h);
+  else
+    merge_rows<D, 16>(a, s_mrow, s_mnp, nm, h);
+  if ((int)threadIdx.x < nm) a.counters[(int64_t)s_mrow[threadIdx.x] * a.num_kv_heads + h] = 0;
 }
 
 // ---------------------------------------------------------------------------
