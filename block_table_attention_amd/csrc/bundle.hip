@@ -42,11 +42,13 @@ __global__ __launch_bounds__(256) void kv_append_bundle_kernel(BundleAppendArgs 
     r /= H;
     const int l = r % L;
     const int i = r / L;
-    const int64_t s = G.slots[i];
-    if (s < 0) return;
-    const int64_t blk = s >> G.log2P, off = s & (P - 1);
+    // The piece and the slot go out together (the piece is in bounds for every task).
     const u32x4 val = *reinterpret_cast<const u32x4*>(
         G.k_new + ((((int64_t)i * L + l) * H + h) * D) * es + 16 * c);
+    const int64_t s = G.slots[i];
+    asm volatile("" ::"v"(val), "v"(s));  // keeps the piece load above the test
+    if (s < 0) return;
+    const int64_t blk = s >> G.log2P, off = s & (P - 1);
     *reinterpret_cast<u32x4*>(G.k + (l * G.k_sl + blk * G.k_sb + h * G.k_sh + off * D) * es +
                               16 * c) = val;
   } else {
@@ -57,11 +59,12 @@ __global__ __launch_bounds__(256) void kv_append_bundle_kernel(BundleAppendArgs 
     r /= H;
     const int l = r % L;
     const int c = r / L;
-    const int64_t s = G.slots[i];
-    if (s < 0) return;
-    const int64_t blk = s >> G.log2P, off = s & (P - 1);
     const u32x4 piece = *reinterpret_cast<const u32x4*>(
         G.v_new + ((((int64_t)i * L + l) * H + h) * D) * es + 16 * c);
+    const int64_t s = G.slots[i];
+    asm volatile("" ::"v"(piece), "v"(s));
+    if (s < 0) return;
+    const int64_t blk = s >> G.log2P, off = s & (P - 1);
     const int epc = 16 / es;
     const int64_t e0 = l * G.v_sl + blk * G.v_sb + h * G.v_sh + (int64_t)(c * epc) * P + off;
     if (es == 2) {

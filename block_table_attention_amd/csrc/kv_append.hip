@@ -3,7 +3,9 @@
 // slot s -> (block s div P, offset s mod P) ("M5.3 - KV Memory Layout and
 // Exact Reuse", 0x03C-0x03D); the rows are bit copies, so NaN payloads and
 // signed zeros survive.  One thread moves one 16-byte piece of one token's row
-// of one kv head, so every load is independent of every store:
+// of one kv head, so every load is independent of every store.  The piece and
+// the slot are both requested before the slot is tested (the piece is in
+// bounds for every task), so they share one memory round trip:
 //   K tasks (piece fastest): the K tile is token major, a row is one run of d
 //      scalars, and neighbouring lanes read and write neighbouring pieces;
 //   V tasks (token fastest): the V tile is dim major ([d][P]), a row becomes d
@@ -31,11 +33,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     const int64_t rest = t / pieces;
     const int h = (int)(rest % H);
     const int64_t i = rest / H;
-    const int64_t s = a.slots[i];
-    if (s < 0) return;
-    const int64_t blk = s >> a.log2P, off = s & (P - 1);
     const u32x4 val = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.k_new) +
                                                       (i * H + h) * D + c * EPC);
+    const int64_t s = a.slots[i];
+    asm volatile("" ::"v"(val), "v"(s));  // keeps the piece load above the test
+    if (s < 0) return;
+    const int64_t blk = s >> a.log2P, off = s & (P - 1);
     *reinterpret_cast<u32x4*>(static_cast<E*>(a.k) + blk * a.k_sb + h * a.k_sh + off * D +
                               c * EPC) = val;
   } else {
@@ -44,15 +47,16 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendArgs a) {
     const int64_t rest = t / a.n;
     const int h = (int)(rest % H);
     const int c = (int)(rest / H);
-    const int64_t s = a.slots[i];
-    if (s < 0) return;
-    const int64_t blk = s >> a.log2P, off = s & (P - 1);
     union {
       u32x4 u;
       E e[EPC];
     } piece;
     piece.u = *reinterpret_cast<const u32x4*>(static_cast<const E*>(a.v_new) + (i * H + h) * D +
                                               c * EPC);
+    const int64_t s = a.slots[i];
+    asm volatile("" ::"v"(piece.u), "v"(s));
+    if (s < 0) return;
+    const int64_t blk = s >> a.log2P, off = s & (P - 1);
     E* dst = static_cast<E*>(a.v) + blk * a.v_sb + h * a.v_sh + (int64_t)(c * EPC) * P + off;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) dst[(int64_t)e * P] = piece.e[e];
