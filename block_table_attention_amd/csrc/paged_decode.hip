@@ -1100,6 +1100,237 @@ typedef const int32_t __attribute__((address_space(4))) item_t;
 constexpr int kItemInts = 8;      // row0, nrows, tb, te, slot, tiles, 0, 0
 constexpr int kMaxItemRows = 64;  // 4 tiles x 16 rows (G = 1)
 
+// One 32-token chunk for NT 16-column tiles that share its K and V (the
+// chunk-first items): one K load and one V load serve every tile, each tile
+// keeps its own online-softmax state.  Otherwise as chunk_step.
+template <int D, int NT>
+__device__ __forceinline__ void chunk_step_nt(const PoolView& pv, int h, int t0, int tn, int t_end,
+                                              const int (&ncols)[NT], float scale_log2,
+                                              const bf16x8 (&qf)[NT][D / 32],
+                                              u32x4 (&kf)[2][D / 32], u32x4 (&vf)[D / 16],
+                                              float (&m_run)[NT], float (&l_run)[NT],
+                                              f32x4 (&acc)[NT][D / 16], int n, int g, bool pf) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int CH = 32;
+  int64_t nb0, nb1;
+  chunk_blocks(pv, tn, nb0, nb1);
+  if (tn + 16 >= t_end) nb1 = nb0;  // no block past the piece's last one is read
+
+  f32x4 s[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int at = 0; at < 2; ++at) {
+      s[t][at] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        s[t][at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, kf[at][kk]), qf[t][kk], s[t][at], 0, 0, 0);
+    }
+  if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
+
+  const int tbase = t0 + 8 * g;
+  bf16x8 phi[NT], plo[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float x[8];
+#pragma unroll
+    for (int at = 0; at < 2; ++at)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * at + i;
+        x[j] = (tbase + j < t_end) ? s[t][at][i] * scale_log2 : -INFINITY;
+      }
+    float cmax = x[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+    const float m_new = fmaxf(m_run[t], cmax);
+    const float alpha = fast_exp2(m_run[t] - m_new);
+    m_run[t] = m_new;
+    float p[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = (n < ncols[t]) ? fast_exp2(x[j] - m_new) : 0.f;
+      psum += p[j];
+    }
+    l_run[t] = l_run[t] * alpha + psum;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= alpha;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 hi = (__bf16)p[j];
+      phi[t][j] = hi;
+      plo[t][j] = (__bf16)(p[j] - (float)hi);
+    }
+  }
+
+  // Tail chunk: zero the V scalars of tokens >= t_end (they may hold NaN).
+  if (t0 + CH > t_end) {
+    const int cnt = t_end - tbase;
+    u32x4 mask;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      mask[q] = (cnt >= 2 * q + 2) ? 0xFFFFFFFFu : ((cnt == 2 * q + 1) ? 0x0000FFFFu : 0u);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) vf[mt] &= mask;
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const bf16x8 va = __builtin_bit_cast(bf16x8, vf[mt]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, phi[t], acc[t][mt], 0, 0, 0);
+      acc[t][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, plo[t], acc[t][mt], 0, 0, 0);
+    }
+  }
+  if (pf) load_v<D>(vf, pv, h, tn, nb0, nb1, n, g);
+}
+
+// The walk of one piece [tb, te) for an item's tiles, and the merge of the
+// waves' states into each column's row or slot.  The tiles form groups of NT
+// (NT = 2 for items of 2 or 4 tiles): the waves of a group split the piece's
+// chunks and each wave serves all NT tiles of its group from one K/V load,
+// so a wave walks piece / (32 * waves per group) chunks whatever the tiles.
+// The states go through LDS one tile of each group at a time.
+template <int D, int NT>
+__device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& st, int* s_slots,
+                                            const PoolView& pv, int h, int row0, int nrows, int tb,
+                                            int te, int tiles, int slot, int rT, int rpb, int rps,
+                                            int part_tokens, int wave, int n, int g) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int CH = 32;
+  constexpr int C4 = D / 4;
+  const int G = a.G;
+  const int rpt = 16 / G;           // rows per 16-column tile
+  const int groups = tiles / NT;
+  const int wpg = kWaves / groups;  // waves per group
+  const int grp = wave / wpg;
+  const int sub = wave - grp * wpg;
+  int ncols[NT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) ncols[j] = max(0, min(rpt, nrows - (grp * NT + j) * rpt)) * G;
+  const int first = tb + sub * CH;
+  const int stride = wpg * CH;
+  const int span = te - first;
+  const int n_w = (span > 0 && ncols[0] > 0) ? (span + stride - 1) / stride : 0;
+
+  int t0 = first;
+  u32x4 qraw[NT][KK];
+  u32x4 kf[2][KK];
+  u32x4 vf[MT];
+  if (n_w > 0) {
+    int64_t pb0, pb1;
+    chunk_blocks(pv, t0, pb0, pb1);
+    if (t0 + 16 >= te) pb1 = pb0;  // no block past the piece's last one is read
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int cn = n < ncols[j] ? n : 0;
+      const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                             ((int64_t)(row0 + (grp * NT + j) * rpt + cn / G) * a.num_q_heads +
+                              (int64_t)h * G + cn % G) * D;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        qraw[j][kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 qf[NT][KK];
+  float m_run[NT], l_run[NT];
+  f32x4 acc[NT][MT];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qf[j][kk] = __builtin_bit_cast(bf16x8, n < ncols[j] ? qraw[j][kk] : u32x4{0u, 0u, 0u, 0u});
+    m_run[j] = -INFINITY;
+    l_run[j] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[j][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int it = 0; it < n_w; ++it, t0 += stride) {
+    const bool more = it + 1 < n_w;
+    const int tn = more ? t0 + stride : t0;
+    chunk_step_nt<D, NT>(pv, h, t0, tn, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n,
+                         g, more);
+  }
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    l_run[j] += __shfl_xor(l_run[j], 16, 64);
+    l_run[j] += __shfl_xor(l_run[j], 32, 64);
+  }
+  // Slot count of each row, clamped to the workspace's slots per row.
+  if ((int)threadIdx.x < nrows) {
+    const int ns = rps + (rT > rpb ? (rT - rpb + part_tokens - 1) / part_tokens : 0);
+    s_slots[threadIdx.x] = min(max(ns, 0), a.n_parts);
+  }
+#pragma unroll
+  for (int p = 0; p < NT; ++p) {
+    if (p) __syncthreads();  // the previous tile's merge has read the LDS states
+    if (g == 0) {
+      st.m[wave][n] = m_run[p];
+      st.l[wave][n] = l_run[p];
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<f32x4*>(&st.o[wave][n][16 * mt + 4 * g]) = acc[p][mt];
+    __syncthreads();
+    // Columns of tile gi * NT + p of every group gi: column n -> item row
+    // t * rpt + n / G, q-head h * G + n % G; the tile's state merges the
+    // states of its group's waves.
+    for (int idx = threadIdx.x; idx < groups * 16 * C4; idx += kDecodeThreads) {
+      const int col = idx / C4;
+      const int c = idx - col * C4;  // dims c + C4 * e, e < 4
+      const int gi = col >> 4;
+      const int cn = col & 15;
+      const int t = gi * NT + p;
+      const int ri = t * rpt + cn / G;
+      if (cn >= rpt * G || ri >= nrows) continue;
+      const int w0 = gi * wpg;
+      const int w1 = w0 + wpg;
+      float M = -INFINITY;
+      for (int w = w0; w < w1; ++w) M = fmaxf(M, st.m[w][cn]);
+      float L = 0.f;
+      f32x4 O = {0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+        for (int w = w0; w < w1; ++w) {
+          const float mw = st.m[w][cn];
+          if (mw == -INFINITY) continue;
+          const float wt = fast_exp2(mw - M);
+          L += wt * st.l[w][cn];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) O[e] += wt * st.o[w][cn][c + C4 * e];
+        }
+      }
+      const int64_t row = (int64_t)(row0 + ri) * a.num_q_heads + (int64_t)h * G + cn % G;
+      if (s_slots[ri] == 1) {
+        const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a.out[row * D + c + C4 * e] = res[e];
+        if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      } else {
+        const int64_t prow = row * a.n_parts + slot;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st_state(a.ws_u + prow * D + c + C4 * e, O[e]);
+        if (c == 0) {
+          st_state(a.ws_ml + prow * 2 + 0, M);
+          st_state(a.ws_ml + prow * 2 + 1, L);
+        }
+      }
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
@@ -1107,10 +1338,6 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     int32_t part_tokens, int32_t log2P, int32_t last_block, int32_t k_sb, int32_t k_sh,
     DecodeArgs a, SharedArgs sa) {
   static_assert(D == 64 || D == 128, "head_dim");
-  constexpr int KK = D / 32;
-  constexpr int MT = D / 16;
-  constexpr int CH = 32;
-  constexpr int C4 = D / 4;
 
   __shared__ WaveStates<D> st;
   __shared__ int s_slots[kMaxItemRows];  // slot count of each row of the item
@@ -1168,111 +1395,12 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   const PoolView pv{(table_t*)(tables + (int64_t)row0 * max_blocks),
                     static_cast<const uint16_t*>(kbase), static_cast<const uint16_t*>(vbase),
                     k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P, a.split_log2};
-  // This wave's columns and chunk walk: wpt waves per tile split its chunks.
-  const int wpt = kWaves / tiles;
-  const int tile = wave / wpt;
-  const int sub = wave - tile * wpt;
-  const int trow0 = tile * rpt;                       // first item row of the tile
-  const int wrows = max(0, min(rpt, nrows - trow0));  // rows of the tile
-  const int ncols = wrows * G;
-  const int first = tb + sub * CH;
-  const int stride = wpt * CH;
-  const int span = te - first;
-  const int n_w = (span > 0 && ncols > 0) ? (span + stride - 1) / stride : 0;
-
-  int t0 = first;
-  u32x4 qraw[KK];
-  u32x4 kf[2][KK];
-  u32x4 vf[MT];
-  if (n_w > 0) {
-    int64_t pb0, pb1;
-    chunk_blocks(pv, t0, pb0, pb1);
-    if (t0 + 16 >= te) pb1 = pb0;  // no block past the piece's last one is read
-    const int cn = n < ncols ? n : 0;
-    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
-                           ((int64_t)(row0 + trow0 + cn / G) * a.num_q_heads +
-                            (int64_t)h * G + cn % G) * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
-    __builtin_amdgcn_sched_barrier(0);
-    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
-    __builtin_amdgcn_sched_barrier(0);
-    load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  bf16x8 qf[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    qf[kk] = __builtin_bit_cast(bf16x8, n < ncols ? qraw[kk] : u32x4{0u, 0u, 0u, 0u});
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 acc[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int it = 0; it < n_w; ++it, t0 += stride) {
-    const bool more = it + 1 < n_w;
-    const int tn = more ? t0 + stride : t0;
-    chunk_step<D>(pv, h, t0, tn, te, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n, g,
-                  more);
-  }
-
-  l_run += __shfl_xor(l_run, 16, 64);
-  l_run += __shfl_xor(l_run, 32, 64);
-  if (g == 0) {
-    st.m[wave][n] = m_run;
-    st.l[wave][n] = l_run;
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(&st.o[wave][n][16 * mt + 4 * g]) = acc[mt];
-  // Slot count of each row, clamped to the workspace's slots per row.
-  if ((int)threadIdx.x < nrows) {
-    const int ns = rps + (rT > rpb ? (rT - rpb + part_tokens - 1) / part_tokens : 0);
-    s_slots[threadIdx.x] = min(max(ns, 0), a.n_parts);
-  }
-  __syncthreads();
-
-  // Columns of the item: tile t, column n -> item row t*rpt + n/G, q-head
-  // h*G + n%G; a tile's state merges the states of its wpt waves.
-  for (int idx = threadIdx.x; idx < tiles * 16 * C4; idx += kDecodeThreads) {
-    const int col = idx / C4;
-    const int c = idx - col * C4;  // dims c + C4 * e, e < 4
-    const int t = col >> 4;
-    const int cn = col & 15;
-    const int ri = t * rpt + cn / G;
-    if (cn >= rpt * G || ri >= nrows) continue;
-    const int w0 = t * wpt;
-    const int w1 = w0 + wpt;
-    float M = -INFINITY;
-    for (int w = w0; w < w1; ++w) M = fmaxf(M, st.m[w][cn]);
-    float L = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int w = w0; w < w1; ++w) {
-        const float mw = st.m[w][cn];
-        if (mw == -INFINITY) continue;
-        const float wt = fast_exp2(mw - M);
-        L += wt * st.l[w][cn];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) O[e] += wt * st.o[w][cn][c + C4 * e];
-      }
-    }
-    const int64_t row = (int64_t)(row0 + ri) * a.num_q_heads + (int64_t)h * G + cn % G;
-    if (s_slots[ri] == 1) {
-      const f32x4 res = (L > 0.f) ? O * (1.f / L) : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) a.out[row * D + c + C4 * e] = res[e];
-      if (a.lse && c == 0) a.lse[row] = (L > 0.f) ? (M + __log2f(L)) * kLn2 : -INFINITY;
-    } else {
-      const int64_t prow = row * a.n_parts + slot;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) st_state(a.ws_u + prow * D + c + C4 * e, O[e]);
-      if (c == 0) {
-        st_state(a.ws_ml + prow * 2 + 0, M);
-        st_state(a.ws_ml + prow * 2 + 1, L);
-      }
-    }
-  }
+  if (tiles >= 2)
+    shared_item<D, 2>(a, st, s_slots, pv, h, row0, nrows, tb, te, tiles, slot, rT, rpb, rps,
+                      part_tokens, wave, n, g);
+  else
+    shared_item<D, 1>(a, st, s_slots, pv, h, row0, nrows, tb, te, tiles, slot, rT, rpb, rps,
+                      part_tokens, wave, n, g);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's state stores are complete
   __syncthreads();
   if ((int)threadIdx.x < nrows) {
