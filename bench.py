@@ -44,6 +44,40 @@ WORKLOADS = ["long16k", "long64k", "batch32", "shared_prefix", "lognormal_p16",
 BUNDLE_WORKLOADS = {"layers32"}
 
 
+_SCRUB = None
+
+
+def cold_launch_ms(torch, fn, stream, reps):
+    """(warm, cold) median duration of one launch of fn, each between its own
+    pair of HIP events on `stream`; cold launches follow a 1 GiB read that
+    evicts the decode's rows from L2 and the 256 MB memory-side cache without
+    leaving dirty lines behind (a write scrub would make the decode pay for
+    their write-back)."""
+    global _SCRUB
+    if _SCRUB is None:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=stream.device)
+        sink = torch.empty(1, dtype=torch.float32, device=stream.device)
+        for _ in range(2):
+            torch.sum(src, dim=0, keepdim=True, out=sink)
+        torch.cuda.synchronize()
+        _SCRUB = (src, sink)
+    src, sink = _SCRUB
+    out = []
+    for cold in (False, True):
+        evs = []
+        for _ in range(reps):
+            if cold:
+                torch.sum(src, dim=0, keepdim=True, out=sink)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        out.append(float(np.median([a.elapsed_time(b) for a, b in evs])))
+    return out[0], out[1]
+
+
 AUTO = -2      # --partition-tokens auto: the caller's choice from the batch's lengths
 BALANCED = -1  # the library's balanced decomposition (PBA_PARTITIONS_BALANCED)
 
@@ -436,6 +470,7 @@ def run_workload(args, name, pba, torch, dev):
     b1.record(stream)
     torch.cuda.synchronize()
     dec_avg_ms = b0.elapsed_time(b1) / K
+    warm1_ms, cold1_ms = cold_launch_ms(torch, decode, stream, K)
     print(f"[bench] {name}: timed {K} steps ({'graph' if use_graph else 'eager'}): "
           f"{ms_per_step * 1e3:.1f} us/step, decode in eager step "
           f"{dec_ms.mean() * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
@@ -493,10 +528,18 @@ def run_workload(args, name, pba, torch, dev):
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(step_kv_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_avg_ms * 1e3, 2),
+        "decode_us_cold": round(cold1_ms * 1e3, 2),
+        "cold_over_warm": round(cold1_ms / warm1_ms, 3),
         "decode_us_in_step": round(float(dec_ms.mean()) * 1e3, 2),
         "decode_rows_per_s": round(B / (dec_avg_ms * 1e-3), 1),
+        "decode_head_rows_per_s": round(B * Hq / (dec_avg_ms * 1e-3), 1),
         "append_us": round(float(append_ms.mean()) * 1e3, 2),
         "copy_us": round(float(copy_ms.mean()) * 1e3, 2),
+        # Bytes read + written by the step's append and copy, over their event-timed durations.
+        "append_gbs": round(len(plan.step_slots) * Hkv * d * es * 2 * 2 /
+                            max(float(append_ms.mean()) * 1e-3, 1e-12) / 1e9, 2),
+        "copy_gbs": round(len(plan.step_src) * Hkv * P * d * es * 2 * 2 /
+                          max(float(copy_ms.mean()) * 1e-3, 1e-12) / 1e9, 2),
         "kv_unique_bytes": kv_unique,
         "kv_logical_bytes": kv_logical,
         "kv_logical_gbs_decode": round(kv_logical / (dec_avg_ms * 1e-3) / 1e9, 2),
@@ -504,6 +547,7 @@ def run_workload(args, name, pba, torch, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
+                     "frac_cold": round(alg_bytes / (cold1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": (f"decode_bf16_shared_kernel<{d}> (chunk-first + sequence-first, "
                                 "merge fused in)") if host_plan is not None else
                                (f"decode_bf16_flat_kernel<{d}> (balanced chunk ranges, cut rows "
@@ -714,6 +758,8 @@ def run_bundle(args, name, pba, torch, dev):
         torch.cuda.synchronize()
         return b0.elapsed_time(b1) / reps
 
+    # The burst cycles through all layers, so each layer's rows have left the
+    # caches (the other layers' rows pass through them) when it is decoded again.
     L = len(layer_pools)
     dec_avg_ms = burst(lambda: [decode_layer(i) for i in range(L)], K) / L
     copy_fused = burst(copies, K)
@@ -880,6 +926,7 @@ def run_contiguous(args, name, pba, torch, dev):
     b1.record(stream)
     torch.cuda.synchronize()
     dec_avg_ms = b0.elapsed_time(b1) / K
+    warm1_ms, cold1_ms = cold_launch_ms(torch, decode, stream, K)
     row = Hkv * d * 2 * 2
     kv_bytes = int(lens.sum()) * row
     alg = kv_bytes + B * Hq * d * 2 + B * Hq * d * 4 + B * Hq * 4 + B * 4 * 2
@@ -909,6 +956,8 @@ def run_contiguous(args, name, pba, torch, dev):
                    "step_launch": "eager"},
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "decode_us": round(dec_avg_ms * 1e3, 2),
+        "decode_us_cold": round(cold1_ms * 1e3, 2),
+        "cold_over_warm": round(cold1_ms / warm1_ms, 3),
         "arena": None if not virtual else
                  {"reserved_bytes": led["reserved_bytes"], "mapped_bytes": led["mapped_bytes"],
                   "pool_bytes": led["pool_bytes"], "page_bundles_mapped": bundles,
@@ -917,6 +966,7 @@ def run_contiguous(args, name, pba, torch, dev):
                   "mapped_over_rows": round(led["mapped_bytes"] / kv_bytes, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac_cold": round(alg / (cold1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": (f"decode_bf16_flat_kernel<{d}, contiguous> (slot index, balanced "
                                 "chunk ranges)" if req_pt == BALANCED and pt == 0 else
                                 f"decode_bf16_kernel<{d}, contiguous> (slot index, no block table)"),
