@@ -122,6 +122,8 @@ def parse():
     ap.add_argument("--page-mib", type=float, default=2.0,
                     help="physical page size of the contiguous arena, MiB")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache decode timing (kernel traces of the warm launches)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode call (profiling runs)")
@@ -470,7 +472,7 @@ def run_workload(args, name, pba, torch, dev):
     b1.record(stream)
     torch.cuda.synchronize()
     dec_avg_ms = b0.elapsed_time(b1) / K
-    warm1_ms, cold1_ms = cold_launch_ms(torch, decode, stream, K)
+    warm1_ms, cold1_ms = (None, None) if args.no_cold else cold_launch_ms(torch, decode, stream, K)
     print(f"[bench] {name}: timed {K} steps ({'graph' if use_graph else 'eager'}): "
           f"{ms_per_step * 1e3:.1f} us/step, decode in eager step "
           f"{dec_ms.mean() * 1e3:.1f} us (p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, "
@@ -528,8 +530,8 @@ def run_workload(args, name, pba, torch, dev):
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(step_kv_gbs / HBM_PEAK_GBS, 4),
         "decode_us": round(dec_avg_ms * 1e3, 2),
-        "decode_us_cold": round(cold1_ms * 1e3, 2),
-        "cold_over_warm": round(cold1_ms / warm1_ms, 3),
+        "decode_us_cold": None if cold1_ms is None else round(cold1_ms * 1e3, 2),
+        "cold_over_warm": None if cold1_ms is None else round(cold1_ms / warm1_ms, 3),
         "decode_us_in_step": round(float(dec_ms.mean()) * 1e3, 2),
         "decode_rows_per_s": round(B / (dec_avg_ms * 1e-3), 1),
         "decode_head_rows_per_s": round(B * Hq / (dec_avg_ms * 1e-3), 1),
@@ -547,7 +549,8 @@ def run_workload(args, name, pba, torch, dev):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "frac_cold": round(alg_bytes / (cold1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac_cold": None if cold1_ms is None else
+                     round(alg_bytes / (cold1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": (f"decode_bf16_shared_kernel<{d}> (chunk-first + sequence-first, "
                                 "merge fused in)") if host_plan is not None else
                                (f"decode_bf16_flat_kernel<{d}> (balanced chunk ranges, cut rows "
@@ -926,7 +929,7 @@ def run_contiguous(args, name, pba, torch, dev):
     b1.record(stream)
     torch.cuda.synchronize()
     dec_avg_ms = b0.elapsed_time(b1) / K
-    warm1_ms, cold1_ms = cold_launch_ms(torch, decode, stream, K)
+    warm1_ms, cold1_ms = (None, None) if args.no_cold else cold_launch_ms(torch, decode, stream, K)
     row = Hkv * d * 2 * 2
     kv_bytes = int(lens.sum()) * row
     alg = kv_bytes + B * Hq * d * 2 + B * Hq * d * 4 + B * Hq * 4 + B * 4 * 2
@@ -956,8 +959,8 @@ def run_contiguous(args, name, pba, torch, dev):
                    "step_launch": "eager"},
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "decode_us": round(dec_avg_ms * 1e3, 2),
-        "decode_us_cold": round(cold1_ms * 1e3, 2),
-        "cold_over_warm": round(cold1_ms / warm1_ms, 3),
+        "decode_us_cold": None if cold1_ms is None else round(cold1_ms * 1e3, 2),
+        "cold_over_warm": None if cold1_ms is None else round(cold1_ms / warm1_ms, 3),
         "arena": None if not virtual else
                  {"reserved_bytes": led["reserved_bytes"], "mapped_bytes": led["mapped_bytes"],
                   "pool_bytes": led["pool_bytes"], "page_bundles_mapped": bundles,
@@ -966,7 +969,8 @@ def run_contiguous(args, name, pba, torch, dev):
                   "mapped_over_rows": round(led["mapped_bytes"] / kv_bytes, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "frac_cold": round(alg / (cold1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "frac_cold": None if cold1_ms is None else
+                     round(alg / (cold1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": (f"decode_bf16_flat_kernel<{d}, contiguous> (slot index, balanced "
                                 "chunk ranges)" if req_pt == BALANCED and pt == 0 else
                                 f"decode_bf16_kernel<{d}, contiguous> (slot index, no block table)"),
