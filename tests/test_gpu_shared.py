@@ -52,12 +52,12 @@ def prepare(w, device):
     return opool, pool, tables, lens, qb
 
 
-def run_shared(pba, w, device, pt=256, threshold=1, check_plain=True):
-    say(w.name, w.shape, "seed", w.seed, "pt", pt, "threshold", threshold)
+def run_shared(pba, w, device, pt=256, threshold=1, check_plain=True, tiles=4):
+    say(w.name, w.shape, "seed", w.seed, "pt", pt, "threshold", threshold, "tiles", tiles)
     opool, pool, tables, lens, qb = prepare(w, device)
     P, Hkv = w.shape.block_size, w.shape.num_kv_heads
     G = w.shape.num_q_heads // Hkv
-    host = shared_plan(tables, lens, P, G, pt, threshold=threshold)
+    host = shared_plan(tables, lens, P, G, pt, threshold=threshold, tiles_per_item=tiles)
     plan = pba.SharedPlan.from_host(host, device)
     q = to_device(qb, w.shape.dtype, device)
     tab = torch.from_numpy(tables).to(device)
@@ -82,6 +82,18 @@ def test_shared_prefix_workload(pba, gpu):
     """The full shared-prefix workload: 2000-token prefix over 128 rows, child
     and sibling suffixes shared in pairs, copy-on-write tails."""
     run_shared(pba, wl.shared_prefix(), gpu)
+
+
+@pytest.mark.parametrize("tiles", [1, 2, 4])
+@pytest.mark.parametrize("G", [1, 4])
+def test_tiles_per_item(pba, gpu, tiles, G):
+    """Items of 1, 2 or 4 tiles (two-tile groups: one K/V load serves both
+    tiles of a wave), full and partly filled last tiles."""
+    w = wl.shared_prefix(children=13, prefix=900, lo=1, hi=300, num_blocks=1024)
+    if G == 1:
+        w.shape = wl.Shape(w.shape.block_size, w.shape.num_kv_heads, w.shape.num_kv_heads,
+                           w.shape.head_dim, w.shape.dtype, w.shape.num_blocks)
+    run_shared(pba, w, gpu, pt=512, tiles=tiles)
 
 
 @pytest.mark.parametrize("pt", [256, 512, 2048])
