@@ -315,7 +315,9 @@ size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_h
                                         int32_t partition_tokens);
 
 /* The partition length (tokens) and count pba_paged_decode would use; returns
- * a pba_status.  Either output pointer may be NULL. */
+ * a pba_status.  Either output pointer may be NULL.  For the balanced
+ * decomposition the length is 0 and the count is the number of waves the
+ * batch's chunks are spread over. */
 int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
                           int32_t max_blocks_per_seq, int32_t partition_tokens,
                           int32_t* partition_tokens_out, int32_t* num_partitions_out);
@@ -334,9 +336,10 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
  *                  [2] tb, [3] te: the key positions [tb, te) of those rows
  *                  [4] slot: index of the item's partial state in each row
  *                  [5] tiles: 1, 2 or 4 tiles of 16/G rows (16 columns);
- *                      nrows <= tiles * (16/G).  The 4/tiles waves of a tile
- *                      split its positions; one K/V read serves every tile,
- *                      up to 64 query columns
+ *                      nrows <= tiles * (16/G).  Tiles go in groups of two:
+ *                      the waves of a group split its positions and each
+ *                      wave serves both tiles from one K/V read (up to 64
+ *                      query columns per work-group)
  *                  [6], [7]: 0
  *   row_private  device int32 [batch][2]: (pb, ps): row r's positions
  *                [pb, T) are decoded alone in pieces of partition_tokens from
