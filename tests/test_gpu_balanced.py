@@ -165,3 +165,16 @@ def test_chunk_pairs(pba, gpu, P, d, P_k):
     ref, ref_lse = att.paged_decode(opool, qb, list(ex.tables), ex.seq_lens, 1 / math.sqrt(d))
     assert np.max(np.abs(out_b.cpu().numpy() - ref)) <= TOL
     assert np.max(np.abs(lse_b.cpu().numpy() - ref_lse)) <= TOL
+
+
+@pytest.mark.parametrize("G,d", [(16, 64), (2, 128)])
+def test_group_sizes(pba, gpu, G, d):
+    """The widest LDS pieces the balanced decode takes (G = 16 at head_dim 64,
+    8 wave pieces of 16 x 66 floats) and a narrow group, on ragged rows."""
+    rng = np.random.default_rng(4100 + G)
+    lengths = [int(x) for x in rng.integers(1, 600, size=150)]
+    w = small_workload("bf16", 16, d, 2, G, lengths, 20261202 + 1900 + G)
+    plan = pba.paged_decode_plan(pba.KVPool.empty(8, 16, 2, d, torch.bfloat16, gpu), 2 * G, 150,
+                                 40, BAL)
+    assert plan[0] == 0  # served by the balanced decode, not the grid
+    run_workload(pba, w, gpu, partition_tokens=BAL)
