@@ -280,13 +280,16 @@ __device__ __forceinline__ void chunk_blocks(const PoolView& pv, int t0, int64_t
 }
 
 template <int D>
+// Rows at or past t_end (a tail chunk) are read as row t_end - 1: the same
+// lines as a visible row, so a tail chunk fetches no K row beyond the end;
+// their scores are masked.
 __device__ __forceinline__ void load_k(u32x4 (&kf)[2][D / 32], const PoolView& pv, int h, int t0,
-                                       int64_t pb0, int64_t pb1, int n, int g) {
+                                       int64_t pb0, int64_t pb1, int n, int g, int t_end) {
   const int P = 1 << pv.log2P;
 #pragma unroll
   for (int at = 0; at < 2; ++at) {
     // A-operand row n of tile `at` holds chunk token 8(n>>2) + 4at + (n&3).
-    const int tk = 8 * (n >> 2) + 4 * at + (n & 3);
+    const int tk = min(8 * (n >> 2) + 4 * at + (n & 3), max(t_end - 1 - t0, 0));
     const int64_t pb = (tk >= 16 && pv.log2P == 4) ? pb1 : pb0;
     const int off = row_of(pv, pb) + ((t0 + tk) & (P - 1));
     const uint16_t* kp =
@@ -357,7 +360,7 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
       s[at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[at][kk]),
                                                        qf[kk], s[at], 0, 0, 0);
   }
-  if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
+  if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g, tn_end);
 
   const int tbase = t0 + 8 * g;  // token of k-slot j = 0 of this lane
   float x[8];
@@ -511,7 +514,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qraw[kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
     __builtin_amdgcn_sched_barrier(0);
-    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
+    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g, T);
     __builtin_amdgcn_sched_barrier(0);
     load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
     __builtin_amdgcn_sched_barrier(0);
@@ -868,7 +871,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       chunk_blocks<IMPLICIT>(pv, t0, pb0, pb1);
       if (t0 + 16 >= T) pb1 = pb0;
       __builtin_amdgcn_sched_barrier(0);
-      load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
+      load_k<D>(kf, pv, h, t0, pb0, pb1, n, g, T);
       __builtin_amdgcn_sched_barrier(0);
       load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
       if (pairs && !(k & 1) && k + 1 < nch && cb + 1 < ce) {
@@ -1129,7 +1132,7 @@ __device__ __forceinline__ void chunk_step_nt(const PoolView& pv, int h, int t0,
         s[t][at] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             __builtin_bit_cast(bf16x8, kf[at][kk]), qf[t][kk], s[t][at], 0, 0, 0);
     }
-  if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g);
+  if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g, t_end);
 
   const int tbase = t0 + 8 * g;
   bf16x8 phi[NT], plo[NT];
@@ -1241,7 +1244,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
         qraw[j][kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
     }
     __builtin_amdgcn_sched_barrier(0);
-    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g);
+    load_k<D>(kf, pv, h, t0, pb0, pb1, n, g, te);
     __builtin_amdgcn_sched_barrier(0);
     load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
     __builtin_amdgcn_sched_barrier(0);
