@@ -241,10 +241,23 @@ def table_ledger(plan: Plan, P: int) -> dict:
             "table_cells_used": int(blocks.sum())}
 
 
+def decode_source_digest(root: str = ROOT) -> str:
+    """SHA-256 of the decode kernels' source with comments and whitespace
+    removed: a profile stays valid across edits that change no code."""
+    import hashlib
+    import re
+
+    csrc = os.path.join(root, "block_table_attention_amd", "csrc")
+    text = "".join(open(os.path.join(csrc, f)).read() for f in ("paged_decode.hip", "pba_internal.h"))
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = re.sub(r"\s+", " ", text).strip()
+    return hashlib.sha256(text.encode()).hexdigest()
+
+
 def profiled_traffic(workload: str):
     """HBM bytes per decode launch from the committed rocprofv3 summary, or None
-    when there is none for this workload or the decode source changed since."""
-    import hashlib
+    when there is none for this workload or the decode code changed since."""
     import re
 
     path = os.path.join(ROOT, "profiles", f"decode_bf16_{workload}.md")
@@ -252,13 +265,8 @@ def profiled_traffic(workload: str):
         return None
     text = open(path).read()
     m_t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    m_h = re.search(r"decode_source_sha256: ([0-9a-f]{64})", text)
-    if not (m_t and m_h):
-        return None
-    csrc = os.path.join(ROOT, "block_table_attention_amd", "csrc")
-    blob = b"".join(open(os.path.join(csrc, f), "rb").read()
-                    for f in ("paged_decode.hip", "pba_internal.h"))
-    if hashlib.sha256(blob).hexdigest() != m_h.group(1):
+    m_h = re.search(r"decode_code_sha256: ([0-9a-f]{64})", text)
+    if not (m_t and m_h) or m_h.group(1) != decode_source_digest():
         return None
     return int(m_t.group(1))
 

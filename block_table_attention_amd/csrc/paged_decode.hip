@@ -564,11 +564,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
 // waves over many short segments get fewer chunks.  With V units and NG
 // work-groups (one per CU), work-group w owns the chunks that start in
 // [w V / NG, (w+1) V / NG), and its wave i those in the i-th quarter of that
-// range.  seg_cost = 0 splits the chunk count evenly.  A wave walks its range chunk by chunk with
-// the grid kernel's software pipeline, the prefetch crossing from one segment
-// into the next (the next segment's q is requested with it), so a ragged batch
-// keeps every CU streaming until the end instead of waiting on its longest
-// rows.
+// range (seg_cost = 0 splits the chunk count evenly).
+// A wave walks its range chunk by chunk with the grid kernel's software
+// pipeline, the prefetch crossing from one segment into the next (the next
+// segment's q is requested with it), so a ragged batch keeps every CU
+// streaming until the end instead of waiting on its longest rows.  With
+// blocks of 64 or more tokens, the prefetch of an even chunk also loads its
+// odd partner's V, which shares the same 128-byte lines.
 // A segment inside one wave's range is written by that wave.  A segment cut
 // by wave boundaries leaves one partial state per wave, in LDS; after the
 // loops the work-group merges the pieces of each such segment that lie in its
@@ -588,9 +590,11 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // fastest: value (dim 16 mt + 4 q + i, column cn) of slot s sits at
 //   s G D + ((mt 4 + i) 4 + q) G + cn,
 // so a wave's store of one accumulator register covers 4 G consecutive floats
-// and a merge load of 64 consecutive items covers whole 4 G-float runs.  The
-// stores and loads are device coherent (they bypass the XCD's L2); without
-// this order each would fill a quarter of every 64-byte write or read.
+// and a merge load of 64 consecutive items covers whole 4 G-float runs: no
+// bank conflicts for the wave pieces in LDS, and whole 64-byte runs for the
+// work-group pieces in memory, whose device-coherent stores and loads (they
+// bypass the XCD's L2) would otherwise each fill a quarter of every 64-byte
+// write or read.
 __device__ __forceinline__ int64_t piece_at(int64_t s, int G, int D, int mt, int i, int q, int cn) {
   return s * G * D + (int64_t)((mt * 4 + i) * 4 + q) * G + cn;
 }
