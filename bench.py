@@ -110,6 +110,9 @@ def parse():
                     help="piece length of the shared-prefix plan")
     ap.add_argument("--shared-tiles", type=int, default=2, choices=[1, 2, 4],
                     help="16-column tiles per chunk-first item of the shared-prefix plan")
+    ap.add_argument("--shared-private", default="auto", choices=["auto", "pieces"],
+                    help="private ranges of the shared-prefix plan: auto = four rows per "
+                         "work-group when every range is short, pieces = a work-group per piece")
     ap.add_argument("--tables", default="dense", choices=["dense", "ragged"],
                     help="block tables as a dense [B, n_max] array or compact rows with offsets")
     ap.add_argument("--kernel-block", type=int, default=0,
@@ -354,6 +357,8 @@ def run_workload(args, name, pba, torch, dev):
         order = sharing_order(tables)
         cand = shared_plan(tables[order], lens_h[order], P, Hq // Hkv, args.shared_partition_tokens,
                            tiles_per_item=args.shared_tiles)
+        if args.shared_private == "pieces":
+            cand.private_tokens = 0
         if path == "shared" or any(b - a > 1 for a, b, _, _ in cand.chunks):
             tables, lens_h, qb, host_plan = tables[order], lens_h[order], qb[order], cand
     path = "shared" if host_plan is not None else "plain"
@@ -490,8 +495,8 @@ def run_workload(args, name, pba, torch, dev):
     kv_unique, kv_logical, alg_bytes = decode_bytes(plan, sh)
     traffic = (profiled_traffic(name if host_plan is None else f"shared_{name}")
                if args.partition_tokens == AUTO and args.shared_partition_tokens == 1024
-               and args.shared_tiles == 2 and args.tables == "dense"
-               and args.kernel_block == 0 else None)
+               and args.shared_tiles == 2 and args.shared_private == "auto"
+               and args.tables == "dense" and args.kernel_block == 0 else None)
     step_kv_gbs = kv_unique / (ms_per_step * 1e-3) / 1e9
     achieved = alg_bytes / (dec_avg_ms * 1e-3) / 1e9
     lens = plan.seq_lens
@@ -530,7 +535,10 @@ def run_workload(args, name, pba, torch, dev):
                    "shared_plan": None if host_plan is None else
                    {"chunks": len(host_plan.chunks), "items": int(host_plan.items.shape[0]),
                     "max_slots": host_plan.max_slots,
-                    "chunk_rows": int(sum(b - a for a, b, _, _ in host_plan.chunks))},
+                    "chunk_rows": int(sum(b - a for a, b, _, _ in host_plan.chunks)),
+                    "private_tokens": host_plan.private_tokens,
+                    "private_ranges": "four rows per work-group"
+                    if 0 < host_plan.private_tokens <= 128 else "a work-group per piece"},
                    "step": f"block_copy({len(plan.step_src)} pairs) + kv_append("
                            f"{len(plan.step_slots)} tokens) + "
                            f"{'paged_decode_shared' if host_plan is not None else 'paged_decode'}",

@@ -79,7 +79,8 @@ class VkvLedgers(ctypes.Structure):
 class SharedPlanDesc(ctypes.Structure):
     _fields_ = [("num_items", ctypes.c_int32), ("max_slots", ctypes.c_int32),
                 ("partition_tokens", ctypes.c_int32), ("private_parts", ctypes.c_int32),
-                ("items", ctypes.c_void_p), ("row_private", ctypes.c_void_p)]
+                ("items", ctypes.c_void_p), ("row_private", ctypes.c_void_p),
+                ("private_tokens", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
 
 
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
@@ -330,13 +331,16 @@ def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
 class SharedPlan:
     """A shared-prefix plan on the device (see ``blocks.shared_plan`` for how a
     caller builds one from its block tables): chunk-first items int32
-    [n, 8] and each row's private range int32 [B, 2]."""
+    [n, 8] and each row's private range int32 [B, 2].  ``private_tokens``
+    bounds every row's private positions (0: no bound given); at most 128,
+    the library walks four rows' private ranges per work-group."""
 
     items: torch.Tensor
     row_private: torch.Tensor
     max_slots: int
     partition_tokens: int
     private_parts: int = 0
+    private_tokens: int = 0
 
     def __post_init__(self):
         dev = self.row_private.device
@@ -347,7 +351,7 @@ class SharedPlan:
         desc = SharedPlanDesc(self.items.shape[0], self.max_slots, self.partition_tokens,
                               self.private_parts,
                               self.items.data_ptr() if self.items.numel() else None,
-                              self.row_private.data_ptr())
+                              self.row_private.data_ptr(), self.private_tokens, 0)
         object.__setattr__(self, "_desc", desc)
         object.__setattr__(self, "_ref", ctypes.byref(desc))
 
@@ -358,7 +362,7 @@ class SharedPlan:
         if items.numel() == 0:
             items = torch.zeros((0, 8), dtype=torch.int32, device=device)
         return cls(items, torch.from_numpy(host.row_private).to(device), host.max_slots,
-                   host.partition_tokens, host.private_parts)
+                   host.partition_tokens, host.private_parts, host.private_tokens)
 
 
 def paged_decode_shared_workspace_bytes(pool: KVPool, num_q_heads: int, batch: int,

@@ -317,6 +317,7 @@ class HostSharedPlan:
     partition_tokens: int
     chunks: List[Tuple[int, int, int, int]]
     private_parts: int = 0     # most private pieces of any row
+    private_tokens: int = 0    # most private positions of any row (0: none given)
 
 
 def shared_plan(tables: np.ndarray, seq_lens: Sequence[int], block_size: int, group: int,
@@ -328,8 +329,10 @@ def shared_plan(tables: np.ndarray, seq_lens: Sequence[int], block_size: int, gr
     key; each piece is one partial state (slot) of every row it covers.  Rows
     of a piece go in 16-column tiles of 16 // group rows, up to
     ``tiles_per_item`` (1, 2 or 4) tiles per item: one K/V read serves them
-    all, and the 4 / tiles waves of a tile split its keys.  A row's slots: its
-    chunks' pieces in path order, then its private pieces.
+    all (tiles go in groups of two whose waves split the keys).  A row's
+    slots: its chunks' pieces in path order, then its private pieces.  The
+    plan also bounds every row's private positions, which lets the library
+    walk short private ranges four rows per work-group.
     """
     if tiles_per_item not in (1, 2, 4):
         raise ValueError("tiles_per_item must be 1, 2 or 4")
@@ -368,4 +371,5 @@ def shared_plan(tables: np.ndarray, seq_lens: Sequence[int], block_size: int, gr
     # The launch holds one grid plane per possible private piece; the true
     # bound keeps it from filling with empty work-groups.
     return HostSharedPlan(arr, row_private, max_slots, pt, chunks,
-                          int(max(1, priv_pieces.max())))
+                          int(max(1, priv_pieces.max())),
+                          int(max(1, np.maximum(lens - private, 0).max())))

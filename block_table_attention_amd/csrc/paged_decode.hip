@@ -1099,6 +1099,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
 //    range [private_begin, T), split from private_begin.  These planes come
 //    last in dispatch order: the long chunk-first items start first (putting
 //    the short private tails first made the launch 10-40 % longer).
+//  * packed private group (item index n_items .. n_items + n_packed - 1, in
+//    the chunk-first planes; only when the plan bounds every private range
+//    to a few chunks): the private ranges of four consecutive rows, one wave
+//    each, in place of the sequence-first planes.
 // Every item leaves one partial state per column in its row's slot list; the
 // last contributor of a (row, kv head) merges the row's slots in slot order,
 // so the result does not depend on which work-group finishes last.
@@ -1339,6 +1343,92 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
   }
 }
 
+// Private ranges of up to four rows [row0, row0 + nrows), one wave each, for
+// plans that bound every private range to a few chunks: wave w walks row
+// row0 + w's positions [pb, T) alone and writes the state to the row's slot,
+// or the row itself when that is its only slot.  s_slots[w] gets the row's
+// slot count, 0 when the row has no private position (nothing to count).
+template <int D>
+__device__ __forceinline__ void packed_private(const DecodeArgs& a, const SharedArgs& sa,
+                                               int* s_slots, const int32_t* tables,
+                                               const PoolView& pv0, int h, int row0, int nrows,
+                                               int part_tokens, int wave, int lane, int n, int g) {
+  constexpr int KK = D / 32;
+  constexpr int MT = D / 16;
+  constexpr int CH = 32;
+  const int G = a.G;
+  const int r = row0 + wave;
+  int T = 0, pb = 0, ps = -1;
+  if (wave < nrows) {
+    T = a.seq_lens[r];
+    pb = sa.row_private[2 * r];
+    ps = sa.row_private[2 * r + 1];
+  }
+  const bool work = wave < nrows && pb >= 0 && pb < T && ps >= 0 && ps < a.n_parts;
+  const int ns = work ? min(ps + (T - pb + part_tokens - 1) / part_tokens, a.n_parts) : 0;
+  if (lane == 0 && wave < nrows) s_slots[wave] = ns;
+  if (!work) return;
+
+  PoolView pv = pv0;
+  pv.trow = (table_t*)(tables + (int64_t)r * pv0.max_blocks);
+  const int ncols[1] = {G};
+  u32x4 qraw[1][KK];
+  u32x4 kf[2][KK];
+  u32x4 vf[MT];
+  {
+    int64_t pb0, pb1;
+    chunk_blocks(pv, pb, pb0, pb1);
+    if (pb + 16 >= T) pb1 = pb0;  // no block past the row's last one is read
+    const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
+                           ((int64_t)r * a.num_q_heads + (int64_t)h * G + (n < G ? n : 0)) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      qraw[0][kk] = *reinterpret_cast<const u32x4*>(qrow + 32 * kk + 8 * g);
+    __builtin_amdgcn_sched_barrier(0);
+    load_k<D>(kf, pv, h, pb, pb0, pb1, n, g, T);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v<D>(vf, pv, h, pb, pb0, pb1, n, g);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  bf16x8 qf[1][KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qf[0][kk] = __builtin_bit_cast(bf16x8, n < G ? qraw[0][kk] : u32x4{0u, 0u, 0u, 0u});
+  float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
+  f32x4 acc[1][MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[0][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int n_w = (T - pb + CH - 1) / CH;
+  int t0 = pb;
+  for (int it = 0; it < n_w; ++it, t0 += CH) {
+    const bool more = it + 1 < n_w;
+    chunk_step_nt<D, 1>(pv, h, t0, more ? t0 + CH : t0, T, ncols, a.scale_log2, qf, kf, vf, m_run,
+                        l_run, acc, n, g, more);
+  }
+  float L = l_run[0] + __shfl_xor(l_run[0], 16, 64);
+  L += __shfl_xor(L, 32, 64);
+  const float M = m_run[0];
+  if (n >= G) return;
+  const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
+  if (ns == 1) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+      *reinterpret_cast<f32x4*>(a.out + row * D + 16 * mt + 4 * g) = acc[0][mt] * inv;
+    if (a.lse && g == 0) a.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+  } else {
+    const int64_t prow = row * a.n_parts + ps;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) st_state(a.ws_u + prow * D + 16 * mt + 4 * g + i, acc[0][mt][i]);
+    if (g == 0) {
+      st_state(a.ws_ml + prow * 2 + 0, M);
+      st_state(a.ws_ml + prow * 2 + 1, L);
+    }
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
@@ -1359,10 +1449,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   const int G = a.G;
   const int rpt = 16 / G;  // rows per 16-column tile
 
-  int row0, nrows, tb, te, slot, tiles;
+  int row0, nrows, tb = 0, te = 0, slot = 0, tiles = 1;
+  bool packed = false;
   if ((int)blockIdx.z < sa.nz_items) {
     const int fa = blockIdx.y + gridDim.y * blockIdx.z;
-    if (fa >= sa.n_items) return;
+    if (fa >= sa.n_items + sa.n_packed) return;
+    packed = fa >= sa.n_items;
+  }
+  if (packed) {
+    // Four rows' private ranges, one wave each (after the items, same planes).
+    row0 = 4 * (blockIdx.y + gridDim.y * blockIdx.z - sa.n_items);
+    nrows = min(4, a.batch - row0);
+  } else if ((int)blockIdx.z < sa.nz_items) {
+    const int fa = blockIdx.y + gridDim.y * blockIdx.z;
     item_t* it = (item_t*)(sa.items + (int64_t)kItemInts * fa);
     row0 = it[0];
     nrows = it[1];
@@ -1393,7 +1492,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   // Length and private range of the item's rows: requested now, used after
   // the loop (slot counts), so the loads wait in flight meanwhile.
   int rT = 0, rpb = 0, rps = 0;
-  if ((int)threadIdx.x < nrows) {
+  if (!packed && (int)threadIdx.x < nrows) {
     const int rr = row0 + threadIdx.x;
     rT = seq_lens[rr];
     rpb = sa.row_private[2 * rr];
@@ -1403,7 +1502,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   const PoolView pv{(table_t*)(tables + (int64_t)row0 * max_blocks),
                     static_cast<const uint16_t*>(kbase), static_cast<const uint16_t*>(vbase),
                     k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P, a.split_log2};
-  if (tiles >= 2)
+  if (packed)
+    packed_private<D>(a, sa, s_slots, tables, pv, h, row0, nrows, part_tokens, wave, lane, n, g);
+  else if (tiles >= 2)
     shared_item<D, 2>(a, st, s_slots, pv, h, row0, nrows, tb, te, tiles, slot, rT, rpb, rps,
                       part_tokens, wave, n, g);
   else

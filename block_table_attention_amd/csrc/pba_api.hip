@@ -263,7 +263,7 @@ bool copy_to_host(std::vector<T>& dst, const T* src, int64_t n, hipStream_t stre
 
 extern "C" {
 
-int pba_version(void) { return 300; }
+int pba_version(void) { return 400; }
 
 int pba_set_validate(int on) { return g_validate.exchange(on ? 1 : 0); }
 
@@ -731,22 +731,32 @@ namespace {
 // in validate mode only).
 int check_shared_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
                       int32_t max_blocks, const pba_shared_plan* plan, int32_t* nz_items,
-                      int32_t* private_parts) {
+                      int32_t* private_parts, int32_t* n_packed = nullptr) {
   if (!plan) return PBA_ERR_NULL_ARG;
   if (pool->dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
-  if (plan->private_parts < 0 || plan->num_items < 0 || plan->max_slots < 1) return PBA_ERR_BAD_SHAPE;
+  if (plan->private_parts < 0 || plan->num_items < 0 || plan->max_slots < 1 ||
+      plan->private_tokens < 0 || plan->reserved0 != 0)
+    return PBA_ERR_BAD_SHAPE;
   const int32_t pt = plan->partition_tokens;
   if (pt <= 0 || pt % kPartGranule) return PBA_ERR_UNSUPPORTED;
   if (batch > 65535) return PBA_ERR_UNSUPPORTED;
   if (batch > 0 && (!plan->row_private || (plan->num_items > 0 && !plan->items)))
     return PBA_ERR_NULL_ARG;
   const int64_t max_T = (int64_t)max_blocks * pool->block_size;
-  const int64_t pp = plan->private_parts > 0 ? plan->private_parts : (max_T + pt - 1) / pt;
-  const int64_t nz = batch > 0 ? ((int64_t)plan->num_items + batch - 1) / batch : 0;
+  // Short private ranges go four rows per work-group, in the items' planes;
+  // otherwise each private piece has a work-group of its own, one plane per
+  // piece index.
+  const bool packed = plan->private_tokens > 0 && plan->private_tokens <= pba::kPackedPrivateTokens;
+  const int64_t npk = packed ? ((int64_t)batch + 3) / 4 : 0;
+  const int64_t pp = packed                   ? 0
+                     : plan->private_parts > 0 ? plan->private_parts
+                                               : (max_T + pt - 1) / pt;
+  const int64_t nz = batch > 0 ? ((int64_t)plan->num_items + npk + batch - 1) / batch : 0;
   if (pp + nz > 65535) return PBA_ERR_UNSUPPORTED;
   if ((int64_t)batch * num_q_heads > INT32_MAX) return PBA_ERR_UNSUPPORTED;
   *nz_items = (int32_t)nz;
   *private_parts = (int32_t)pp;
+  if (n_packed) *n_packed = (int32_t)npk;
   return PBA_OK;
 }
 
@@ -797,6 +807,7 @@ int validate_shared_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t b
       slots[r].push_back(ps + k);
     }
     if (plan->private_parts > 0 && k > plan->private_parts) return PBA_ERR_OUT_OF_RANGE;
+    if (plan->private_tokens > 0 && T - pb > plan->private_tokens) return PBA_ERR_OUT_OF_RANGE;
     std::sort(spans[r].begin(), spans[r].end());
     int64_t at = 0;
     for (const auto& sp : spans[r]) {
@@ -835,8 +846,8 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
                             size_t workspace_bytes, void* stream) {
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
-  int32_t nz = 0, pp = 0;
-  st = check_shared_plan(pool, num_q_heads, batch, max_blocks_per_seq, plan, &nz, &pp);
+  int32_t nz = 0, pp = 0, npk = 0;
+  st = check_shared_plan(pool, num_q_heads, batch, max_blocks_per_seq, plan, &nz, &pp, &npk);
   if (st) return st;
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
@@ -897,6 +908,7 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
   sa.items = plan->items;
   sa.row_private = plan->row_private;
   sa.n_items = plan->num_items;
+  sa.n_packed = npk;
   sa.nz_items = nz;
   return pba::launch_paged_decode_shared(a, sa, pool->head_dim, (int)pp, s) == hipSuccess
              ? PBA_OK

@@ -75,8 +75,13 @@ struct SharedArgs {
   const int32_t* items;
   const int32_t* row_private;  // [batch][2]
   int32_t n_items;
-  int32_t nz_items;  // grid z planes of chunk-first items: ceil(n_items / batch)
+  int32_t n_packed;  // work-groups of four rows' private ranges after the items (0: none)
+  int32_t nz_items;  // grid z planes of items and packed groups: ceil((n_items + n_packed) / batch)
 };
+
+// Private ranges of at most this many positions (four 32-token chunks) are
+// walked one wave per row, four rows per work-group.
+constexpr int kPackedPrivateTokens = 128;
 
 // Balanced decode: partial states of segments cut by work-group range
 // boundaries, two slots per work-group ([slots][G][2], [slots][G][D]).

@@ -348,7 +348,8 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
  * Contract (checked in validate mode, PBA_ERR_OUT_OF_RANGE / PBA_ERR_OVERLAP):
  * for every row the item ranges covering it and its private pieces tile
  * [0, T) exactly, its slots are exactly 0 .. n-1 with n <= max_slots, its
- * private pieces number at most private_parts (when that is nonzero); tb
+ * private pieces number at most private_parts (when that is nonzero) and its
+ * private positions T - pb at most private_tokens (when that is nonzero); tb
  * and pb are multiples of min(P, 32); te <= T of every covered row; every
  * covered row maps blocks [tb/P, ceil(te/P)) to the same ids as row0.  Outside
  * validate mode a plan that breaks the contract gives undefined results but
@@ -365,6 +366,12 @@ typedef struct pba_shared_plan {
                                 partition_tokens); 0: from the table width */
   const int32_t* items;
   const int32_t* row_private;
+  int32_t private_tokens;    /* bound on any row's private positions T - pb; 0:
+                                none given.  At most 128 (four 32-token chunks):
+                                four rows' private ranges share a work-group,
+                                one wave each, instead of a work-group per
+                                private piece */
+  int32_t reserved0;         /* 0 */
 } pba_shared_plan;
 
 /* Workspace bytes pba_paged_decode_shared needs (0 when max_slots == 1);

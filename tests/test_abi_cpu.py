@@ -23,7 +23,7 @@ def test_header_symbols_exported():
     assert declared == sorted(pba.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert pba.version() == 300
+    assert pba.version() == 400
 
 
 def _desc(**kw):
@@ -275,8 +275,10 @@ def test_shared_decode_host_rejections():
     d = _desc()
     items, rowp = 0x90000, 0xA0000
 
-    def plan(num_items=2, max_slots=3, pt=256, private_parts=0, it=items, rp=rowp):
-        return pba.SharedPlanDesc(num_items, max_slots, pt, private_parts, it, rp)
+    def plan(num_items=2, max_slots=3, pt=256, private_parts=0, it=items, rp=rowp,
+             private_tokens=0, reserved0=0):
+        return pba.SharedPlanDesc(num_items, max_slots, pt, private_parts, it, rp,
+                                  private_tokens, reserved0)
 
     def call(desc, p, ws=0x80000, wsb=1 << 30, batch=2, q=0x30000):
         return lib.pba_paged_decode_shared(ctypes.byref(desc), q, 8, 0x40000, 4, 0x50000, batch,
@@ -290,6 +292,8 @@ def test_shared_decode_host_rejections():
     assert call(d, plan(private_parts=-1)) == -3
     assert call(d, plan(max_slots=0)) == -3
     assert call(d, plan(num_items=-1)) == -3
+    assert call(d, plan(private_tokens=-1)) == -3
+    assert call(d, plan(reserved0=1)) == -3
     assert call(d, plan(it=None)) == -1
     assert call(d, plan(rp=None)) == -1
     assert call(d, plan(), batch=70000) == -4
@@ -302,6 +306,10 @@ def test_shared_decode_host_rejections():
     assert call(d, plan(), wsb=need - 1) == -5
     assert lib.pba_paged_decode_shared_workspace_bytes(
         ctypes.byref(d), 8, 2, 4, ctypes.byref(plan(max_slots=1))) == 0
+    # Short private ranges (packed four rows per work-group) need the same workspace.
+    for ptok in (1, 128, 129):
+        assert lib.pba_paged_decode_shared_workspace_bytes(
+            ctypes.byref(d), 8, 2, 4, ctypes.byref(plan(private_tokens=ptok))) == need
     assert lib.pba_paged_decode_shared_workspace_bytes(
         ctypes.byref(_desc(dtype=0)), 8, 2, 4, ctypes.byref(plan())) == 0
     assert call(d, plan(), q=0x30008) == -4

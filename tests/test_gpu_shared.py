@@ -52,12 +52,18 @@ def prepare(w, device):
     return opool, pool, tables, lens, qb
 
 
-def run_shared(pba, w, device, pt=256, threshold=1, check_plain=True, tiles=4):
-    say(w.name, w.shape, "seed", w.seed, "pt", pt, "threshold", threshold, "tiles", tiles)
+def run_shared(pba, w, device, pt=256, threshold=1, check_plain=True, tiles=4, packed=True):
+    """packed=False drops the plan's private-range bound, so every private
+    piece gets a work-group of its own; with it, ranges of at most 128
+    positions go four rows per work-group."""
+    say(w.name, w.shape, "seed", w.seed, "pt", pt, "threshold", threshold, "tiles", tiles,
+        "packed", packed)
     opool, pool, tables, lens, qb = prepare(w, device)
     P, Hkv = w.shape.block_size, w.shape.num_kv_heads
     G = w.shape.num_q_heads // Hkv
     host = shared_plan(tables, lens, P, G, pt, threshold=threshold, tiles_per_item=tiles)
+    if not packed:
+        host.private_tokens = 0
     plan = pba.SharedPlan.from_host(host, device)
     q = to_device(qb, w.shape.dtype, device)
     tab = torch.from_numpy(tables).to(device)
@@ -69,7 +75,7 @@ def run_shared(pba, w, device, pt=256, threshold=1, check_plain=True, tiles=4):
     err = np.max(np.abs(out.cpu().numpy() - ref))
     lerr = np.max(np.abs(lse.cpu().numpy() - ref_lse))
     say("   chunks", len(host.chunks), "items", host.items.shape[0], "max_slots", host.max_slots,
-        "max err", err, "lse err", lerr)
+        "private_tokens", host.private_tokens, "max err", err, "lse err", lerr)
     assert err <= TOL and lerr <= TOL
     if check_plain:
         out2, _ = pba.paged_decode(pool, q, tab, ln, scale)
@@ -78,10 +84,38 @@ def run_shared(pba, w, device, pt=256, threshold=1, check_plain=True, tiles=4):
     return out, lse, host
 
 
-def test_shared_prefix_workload(pba, gpu):
+@pytest.mark.parametrize("packed", [True, False])
+def test_shared_prefix_workload(pba, gpu, packed):
     """The full shared-prefix workload: 2000-token prefix over 128 rows, child
-    and sibling suffixes shared in pairs, copy-on-write tails."""
-    run_shared(pba, wl.shared_prefix(), gpu)
+    and sibling suffixes shared in pairs, copy-on-write tails (private ranges
+    of one block: packed four rows per work-group, or not)."""
+    run_shared(pba, wl.shared_prefix(), gpu, packed=packed)
+
+
+@pytest.mark.parametrize("G,P,d,batch", [(4, 16, 128, 6), (1, 64, 64, 5), (8, 32, 128, 7),
+                                         (16, 16, 64, 3), (2, 256, 128, 9)])
+def test_packed_private_ranges(pba, gpu, G, P, d, batch):
+    """Private ranges of 1 to 128 positions, four rows per work-group: batches
+    that leave the last group partly filled, rows whose only slot is the
+    private one, rows with no private position, and tail chunks of every
+    length."""
+    rng = np.random.default_rng(20261202 + 7200 + G * 100 + P + batch)
+    Hkv = 2
+    w = wl.Workload(f"packed_g{G}_p{P}_d{d}", wl.Shape(P, G * Hkv, Hkv, d, "bf16", 512),
+                    20261202 + 7200 + G)
+    # Row 0 alone (its only slot is private); the others fork a common
+    # prefix of whole blocks and add tokens of their own (none for the
+    # first, 1..127 for the rest).
+    w.actions = [("new",), ("prefill", 0, int(rng.integers(1, 129))),
+                 ("new",), ("prefill", 1, 2 * P)]
+    leaves = [0]
+    for i in range(batch - 1):
+        w.actions.append(("fork", 1))
+        w.actions.append(("prefill", 2 + i, 0 if i == 0 else int(rng.integers(1, 128))))
+        leaves.append(2 + i)
+    w.decode = leaves
+    _, _, host = run_shared(pba, w, gpu)
+    assert 0 < host.private_tokens <= 128
 
 
 @pytest.mark.parametrize("tiles", [1, 2, 4])
@@ -131,6 +165,7 @@ def test_random_trees(pba, gpu, G, P, d):
     w = _tree_workload(G, P, d, seed=20261202 + 7000 + G * 10 + P)
     for thr in (1, 0):
         run_shared(pba, w, gpu, threshold=thr)
+    run_shared(pba, w, gpu, packed=False)
 
 
 def test_page_tree(pba, gpu):
@@ -205,6 +240,15 @@ def test_validate_mode_rejects_bad_plans(pba, gpu):
     assert attempt(dup, rp) == -7
     bad = it.copy(); bad[0, 2] = -16
     assert attempt(bad, rp) == -6
+    # A private-range bound below a row's private positions.
+    assert host.private_tokens > 1
+    h = type(host)(it, rp, host.max_slots, host.partition_tokens, host.chunks,
+                   host.private_parts, host.private_tokens - 1)
+    out = torch.full(qb.shape, 7.0, device=gpu)
+    with pytest.raises(pba.PBAError) as e:
+        pba.paged_decode_shared(pool, q, tab, ln, pba.SharedPlan.from_host(h, gpu), out=out)
+    torch.cuda.synchronize()
+    assert e.value.status == -6 and (out == 7.0).all()
     # A row whose table differs inside a chunk: swap in another row's tail id.
     assert tables[1, 0] == tables[0, 0]                    # both map the prefix's first block
     tab2 = tables.copy()

@@ -60,6 +60,10 @@ def check_contract(plan, tables, lens, P, G):
         slots = sorted(p[2] for p in pcs)
         assert slots == list(range(len(slots))) and len(slots) <= plan.max_slots
         assert plan.row_private[r, 0] % align == 0
+        assert lens[r] - plan.row_private[r, 0] <= plan.private_tokens
+    # The bound is tight (at least one position: a plan with no private
+    # position still gives a nonzero bound).
+    assert plan.private_tokens == max(1, int(max(lens - plan.row_private[:, 0])))
 
 
 def plan_kv_rows(plan, lens):
@@ -137,6 +141,7 @@ def test_page_tree_from_block_tables():
     assert private.tolist() == [48, 48, 64, 64]
     plan = shared_plan(tables, lens, 16, 1, 256)
     check_contract(plan, tables, lens, 16, 1)
+    assert plan.private_tokens == 32  # s0's 32 private rows; the others have 16
     # Logical pairs 19, unique 10 (in blocks here: 19 and 10 blocks of 16 rows).
     assert int(lens.sum()) // 16 == 19
     assert plan_kv_rows(plan, lens) // 16 == 10
