@@ -244,32 +244,54 @@ def table_ledger(plan: Plan, P: int) -> dict:
             "table_cells_used": int(blocks.sum())}
 
 
+# The sources that decide a decode launch's HBM traffic: the kernels, the
+# library's planner (partition plan, balanced or grid decomposition, workspace
+# layout) and the caller-side helpers that choose the partitions and build the
+# shared-prefix plan.
+DIGEST_SOURCES = ("block_table_attention_amd/csrc/paged_decode.hip",
+                  "block_table_attention_amd/csrc/pba_internal.h",
+                  "block_table_attention_amd/csrc/pba_api.hip",
+                  "block_table_attention_amd/csrc/plan.cpp",
+                  "block_table_attention_amd/blocks.py")
+
+
 def decode_source_digest(root: str = ROOT) -> str:
-    """SHA-256 of the decode kernels' source with comments and whitespace
-    removed: a profile stays valid across edits that change no code."""
+    """SHA-256 of the sources that decide the decode's traffic (DIGEST_SOURCES)
+    with comments and whitespace removed: a profile stays valid across edits
+    that change no code, and any code edit to the kernels or the planners
+    voids it."""
     import hashlib
     import re
 
-    csrc = os.path.join(root, "block_table_attention_amd", "csrc")
-    text = "".join(open(os.path.join(csrc, f)).read() for f in ("paged_decode.hip", "pba_internal.h"))
-    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", " ", text)
-    text = re.sub(r"\s+", " ", text).strip()
-    return hashlib.sha256(text.encode()).hexdigest()
+    parts = []
+    for rel in DIGEST_SOURCES:
+        path = os.path.join(root, rel)
+        if not os.path.exists(path):
+            parts.append(f"<missing {rel}>")
+            continue
+        text = open(path).read()
+        if rel.endswith(".py"):
+            text = re.sub(r"#[^\n]*", " ", text)
+        else:
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
+        parts.append(re.sub(r"\s+", " ", text).strip())
+    return hashlib.sha256("\x00".join(parts).encode()).hexdigest()
 
 
-def profiled_traffic(workload: str):
+def profiled_traffic(workload: str, root: str = ROOT):
     """HBM bytes per decode launch from the committed rocprofv3 summary, or None
-    when there is none for this workload or the decode code changed since."""
+    when there is none for this workload or the decode code or planners changed
+    since."""
     import re
 
-    path = os.path.join(ROOT, "profiles", f"decode_bf16_{workload}.md")
+    path = os.path.join(root, "profiles", f"decode_bf16_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m_t = re.search(r"traffic_bytes_per_launch: (\d+)", text)
     m_h = re.search(r"decode_code_sha256: ([0-9a-f]{64})", text)
-    if not (m_t and m_h) or m_h.group(1) != decode_source_digest():
+    if not (m_t and m_h) or m_h.group(1) != decode_source_digest(root):
         return None
     return int(m_t.group(1))
 
@@ -1000,11 +1022,56 @@ def run_contiguous(args, name, pba, torch, dev):
     return result
 
 
+def host_cpu():
+    """(usable cores, CPU model name) of this host: the cores from the
+    process's affinity mask, the model from lscpu (else /proc/cpuinfo)."""
+    import subprocess
+
+    cores = len(os.sched_getaffinity(0))
+    model = None
+    try:
+        out = subprocess.run(["lscpu"], stdout=subprocess.PIPE, stderr=subprocess.DEVNULL,
+                             text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.split(":")[0].strip() == "Model name":
+                model = line.split(":", 1)[1].strip()
+                break
+    except (OSError, subprocess.SubprocessError):
+        pass
+    if model is None:
+        try:
+            for line in open("/proc/cpuinfo"):
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+        except OSError:
+            pass
+    return cores, model or "unknown"
+
+
+def timed_oracle_rows(run_row, n_rows, seconds, threads):
+    """Whole decode rows of the oracle, in batch order, until about `seconds`
+    have elapsed, with `threads` BLAS threads: (rows done, elapsed s)."""
+    from threadpoolctl import threadpool_limits
+
+    done = 0
+    with threadpool_limits(limits=threads):
+        start = time.perf_counter()
+        r = 0
+        while True:
+            run_row(r)
+            done += 1
+            r = (r + 1) % n_rows
+            if time.perf_counter() - start >= seconds:
+                break
+        el = time.perf_counter() - start
+    return done, el
+
+
 def cpu_baseline_bundle(w, seconds, kv_bytes_total):
     """The CPU oracle on a bounded sample: whole decode rows of layer 0 (a
     single-layer oracle pool of the first group, replayed with that layer's
     rows), scaled to the bytes of every layer."""
-    from threadpoolctl import threadpool_limits
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from harness import execute_bundle
@@ -1029,24 +1096,23 @@ def cpu_baseline_bundle(w, seconds, kv_bytes_total):
     scale = 1.0 / math.sqrt(d)
     print(f"[bench] cpu oracle set-up {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     B = len(w.decode)
-    done = 0
-    with threadpool_limits(limits=1):
-        start = time.perf_counter()
-        r = 0
-        while True:
-            att.paged_decode(pool, qb, list(ex.tables[0]), ex.seq_lens, scale,
-                             rows=[(r, h) for h in range(H)])
-            done += 1
-            r = (r + 1) % B
-            if time.perf_counter() - start >= seconds:
-                break
-        el = time.perf_counter() - start
+    tables0 = list(ex.tables[0])
+
+    def run_row(r):
+        att.paged_decode(pool, qb, tables0, ex.seq_lens, scale, rows=[(r, h) for h in range(H)])
+
+    cores, model = host_cpu()
+    done, el = timed_oracle_rows(run_row, B, seconds, cores)
+    done1, el1 = timed_oracle_rows(run_row, B, seconds / 2, 1)
     per_layer = kv_bytes_total / w.total_layers
-    return {"value": round(per_layer * done / B / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "rows_per_s": round(done / el, 3),
+    return {"value": round(per_layer * done / B / el / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "kind": "oracle", "cpu_model": model, "rows_per_s": round(done / el, 3),
+            "value_1_thread": round(per_layer * done1 / B / el1 / 1e9, 4),
+            "rows_per_s_1_thread": round(done1 / el1, 3),
             "sample": f"{done} whole decode rows of layer 0 (all {w.num_q_heads} q-heads) of the "
-                      f"same workload, binary64 numpy oracle, 1 BLAS thread, {el:.1f}s; bytes "
-                      f"per row scaled to one layer"}
+                      f"same workload, binary64 numpy oracle, {cores} BLAS threads (the host's "
+                      f"usable cores), {el:.1f}s; then {done1} rows with 1 BLAS thread in "
+                      f"{el1:.1f}s; bytes per row scaled to one layer"}
 
 
 def cpu_baseline(w, seconds, kv_bytes_total):
@@ -1054,7 +1120,6 @@ def cpu_baseline(w, seconds, kv_bytes_total):
     workload: whole decode rows (all kv heads), in batch order, until about
     `seconds` have elapsed.  Bytes are the same count as the GPU value, scaled by
     the fraction of the batch done."""
-    from threadpoolctl import threadpool_limits
 
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from harness import execute, oracle_pool
@@ -1071,24 +1136,24 @@ def cpu_baseline(w, seconds, kv_bytes_total):
     print(f"[bench] cpu oracle set-up {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     Hkv = w.shape.num_kv_heads
     B = len(w.decode)
-    done_rows = 0
-    with threadpool_limits(limits=1):
-        start = time.perf_counter()
-        r = 0
-        while True:
-            att.paged_decode(opool, qb, list(ex.tables), ex.seq_lens, scale,
-                             rows=[(r, h) for h in range(Hkv)])
-            done_rows += 1
-            r = (r + 1) % B
-            if time.perf_counter() - start >= seconds:
-                break
-        el = time.perf_counter() - start
+    tables = list(ex.tables)
+
+    def run_row(r):
+        att.paged_decode(opool, qb, tables, ex.seq_lens, scale, rows=[(r, h) for h in range(Hkv)])
+
+    cores, model = host_cpu()
+    done_rows, el = timed_oracle_rows(run_row, B, seconds, cores)
+    done1, el1 = timed_oracle_rows(run_row, B, seconds / 2, 1)
     lens = ex.seq_lens
-    return {"value": round(kv_bytes_total * done_rows / B / el / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "rows_per_s": round(done_rows / el, 3),
+    return {"value": round(kv_bytes_total * done_rows / B / el / 1e9, 4), "unit": "GB/s",
+            "cores": cores, "kind": "oracle", "cpu_model": model,
+            "rows_per_s": round(done_rows / el, 3),
+            "value_1_thread": round(kv_bytes_total * done1 / B / el1 / 1e9, 4),
+            "rows_per_s_1_thread": round(done1 / el1, 3),
             "sample": f"{done_rows} whole decode rows (all {w.shape.num_q_heads} q-heads; contexts "
                       f"{int(lens.min())}..{int(lens.max())}) of the same workload, binary64 numpy "
-                      f"oracle, 1 BLAS thread, {el:.1f}s"}
+                      f"oracle, {cores} BLAS threads (the host's usable cores), {el:.1f}s; then "
+                      f"{done1} rows with 1 BLAS thread in {el1:.1f}s"}
 
 
 def copy_calibration(args, pba, torch, dev):

@@ -11,6 +11,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
+from collections import OrderedDict
 from dataclasses import dataclass
 from typing import Optional, Tuple
 
@@ -267,24 +268,54 @@ def paged_decode_workspace_bytes(pool: KVPool, num_q_heads: int, batch: int,
                                                      max_blocks_per_seq, partition_tokens))
 
 
-_WORKSPACES = {}
+_WORKSPACES: "OrderedDict[tuple, torch.Tensor]" = OrderedDict()
+_WORKSPACE_CACHE_SIZE = 16
+
+
+def _torch_stream(stream, device):
+    if stream is None:
+        return torch.cuda.current_stream(device)
+    return stream
+
+
+def _cached_workspace(device, stream, layout: tuple, need: int) -> torch.Tensor:
+    """A zero-filled workspace of ``need`` bytes for one workspace layout,
+    cached per (device, stream, layout), least recently used first out.
+
+    The layout (entry point, batch, kv heads, q heads, head_dim, partial-state
+    slots) is part of the key: the completion counters occupy the first
+    4 * batch * kv_heads bytes, so two layouts of equal size would otherwise
+    put one call's counters on the other's partial states.  The buffer is
+    allocated and zeroed on the stream the decode runs on, so the zero fill is
+    ordered before the first launch that reads it."""
+    s = _torch_stream(stream, device)
+    key = (str(device), int(s.cuda_stream), layout, need)
+    ws = _WORKSPACES.get(key)
+    if ws is None:
+        with torch.cuda.stream(s):
+            ws = torch.zeros(need, dtype=torch.uint8, device=device)
+        _WORKSPACES[key] = ws
+        while len(_WORKSPACES) > _WORKSPACE_CACHE_SIZE:
+            _WORKSPACES.popitem(last=False)
+    else:
+        _WORKSPACES.move_to_end(key)
+    return ws
 
 
 def decode_workspace(pool: KVPool, num_q_heads: int, batch: int, max_blocks_per_seq: int,
                      partition_tokens: int = 0, stream=None) -> Optional[torch.Tensor]:
-    """A zero-initialised workspace for paged_decode, cached per (device,
-    stream, size).  The library leaves its counters at zero after every call,
-    so one workspace serves every call ordered on that stream."""
+    """A zero-initialised workspace for paged_decode (and its ragged and
+    contiguous forms), cached per (device, stream, layout).  The library
+    leaves its counters at zero after every call, so one workspace serves
+    every call ordered on that stream."""
     need = paged_decode_workspace_bytes(pool, num_q_heads, batch, max_blocks_per_seq,
                                         partition_tokens)
     if need == 0:
         return None
-    key = (pool.device, _stream(stream), need)
-    ws = _WORKSPACES.get(key)
-    if ws is None:
-        ws = torch.zeros(need, dtype=torch.uint8, device=pool.device)
-        _WORKSPACES[key] = ws
-    return ws
+    pt, n_parts = paged_decode_plan(pool, num_q_heads, batch, max_blocks_per_seq,
+                                    partition_tokens)
+    layout = ("decode", batch, pool.num_kv_heads, num_q_heads, pool.head_dim, pt, n_parts)
+    return _cached_workspace(pool.device, stream, layout, need)
 
 
 def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
@@ -402,11 +433,8 @@ def paged_decode_shared(pool: KVPool, q: torch.Tensor, block_tables: torch.Tenso
     if workspace is None and B > 0:
         need = paged_decode_shared_workspace_bytes(pool, Hq, B, max_blocks, plan)
         if need:
-            key = (dev, _stream(stream), need)
-            workspace = _WORKSPACES.get(key)
-            if workspace is None:
-                workspace = torch.zeros(need, dtype=torch.uint8, device=dev)
-                _WORKSPACES[key] = workspace
+            layout = ("shared", B, pool.num_kv_heads, Hq, D, plan.max_slots)
+            workspace = _cached_workspace(dev, stream, layout, need)
     ws_ptr = None if workspace is None else workspace.data_ptr()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("pba_paged_decode_shared", _lib.pba_paged_decode_shared(

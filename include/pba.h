@@ -308,8 +308,23 @@ int pba_expand_block_tables(const int32_t* src, int64_t n_entries, int32_t split
 int pba_pack_block_tables(const int32_t* src, int32_t batch, int32_t width,
                           const int64_t* row_offsets, int32_t* dst, void* stream);
 
-/* Workspace bytes pba_paged_decode needs for these arguments (0 when one
- * partition per row suffices); returns 0 for arguments it would reject. */
+/*
+ * Workspace bytes pba_paged_decode (and its ragged and contiguous forms) needs
+ * for these arguments; 0 when one partition per row suffices, and 0 for
+ * arguments the call would reject.  Host only, no device access.
+ *
+ * The workspace holds what the pages call the partition API's canonical
+ * state of every independently computed key partition of a score row,
+ * (m_p, l_p, u_p) per (request, q-head, partition), until the log-sum-exp
+ * merge combines them ("M5.3", 0x0BA: one score row, disjoint key partitions,
+ * one denominator), plus one completion counter per (request, kv head):
+ *   [int32 counters, batch * num_kv_heads | pad to 256 B]
+ *   [float (m, l), batch * num_q_heads * n_partitions * 2 | pad to 256 B]
+ *   [float u, batch * num_q_heads * n_partitions * head_dim]
+ * (the balanced decomposition holds two work-group partial states per CU in
+ * place of the per-partition ones).  The same arguments always give the same
+ * size and layout.
+ */
 size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_heads,
                                         int32_t batch, int32_t max_blocks_per_seq,
                                         int32_t partition_tokens);
@@ -481,10 +496,19 @@ int pba_paged_decode_contiguous(const pba_kv_pool* pool, const void* q, int32_t 
 /* Static description of a status code. */
 const char* pba_status_string(int status);
 
-/* Validate mode (process wide, default off).  When on, every call first copies
+/*
+ * Validate mode (process wide, default off).  When on, every call first copies
  * its device-resident ids, slots and lengths to the host (synchronising the
- * stream), checks them, and returns PBA_ERR_OUT_OF_RANGE / PBA_ERR_OVERLAP
- * without launching anything if one is bad.  Returns the previous setting. */
+ * stream), checks them, and returns PBA_ERR_OUT_OF_RANGE / PBA_ERR_OVERLAP /
+ * PBA_ERR_HALF_BUNDLE without launching anything if one is bad, so a rejected
+ * call changes no device byte.  This is the pages' rule that every id is
+ * checked against its bound before any byte is touched ("Cache Concepts:
+ * Prefix Matching vs. Storage", "Virtual block placement within a shared
+ * physical plan": ids are validated before any bytes are cleared) and that a
+ * failed or rejected operation leaves the predecessor state unchanged
+ * ("M5.3", 0x05G Failure Lab).  Host-visible arguments are checked in either
+ * mode.  Returns the previous setting.
+ */
 int pba_set_validate(int on);
 
 /* ABI version: major * 10000 + minor * 100 + patch. */

@@ -24,9 +24,24 @@ def test_cpu_baseline_fields():
     w = bench.make_workload("tiny")
     kv = 35 * 64 * 4 * 2  # the tiny workload's K/V bytes (35 fp32 rows of 64, K and V)
     r = bench.cpu_baseline(w, 0.2, kv)
-    assert r["kind"] == "oracle" and r["unit"] == "GB/s" and r["cores"] == 1
+    assert r["kind"] == "oracle" and r["unit"] == "GB/s"
+    assert r["cores"] == len(os.sched_getaffinity(0))
+    assert r["cpu_model"] and r["cpu_model"] != "unknown"
     assert r["value"] > 0 and r["rows_per_s"] > 0
+    assert r["value_1_thread"] > 0 and r["rows_per_s_1_thread"] > 0
     assert "whole decode rows" in r["sample"] and "binary64" in r["sample"]
+
+
+def _digest_tree(tmp):
+    import shutil
+
+    import bench
+
+    for rel in bench.DIGEST_SOURCES:
+        src = os.path.join(ROOT, rel)
+        if os.path.exists(src):
+            os.makedirs(os.path.dirname(os.path.join(tmp, rel)), exist_ok=True)
+            shutil.copy(src, os.path.join(tmp, rel))
 
 
 def test_profile_digest_ignores_comments_only():
@@ -42,13 +57,9 @@ def test_profile_digest_ignores_comments_only():
 
     tmp = tempfile.mkdtemp()
     try:
-        src = os.path.join(ROOT, "block_table_attention_amd", "csrc")
-        dst = os.path.join(tmp, "block_table_attention_amd", "csrc")
-        os.makedirs(dst)
-        for f in ("paged_decode.hip", "pba_internal.h"):
-            shutil.copy(os.path.join(src, f), dst)
+        _digest_tree(tmp)
         base = bench.decode_source_digest(tmp)
-        path = os.path.join(dst, "paged_decode.hip")
+        path = os.path.join(tmp, "block_table_attention_amd", "csrc", "paged_decode.hip")
         text = open(path).read()
         open(path, "w").write("// a note\n/* and a block\n comment */\n" + text.replace("\n", "\n  "))
         assert bench.decode_source_digest(tmp) == base
@@ -60,3 +71,35 @@ def test_profile_digest_ignores_comments_only():
     assert files
     for f in files:
         assert re.search(r"decode_code_sha256: [0-9a-f]{64}", open(f).read()), f
+
+
+def test_planner_edit_voids_profiled_traffic():
+    """The traffic figure of a profile is tied to the planners too: an edit to
+    the library's partition planner or to the caller-side partition helper
+    makes profiled_traffic return None (roofline.traffic null)."""
+    import shutil
+    import tempfile
+
+    import bench
+
+    tmp = tempfile.mkdtemp()
+    try:
+        _digest_tree(tmp)
+        os.makedirs(os.path.join(tmp, "profiles"))
+        prof = os.path.join(tmp, "profiles", "decode_bf16_long16k.md")
+        open(prof, "w").write(f"    traffic_bytes_per_launch: 1234\n"
+                              f"    decode_code_sha256: {bench.decode_source_digest(tmp)}\n")
+        assert bench.profiled_traffic("long16k", tmp) == 1234
+        for rel, edit in (("block_table_attention_amd/csrc/pba_api.hip",
+                           "\nstatic int planner_edit = 2;\n"),
+                          ("block_table_attention_amd/blocks.py", "\nPLANNER_EDIT = 2\n")):
+            path = os.path.join(tmp, rel)
+            text = open(path).read()
+            open(path, "a").write("# a comment only\n" if rel.endswith(".py") else "// a comment only\n")
+            assert bench.profiled_traffic("long16k", tmp) == 1234, rel
+            open(path, "w").write(text + edit)
+            assert bench.profiled_traffic("long16k", tmp) is None, rel
+            open(path, "w").write(text)
+            assert bench.profiled_traffic("long16k", tmp) == 1234, rel
+    finally:
+        shutil.rmtree(tmp)

@@ -3,7 +3,7 @@ the batch's 32-token chunks split evenly over one work-group per CU, pieces of
 cut rows merged by work-group and across work-groups.
 
 * Every small shape (P, d, G; fp32 pools fall back to the grid), the workload
-  batches, and the long-context workloads at full size (sampled rows) match
+  batches, and the long-context workloads at full size (every (request, kv head) pair) match
   the binary64 oracle within 2e-3.
 * Edge cases: one row of one token; fewer chunks than waves; 2048 rows (the
   largest balanced batch); rows much longer than a work-group's range.
@@ -48,12 +48,12 @@ def test_workloads_balanced(pba, gpu, make):
     run_workload(pba, make(), gpu, partition_tokens=BAL)
 
 
-def test_long16k_balanced_sampled(pba, gpu):
-    run_workload(pba, wl.long16k(), gpu, pairs=[(0, 0), (4, 3), (7, 7)], partition_tokens=BAL)
+def test_long16k_balanced_all_pairs(pba, gpu):
+    run_workload(pba, wl.long16k(), gpu, partition_tokens=BAL)
 
 
-def test_long64k_balanced_sampled(pba, gpu):
-    run_workload(pba, wl.long64k(), gpu, pairs=[(0, 1), (0, 7)], partition_tokens=BAL)
+def test_long64k_balanced_all_pairs(pba, gpu):
+    run_workload(pba, wl.long64k(), gpu, partition_tokens=BAL)
 
 
 def test_single_token_row(pba, gpu):
@@ -67,8 +67,7 @@ def test_max_batch_of_short_rows(pba, gpu):
     rng = np.random.default_rng(31)
     lengths = [int(x) for x in rng.integers(1, 91, size=2048)]
     w = small_workload("bf16", 16, 64, 2, 2, lengths, 20261202 + 1600)
-    run_workload(pba, w, gpu, check_pool=False, partition_tokens=BAL,
-                 pairs=[(r, h) for r in range(0, 2048, 37) for h in range(2)])
+    run_workload(pba, w, gpu, check_pool=False, partition_tokens=BAL)
 
 
 def _prepare(w, device):

@@ -1,6 +1,8 @@
 """GPU parity at the workload sizes: batch32, shared prefix with copy-on-write,
 lognormal lengths at P in {16, 64, 256}, and the long-context workloads at full
-size in the launch configuration bench.py times (sampled output rows)."""
+size in the launch configuration bench.py times.  Every (request, kv head)
+pair of every workload is compared with the binary64 oracle (out and lse),
+and the whole pool bit for bit."""
 import pytest
 
 import workloads as wl
@@ -30,14 +32,14 @@ def test_lognormal_block_sizes(pba, gpu, P):
     run_workload(pba, wl.lognormal(P), gpu)
 
 
-def test_long16k_sampled(pba, gpu):
-    w = wl.long16k()
-    pairs = [(0, 0), (3, 5), (7, 7)]
-    run_workload(pba, w, gpu, pairs=pairs)
+def test_long16k_all_pairs(pba, gpu):
+    """8 x 16,384 tokens, 4 partitions of 4096 per (request, kv head), merged
+    in the launch: all 64 pairs against the oracle."""
+    run_workload(pba, wl.long16k(), gpu)
 
 
-def test_long64k_sampled(pba, gpu):
-    w = wl.long64k()
-    run_workload(pba, w, gpu, pairs=[(0, 2), (0, 6)])
+def test_long64k_all_pairs(pba, gpu):
+    """1 x 65,536 tokens, 32 partitions of 2048 per kv head: all 8 kv heads."""
+    run_workload(pba, wl.long64k(), gpu)
 
 
