@@ -18,6 +18,7 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_plan",
+           "paged_decode_noalloc",
            "paged_decode_ragged", "expand_block_tables", "pack_block_tables",
            "paged_decode_shared", "paged_decode_shared_workspace_bytes", "SharedPlan",
            "paged_decode_workspace_bytes", "decode_workspace", "KVGroup", "kv_append_bundle",
@@ -43,7 +44,9 @@ PBA_F32, PBA_BF16 = 0, 1
 STATUS = {0: "PBA_OK", -1: "PBA_ERR_NULL_ARG", -2: "PBA_ERR_BAD_DTYPE", -3: "PBA_ERR_BAD_SHAPE",
           -4: "PBA_ERR_UNSUPPORTED", -5: "PBA_ERR_WORKSPACE_TOO_SMALL",
           -6: "PBA_ERR_OUT_OF_RANGE", -7: "PBA_ERR_OVERLAP", -8: "PBA_ERR_HIP",
-          -9: "PBA_ERR_HALF_BUNDLE", -10: "PBA_ERR_OUT_OF_MEMORY"}
+          -9: "PBA_ERR_HALF_BUNDLE", -10: "PBA_ERR_OUT_OF_MEMORY", -11: "PBA_ERR_SCRATCH_LIMIT"}
+NOALLOC_COUNTER_BYTES = 256 * 1024        # PBA_NOALLOC_COUNTER_BYTES
+NOALLOC_STATE_BYTES = 32 * 1024 * 1024    # PBA_NOALLOC_STATE_BYTES
 MAX_GROUPS = 8
 PARTITIONS_BALANCED = -1   # partition_tokens: balance the batch's chunks over the CUs
 _DTYPES = {torch.float32: PBA_F32, torch.bfloat16: PBA_BF16}
@@ -115,6 +118,8 @@ _SIGS = {
     "pba_vkv_get_ledgers": (ctypes.c_int, [_vp, ctypes.POINTER(VkvLedgers)]),
     "pba_paged_decode_contiguous": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32,
                                                    ctypes.c_float, _vp, _vp, _i32, _vp, _sz, _vp]),
+    "pba_paged_decode_noalloc": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float,
+                                                _vp, _vp, _i32, _vp]),
     "pba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pba_set_validate": (ctypes.c_int, [ctypes.c_int]),
     "pba_version": (ctypes.c_int, []),
@@ -355,6 +360,38 @@ def paged_decode(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
         pool._ref, q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks, seq_lens.data_ptr(), B,
         ctypes.c_float(scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
         partition_tokens, ws_ptr, ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def paged_decode_noalloc(pool: KVPool, q: torch.Tensor, block_tables: torch.Tensor,
+                         seq_lens: torch.Tensor, scale: Optional[float] = None,
+                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                         want_lse: bool = True, partition_tokens: int = 0, stream=None):
+    """paged_decode through the allocation-free entry point: the library's
+    fixed device scratch holds the partial states, so the call allocates no
+    device memory when ``out`` (and ``lse``, if wanted) are given.  Calls on
+    one GPU share that scratch: calls that overlap in time race."""
+    dev = pool.device
+    _require(q, "q", pool.dtype, dev, 3)
+    _require(block_tables, "block_tables", torch.int32, dev, 2)
+    _require(seq_lens, "seq_lens", torch.int32, dev, 1)
+    B, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, block_tables, seq_lens and the pool")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    else:
+        _require(out, "out", torch.float32, dev, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _require(lse, "lse", torch.float32, dev, 2)
+    _check("pba_paged_decode_noalloc", _lib.pba_paged_decode_noalloc(
+        pool._ref, q.data_ptr(), Hq, block_tables.data_ptr(), block_tables.shape[1],
+        seq_lens.data_ptr(), B, ctypes.c_float(scale), out.data_ptr(),
+        None if lse is None else lse.data_ptr(), partition_tokens, _stream(stream)))
     return out, lse
 
 

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libpba.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pba_api.hip", "kv_append.hip", "block_copy.hip", "paged_decode.hip", "tables.hip",
-           "bundle.hip", "vkv.hip"]
+           "bundle.hip", "vkv.hip", "noalloc.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # MFMA accumulators in arch VGPRs: the online-softmax rescale is VALU

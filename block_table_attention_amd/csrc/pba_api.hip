@@ -280,6 +280,8 @@ const char* pba_status_string(int status) {
     case PBA_ERR_HIP: return "HIP runtime error";
     case PBA_ERR_HALF_BUNDLE: return "a token or copy would move some cache groups only";
     case PBA_ERR_OUT_OF_MEMORY: return "no free or reclaimable physical page in the arena";
+    case PBA_ERR_SCRATCH_LIMIT:
+      return "the call needs more than the allocation-free entry point's fixed scratch";
     default: return "unknown status";
   }
 }
@@ -543,15 +545,20 @@ size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_h
                           pool->head_dim).bytes;
 }
 
+}  // extern "C"
+
+namespace pba {
+
 // Dense (row r at r * max_blocks_per_seq), ragged (row r =
 // block_tables[row_offsets[r] .. row_offsets[r + 1])) or contiguous
 // (block_tables = slot index, max_blocks_per_seq = blocks per slot) decode.
-static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
-                       const int32_t* block_tables, const int64_t* row_offsets,
-                       int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch,
-                       float scale, float* out, float* lse, int32_t partition_tokens,
-                       void* workspace, size_t workspace_bytes, void* stream,
-                       int mode = pba::kTablesDense) {
+// The counters and partial states go to the caller's workspace (counters
+// first), or, with `scratch`, to its two fixed regions.
+int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                const int32_t* block_tables, const int64_t* row_offsets,
+                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, float scale,
+                float* out, float* lse, int32_t partition_tokens, void* workspace,
+                size_t workspace_bytes, void* stream, int mode, const ScratchArea* scratch) {
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
   if (mode == pba::kTablesContiguous && pool->dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
@@ -571,8 +578,27 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
   const WsLayout ws = flat ? flat_layout(batch, pool->num_kv_heads, G, pool->head_dim)
                            : workspace_layout(batch, pool->num_kv_heads, rows, np, pool->head_dim);
   const size_t need = ws.bytes;
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return PBA_ERR_WORKSPACE_TOO_SMALL;
+  // Counters, then the (m, l) and u states: at the layout's offsets in the
+  // caller's workspace, or in the scratch's two regions (states from its
+  // state region's start).
+  int32_t* counters = nullptr;
+  float* ws_ml = nullptr;
+  float* ws_u = nullptr;
+  if (need > 0 && scratch) {
+    if ((size_t)batch * pool->num_kv_heads * sizeof(int32_t) > scratch->counter_bytes ||
+        need - ws.ml_off > scratch->state_bytes)
+      return PBA_ERR_SCRATCH_LIMIT;
+    counters = scratch->counters;
+    ws_ml = reinterpret_cast<float*>(scratch->states);
+    ws_u = reinterpret_cast<float*>(scratch->states + (ws.u_off - ws.ml_off));
+  } else if (need > 0) {
+    if (!workspace || workspace_bytes < need || !aligned16(workspace))
+      return PBA_ERR_WORKSPACE_TOO_SMALL;
+    char* wsb = static_cast<char*>(workspace);
+    counters = reinterpret_cast<int32_t*>(wsb);
+    ws_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
+    ws_u = reinterpret_cast<float*>(wsb + ws.u_off);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g_validate.load()) {
     std::vector<int32_t> lens, tab;
@@ -622,10 +648,9 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
   a.seq_lens = seq_lens;
   a.out = out;
   a.lse = lse;
-  char* wsb = static_cast<char*>(workspace);
-  a.counters = need ? reinterpret_cast<int32_t*>(wsb) : nullptr;
-  a.ws_ml = need ? reinterpret_cast<float*>(wsb + ws.ml_off) : nullptr;
-  a.ws_u = need ? reinterpret_cast<float*>(wsb + ws.u_off) : nullptr;
+  a.counters = counters;
+  a.ws_ml = ws_ml;
+  a.ws_u = ws_u;
   a.max_blocks = max_blocks_per_seq;
   a.num_blocks = pool->num_blocks;
   a.split_log2 = pool->split_log2;
@@ -643,8 +668,8 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
   a.scale_log2 = scale * 1.4426950408889634f;
   if (flat) {
     pba::FlatArgs f;
-    f.piece_ml = reinterpret_cast<float*>(wsb + ws.ml_off);
-    f.piece_u = reinterpret_cast<float*>(wsb + ws.u_off);
+    f.piece_ml = ws_ml;
+    f.piece_u = ws_u;
     f.seg_cost = flat_seg_cost(pool->block_size);  // the kernel block
     return pba::launch_paged_decode_flat(a, f, pool->head_dim, flat_workgroups(), s) == hipSuccess
                ? PBA_OK
@@ -654,13 +679,18 @@ static int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_hea
                                                                                   : PBA_ERR_HIP;
 }
 
+}  // namespace pba
+
+extern "C" {
+
 int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
                      const int32_t* block_tables, int32_t max_blocks_per_seq,
                      const int32_t* seq_lens, int32_t batch, float scale, float* out, float* lse,
                      int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                      void* stream) {
-  return decode_impl(pool, q, num_q_heads, block_tables, nullptr, max_blocks_per_seq, seq_lens,
-                     batch, scale, out, lse, partition_tokens, workspace, workspace_bytes, stream);
+  return pba::decode_impl(pool, q, num_q_heads, block_tables, nullptr, max_blocks_per_seq,
+                          seq_lens, batch, scale, out, lse, partition_tokens, workspace,
+                          workspace_bytes, stream, pba::kTablesDense, nullptr);
 }
 
 int pba_paged_decode_ragged(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
@@ -669,9 +699,9 @@ int pba_paged_decode_ragged(const pba_kv_pool* pool, const void* q, int32_t num_
                             float scale, float* out, float* lse, int32_t partition_tokens,
                             void* workspace, size_t workspace_bytes, void* stream) {
   if (batch > 0 && !row_offsets) return PBA_ERR_NULL_ARG;
-  return decode_impl(pool, q, num_q_heads, block_entries, row_offsets, max_blocks_per_seq,
-                     seq_lens, batch, scale, out, lse, partition_tokens, workspace,
-                     workspace_bytes, stream);
+  return pba::decode_impl(pool, q, num_q_heads, block_entries, row_offsets, max_blocks_per_seq,
+                          seq_lens, batch, scale, out, lse, partition_tokens, workspace,
+                          workspace_bytes, stream, pba::kTablesDense, nullptr);
 }
 
 int pba_paged_decode_contiguous(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
@@ -681,9 +711,9 @@ int pba_paged_decode_contiguous(const pba_kv_pool* pool, const void* q, int32_t 
                                 size_t workspace_bytes, void* stream) {
   if (pool && blocks_per_slot > 0 && pool->num_blocks % blocks_per_slot) return PBA_ERR_BAD_SHAPE;
   if (pool && pool->split_log2) return PBA_ERR_UNSUPPORTED;
-  return decode_impl(pool, q, num_q_heads, slot_index, nullptr, blocks_per_slot, seq_lens, batch,
-                     scale, out, lse, partition_tokens, workspace, workspace_bytes, stream,
-                     pba::kTablesContiguous);
+  return pba::decode_impl(pool, q, num_q_heads, slot_index, nullptr, blocks_per_slot, seq_lens,
+                          batch, scale, out, lse, partition_tokens, workspace, workspace_bytes,
+                          stream, pba::kTablesContiguous, nullptr);
 }
 
 int pba_expand_block_tables(const int32_t* src, int64_t n_entries, int32_t split_log2,

@@ -94,6 +94,25 @@ constexpr int kChunkUnits = 8;  // cost of one 32-token chunk on the balancing a
 constexpr int kFlatMaxBatch = 2048;        // rows the balanced decode takes
 constexpr int64_t kFlatMaxLds = 64 * 1024;  // its dynamic LDS, bytes
 
+// The library's own fixed scratch (the allocation-free decode): completion
+// counters in a region of their own, which no call's partial states overlap,
+// so the counters' zero invariant holds across calls of any layout.
+struct ScratchArea {
+  int32_t* counters;
+  size_t counter_bytes;
+  char* states;
+  size_t state_bytes;
+};
+
+// The decode entry points' common host path (argument checks, plan, validate
+// mode, launch).  mode: kTablesDense / kTablesRagged / kTablesContiguous (a
+// dense call with row_offsets is ragged); scratch: nullptr to use `workspace`.
+int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                const int32_t* block_tables, const int64_t* row_offsets,
+                int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, float scale,
+                float* out, float* lse, int32_t partition_tokens, void* workspace,
+                size_t workspace_bytes, void* stream, int mode, const ScratchArea* scratch);
+
 hipError_t launch_paged_decode_flat(const DecodeArgs& a, const FlatArgs& f, int head_dim,
                                     int n_wg, hipStream_t stream);
 hipError_t launch_expand_tables(const int32_t* src, int64_t n_src, int split_log2, int32_t* dst,

@@ -49,8 +49,10 @@ typedef enum pba_status {
   PBA_ERR_HIP = -8,                 /* a HIP runtime call failed               */
   PBA_ERR_HALF_BUNDLE = -9,         /* validate mode: a token or copy list that
                                        would move some cache groups only       */
-  PBA_ERR_OUT_OF_MEMORY = -10       /* contiguous arena: no free or reclaimable
+  PBA_ERR_OUT_OF_MEMORY = -10,      /* contiguous arena: no free or reclaimable
                                        physical page for the request           */
+  PBA_ERR_SCRATCH_LIMIT = -11       /* allocation-free decode: the arguments need
+                                       more than the library's fixed scratch    */
 } pba_status;
 
 typedef enum pba_dtype { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
@@ -328,6 +330,35 @@ int pba_pack_block_tables(const int32_t* src, int32_t batch, int32_t width,
 size_t pba_paged_decode_workspace_bytes(const pba_kv_pool* pool, int32_t num_q_heads,
                                         int32_t batch, int32_t max_blocks_per_seq,
                                         int32_t partition_tokens);
+
+/*
+ * pba_paged_decode_noalloc -- pba_paged_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments and results as
+ * pba_paged_decode (dense block tables, any partition_tokens), without the
+ * workspace: the completion counters and partial states live in a fixed
+ * array of device memory inside the library, PBA_NOALLOC_COUNTER_BYTES of
+ * counters and PBA_NOALLOC_STATE_BYTES of partial states, which every GPU the
+ * library runs on holds until the process ends.  The call allocates nothing:
+ * no hipMalloc, no hipFree, no allocating library routine.  The first call on
+ * a device looks up the array's address there and clears its counters with a
+ * kernel on `stream`; every call leaves them at zero again.
+ *
+ * Limits: batch * num_kv_heads * 4 <= PBA_NOALLOC_COUNTER_BYTES and
+ * pba_paged_decode_workspace_bytes(...) minus its counter part (batch *
+ * num_kv_heads * 4 rounded up to 256) <= PBA_NOALLOC_STATE_BYTES; larger
+ * arguments return PBA_ERR_SCRATCH_LIMIT before anything is launched.
+ * Calls on one GPU share the array: calls that overlap in time on one GPU
+ * (on two streams, or from host threads without ordering) race and give
+ * undefined results.  Validate mode works as for pba_paged_decode (it
+ * copies device ids to host memory and synchronises the stream).
+ */
+#define PBA_NOALLOC_COUNTER_BYTES (256u * 1024u)
+#define PBA_NOALLOC_STATE_BYTES (32u * 1024u * 1024u)
+int pba_paged_decode_noalloc(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                             float* lse, int32_t partition_tokens, void* stream);
 
 /* The partition length (tokens) and count pba_paged_decode would use; returns
  * a pba_status.  Either output pointer may be NULL.  For the balanced

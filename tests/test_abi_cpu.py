@@ -338,3 +338,26 @@ def test_kernel_view_host_rules():
     assert lib.pba_pack_block_tables(NULL, 2, 4, 0x2000, 0x3000, NULL) == -1
     assert lib.pba_paged_decode_ragged(ctypes.byref(view), 0x30000, 8, 0x40000, NULL, 4, 0x50000,
                                        2, ctypes.c_float(0.1), 0x60000, NULL, 0, NULL, 0, NULL) == -1
+
+
+def test_noalloc_limits_rejected_on_the_host():
+    """The allocation-free decode rejects arguments that need more than its
+    fixed scratch (states, then counters) and NULL pointers before it looks
+    up the scratch or launches anything: no GPU is needed to see it."""
+    import block_table_attention_amd as pba
+
+    lib = _lib()
+    d = _desc(num_kv_heads=8, k_stride_block=8 * 16 * 128, v_stride_block=8 * 16 * 128)
+    ws = lib.pba_paged_decode_workspace_bytes(ctypes.byref(d), 64, 64, 2048, 256)
+    assert ws > pba.NOALLOC_STATE_BYTES
+    assert lib.pba_paged_decode_noalloc(ctypes.byref(d), 0x30000, 64, 0x40000, 2048, 0x50000, 64,
+                                        ctypes.c_float(0.1), 0x60000, NULL, 256, NULL) == -11
+    assert 40000 * 8 * 4 > pba.NOALLOC_COUNTER_BYTES
+    assert lib.pba_paged_decode_noalloc(ctypes.byref(d), 0x30000, 8, 0x40000, 32, 0x50000, 40000,
+                                        ctypes.c_float(0.1), 0x60000, NULL, 256, NULL) == -11
+    assert lib.pba_paged_decode_noalloc(ctypes.byref(d), NULL, 8, 0x40000, 64, 0x50000, 4,
+                                        ctypes.c_float(0.1), 0x60000, NULL, 256, NULL) == -1
+    assert lib.pba_paged_decode_noalloc(NULL, 0x30000, 8, 0x40000, 64, 0x50000, 4,
+                                        ctypes.c_float(0.1), 0x60000, NULL, 256, NULL) == -1
+    assert pba.STATUS[-11] == "PBA_ERR_SCRATCH_LIMIT"
+    assert "scratch" in lib.pba_status_string(-11).decode()
