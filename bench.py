@@ -124,6 +124,10 @@ def parse():
                          "the same contiguous layout in one ordinary device allocation")
     ap.add_argument("--page-mib", type=float, default=2.0,
                     help="physical page size of the contiguous arena, MiB")
+    ap.add_argument("--step", default="fused", choices=["fused", "separate"],
+                    help="fused: the step's new tokens are appended by the decode call "
+                         "(paged_decode_append) when each is its row's last position; "
+                         "separate: kv_append, then the decode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache decode timing (kernel traces of the warm launches)")
@@ -369,6 +373,14 @@ def run_workload(args, name, pba, torch, dev):
     copy_dst = torch.from_numpy(plan.step_dst).to(dev)
     qb = wl.q_bits(w)
     B = len(plan.seq_lens)
+    # Fused step: each new token of the step is its decode row's last position
+    # (the appends of a decode step), so the decode call appends them.
+    last_slot = np.array([int(plan.tables[r, (T - 1) // P]) * P + (T - 1) % P
+                          for r, T in enumerate(plan.seq_lens)], dtype=np.int64)
+    row_of_slot = {int(sl): r for r, sl in enumerate(last_slot)}
+    step_row = [row_of_slot.get(int(sl), -1) for sl in plan.step_slots]
+    fusable = (len(plan.step_slots) > 0 and min(step_row) >= 0 and
+               len(set(step_row)) == len(step_row))
     tables, lens_h = plan.tables, plan.seq_lens
     # Shared-prefix execution: the caller orders the batch so rows sharing
     # leading blocks are adjacent and describes the shared chunks.
@@ -434,10 +446,25 @@ def run_workload(args, name, pba, torch, dev):
     # Zero-filled once: the library keeps the completion counters at zero.
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
+    fused = (args.step == "fused" and fusable and host_plan is None and row_offsets is None
+             and not args.decode_only)
+    if fused:
+        ns = np.full(B, -1, dtype=np.int64)
+        ns[step_row] = plan.step_slots
+        new_slots = torch.from_numpy(ns).to(dev)
+        knew = torch.zeros((B, Hkv, d), dtype=tdtype, device=dev)
+        vnew = torch.zeros_like(knew)
+        idx = torch.tensor(step_row, dtype=torch.int64, device=dev)
+        knew[idx] = k_step
+        vnew[idx] = v_step
     torch.cuda.synchronize()
 
     def decode(st=stream):
-        if host_plan is None and row_offsets is not None:
+        if fused:   # the step's call: appends its new tokens again (same bytes, same slots)
+            pba.paged_decode_append(dpool, new_slots, knew, vnew, q, tab_d, lens_d, scale,
+                                    out=out, lse=lse, partition_tokens=req_pt, workspace=ws,
+                                    stream=st)
+        elif host_plan is None and row_offsets is not None:
             pba.paged_decode_ragged(dpool, q, tab_d, row_offsets, lens_d, mb, scale, out=out,
                                     lse=lse, partition_tokens=req_pt, workspace=ws, stream=st)
         elif host_plan is None:
@@ -454,7 +481,8 @@ def run_workload(args, name, pba, torch, dev):
             pba.block_copy(pool, copy_src, copy_dst, stream=st)
             if evs is not None:
                 evs[1].record(st)
-            pba.kv_append(pool, step_slots, k_step, v_step, stream=st)
+            if not fused:
+                pba.kv_append(pool, step_slots, k_step, v_step, stream=st)
         if evs is not None:
             evs[2].record(st)
         decode(st)
@@ -561,9 +589,12 @@ def run_workload(args, name, pba, torch, dev):
                     "private_tokens": host_plan.private_tokens,
                     "private_ranges": "four rows per work-group"
                     if 0 < host_plan.private_tokens <= 128 else "a work-group per piece"},
-                   "step": f"block_copy({len(plan.step_src)} pairs) + kv_append("
-                           f"{len(plan.step_slots)} tokens) + "
-                           f"{'paged_decode_shared' if host_plan is not None else 'paged_decode'}",
+                   "step": f"block_copy({len(plan.step_src)} pairs) + " +
+                           (f"paged_decode_append({len(plan.step_slots)} new tokens appended "
+                            f"in the decode launch)" if fused else
+                            f"kv_append({len(plan.step_slots)} tokens) + "
+                            f"{'paged_decode_shared' if host_plan is not None else 'paged_decode'}"),
+                   "step_fused": fused,
                    "step_launch": "HIP graph replay" if use_graph else "eager"},
         "query_rows_per_s": round(B / (ms_per_step * 1e-3), 1),
         "hbm_peak_frac_step": round(step_kv_gbs / HBM_PEAK_GBS, 4),
@@ -573,11 +604,12 @@ def run_workload(args, name, pba, torch, dev):
         "decode_us_in_step": round(float(dec_ms.mean()) * 1e3, 2),
         "decode_rows_per_s": round(B / (dec_avg_ms * 1e-3), 1),
         "decode_head_rows_per_s": round(B * Hq / (dec_avg_ms * 1e-3), 1),
-        "append_us": round(float(append_ms.mean()) * 1e3, 2),
+        "append_us": None if fused else round(float(append_ms.mean()) * 1e3, 2),
         "copy_us": round(float(copy_ms.mean()) * 1e3, 2),
         # Bytes read + written by the step's append and copy, over their event-timed durations.
-        "append_gbs": round(len(plan.step_slots) * Hkv * d * es * 2 * 2 /
-                            max(float(append_ms.mean()) * 1e-3, 1e-12) / 1e9, 2),
+        "append_gbs": None if fused else
+        round(len(plan.step_slots) * Hkv * d * es * 2 * 2 /
+              max(float(append_ms.mean()) * 1e-3, 1e-12) / 1e9, 2),
         "copy_gbs": round(len(plan.step_src) * Hkv * P * d * es * 2 * 2 /
                           max(float(copy_ms.mean()) * 1e-3, 1e-12) / 1e9, 2),
         "kv_unique_bytes": kv_unique,
@@ -593,7 +625,8 @@ def run_workload(args, name, pba, torch, dev):
                                 "merge fused in)") if host_plan is not None else
                                (f"decode_bf16_flat_kernel<{d}> (balanced chunk ranges, cut rows "
                                 "merged in)" if flat else
-                                f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in)"),
+                                f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in"
+                                + (", the step's appends too)" if fused else ")")),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "_kv_value_bytes": kv_unique,
     }

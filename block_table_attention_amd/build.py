@@ -1,6 +1,8 @@
 """Build libpba.so for gfx950 with hipcc (in-tree, next to this file).
 
-    python -m block_table_attention_amd.build [--asm]
+    python block_table_attention_amd/build.py [--asm]
+
+(run as a script: importing the package would load the library first).
 
 Every HIP source under csrc/ is compiled for gfx950 only.  Packed-FP32 VALU
 instructions are disabled.  ``--asm`` also writes the gfx950 assembly of each

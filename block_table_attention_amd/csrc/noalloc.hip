@@ -84,5 +84,5 @@ extern "C" int pba_paged_decode_noalloc(const pba_kv_pool* pool, const void* q,
   }
   return pba::decode_impl(pool, q, num_q_heads, block_tables, nullptr, max_blocks_per_seq,
                           seq_lens, batch, scale, out, lse, partition_tokens, nullptr, 0, stream,
-                          pba::kTablesDense, &area);
+                          pba::kTablesDense, &area, nullptr);
 }

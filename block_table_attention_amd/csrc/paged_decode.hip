@@ -326,6 +326,127 @@ __device__ __forceinline__ void load_v(u32x4 (&vf)[D / 16], const PoolView& pv, 
     vf[mt] = *reinterpret_cast<const u32x4*>(vp + (int64_t)(16 * mt) * Pa);
 }
 
+// Fused append: the wave that reads a row's last position T - 1 writes the
+// step's new token there first (the kv_append of one token per row), so the
+// decode of that row reads it in the same launch.  Lanes 0 .. D/8 - 1 hold
+// 16 bytes of the K row each, every lane two scalars of the V row (dims
+// 2 lane, 2 lane + 1); they are loaded when the wave starts and stored just
+// before the wave prefetches the chunk holding T - 1.  The address is the
+// caller's slot, which the contract makes the row's position T - 1 through
+// its table (validate mode checks it), so the stores hit the bytes that
+// chunk's loads read; a wavefront-scope release/acquire orders the stores of
+// some lanes before the loads of others (the wave's memory operations are
+// performed in order, so the fences need no instruction).
+struct NewToken {
+  u32x4 k;      // 8 K scalars (lanes < D / 8)
+  uint32_t v;   // 2 V scalars
+  int64_t slot;
+};
+
+template <int D>
+__device__ __forceinline__ void load_new_token(NewToken& nt, const DecodeArgs& a, int r, int h,
+                                               int lane) {
+  const int64_t row = ((int64_t)r * a.num_kv_heads + h) * D;
+  const uint16_t* kn = static_cast<const uint16_t*>(a.k_new) + row;
+  const uint16_t* vn = static_cast<const uint16_t*>(a.v_new) + row;
+  if (lane < D / 8) nt.k = *reinterpret_cast<const u32x4*>(kn + 8 * lane);
+  if (lane < D / 2) nt.v = *reinterpret_cast<const uint32_t*>(vn + 2 * lane);
+}
+
+template <int D>
+__device__ __forceinline__ void store_new_token(const NewToken& nt, const PoolView& pv, int h,
+                                                int lane) {
+  const int P = 1 << pv.log2P;
+  const int64_t pb = nt.slot >> pv.log2P;  // kernel block of the slot
+  const int off = row_of(pv, pb) + (int)(nt.slot & (P - 1));
+  uint16_t* kp = const_cast<uint16_t*>(pv.k) + tile_of(pv, pb) * pv.k_sb + (int64_t)h * pv.k_sh +
+                 (int64_t)off * D;
+  const int Pa = P << pv.split;
+  uint16_t* vp = const_cast<uint16_t*>(pv.v) + tile_of(pv, pb) * pv.v_sb + (int64_t)h * pv.v_sh + off;
+  if (lane < D / 8) *reinterpret_cast<u32x4*>(kp + 8 * lane) = nt.k;
+  if (lane < D / 2) {
+    vp[(int64_t)(2 * lane) * Pa] = (uint16_t)(nt.v & 0xFFFFu);
+    vp[(int64_t)(2 * lane + 1) * Pa] = (uint16_t)(nt.v >> 16);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// The running maximum moves only when a chunk's maximum exceeds it by more
+// than this many log2 units, so probabilities stay below 2^kRescaleSlack and
+// the accumulators are rescaled (a multiply per accumulator) only a few times
+// per row instead of whenever the maximum grows.  Every (m, l, u) state keeps
+// l and u relative to its own m, so merges are unaffected.
+constexpr float kRescaleSlack = 8.f;
+
+// Scores enter the softmax unscaled and |scale| * log2(e) is folded into the
+// exponent (one fma per score).  A negative scale is carried by the queries:
+// their bf16 sign bits are flipped when they are loaded.
+__device__ __forceinline__ float abs_scale(float scale_log2) { return fabsf(scale_log2); }
+__device__ __forceinline__ uint32_t q_sign_mask(float scale_log2) {
+  return scale_log2 < 0.f ? 0x80008000u : 0u;
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// Online-softmax update of one 16-column tile over a 32-token chunk.  s holds
+// this lane's raw scores: tokens tbase + 4 at + i (tbase = t0 + 8 g) of
+// column n.  In a tail chunk (tail = true) tokens at or past t_end are
+// removed; columns without a query (zero q, padding) are computed like the
+// others and never stored.  Returns the probabilities as the B operand of
+// the value product, split p = hi + lo into two bf16 parts (~16 significant
+// bits).
+template <int MT>
+__device__ __forceinline__ void softmax_tile(const f32x4 (&s)[2], bool tail, int tbase, int t_end,
+                                             float sl, float& m_run, float& l_run,
+                                             f32x4 (&acc)[MT], bf16x8& phi, bf16x8& plo) {
+  float x[8];
+#pragma unroll
+  for (int at = 0; at < 2; ++at)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[4 * at + i] = s[at][i];
+  if (tail) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[j] = (tbase + j < t_end) ? x[j] : -INFINITY;
+  }
+  float cmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])),
+                     fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
+  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
+  const float cm = cmax * sl;
+  if (__any(cm > m_run + kRescaleSlack)) {  // the first chunk always takes this
+    const float m_new = fmaxf(m_run, cm);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
+  }
+  const float nm = -m_run;
+  float p[8];
+  float psum = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    p[j] = fast_exp2(fmaf(x[j], sl, nm));
+    psum += p[j];
+  }
+  l_run += psum;
+  u32x4 hi, lo;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    hi[q] = pack_bf16(p[2 * q], p[2 * q + 1]);
+    const float h0 = __uint_as_float(hi[q] << 16);
+    const float h1 = __uint_as_float(hi[q] & 0xFFFF0000u);
+    lo[q] = pack_bf16(p[2 * q] - h0, p[2 * q + 1] - h1);
+  }
+  phi = __builtin_bit_cast(bf16x8, hi);
+  plo = __builtin_bit_cast(bf16x8, lo);
+}
+
 // One 32-token chunk of a wave: the score product over its K fragments, the
 // online-softmax update of (m_run, l_run), the value product into acc, and
 // the loads of the wave's next chunk tn, each issued as soon as the registers
@@ -374,47 +495,12 @@ __device__ __forceinline__ void chunk_step(const PoolView& pv, int h, int t0, in
   if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g, tn_end);
 
   const int tbase = t0 + 8 * g;  // token of k-slot j = 0 of this lane
-  float x[8];
-#pragma unroll
-  for (int at = 0; at < 2; ++at)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int j = 4 * at + i;
-      const float v = s[at][i] * scale_log2;
-      x[j] = (tbase + j < t_end) ? v : -INFINITY;
-    }
-  float cmax = x[0];
-#pragma unroll
-  for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-  cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-  const float m_new = fmaxf(m_run, cmax);
-  const float alpha = fast_exp2(m_run - m_new);
-  m_run = m_new;
-
-  float p[8];
-  float psum = 0.f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    p[j] = (n < ncols) ? fast_exp2(x[j] - m_new) : 0.f;
-    psum += p[j];
-  }
-  l_run = l_run * alpha + psum;
-  if (__any(alpha != 1.f)) {
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[mt] *= alpha;
-  }
-
+  const bool tail = t0 + CH > t_end;  // wave uniform
   bf16x8 phi, plo;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const __bf16 hi = (__bf16)p[j];
-    phi[j] = hi;
-    plo[j] = (__bf16)(p[j] - (float)hi);
-  }
+  softmax_tile<MT>(s, tail, tbase, t_end, scale_log2, m_run, l_run, acc, phi, plo);
 
   // Tail chunk: zero the V scalars of tokens >= t_end (they may hold NaN).
-  if (t0 + CH > t_end) {
+  if (tail) {
     const int cnt = t_end - tbase;  // valid tokens among this lane's 8
     u32x4 mask;
 #pragma unroll
@@ -513,6 +599,24 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
   // This wave's chunks: p_begin + wave*CH + k*kWaves*CH for k < n_w.
   const int span = p_end - p_begin - wave * CH;
   const int n_w = span > 0 ? (span + kWaves * CH - 1) / (kWaves * CH) : 0;
+  // Fused append: this wave writes the row's new token if it reads T - 1,
+  // before prefetching the chunk that holds it (t_new).
+  NewToken nt;
+  nt.slot = -1;
+  int t_new = -1;
+  if (a.new_slots && p_end == T) {
+    const int64_t slot = ((const int64_t __attribute__((address_space(4)))*)a.new_slots)[r];
+    const int c_new = (T - 1 - p_begin) / CH;
+    if (slot >= 0 && c_new % kWaves == wave) {
+      nt.slot = slot;
+      t_new = p_begin + c_new * CH;
+    }
+  }
+  if (t_new == t0) {  // the wave's first chunk: write before its first loads
+    load_new_token<D>(nt, a, r, h, lane);
+    store_new_token<D>(nt, pv, h, lane);
+    t_new = -1;
+  }
 
   u32x4 qraw[KK];
   u32x4 kf[2][KK];
@@ -530,12 +634,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     load_v<D>(vf, pv, h, t0, pb0, pb1, n, g);
     __builtin_amdgcn_sched_barrier(0);
   }
+  if (t_new >= 0) load_new_token<D>(nt, a, r, h, lane);
   // Padding heads (n >= G) get zero queries; applied after every first load
   // is in flight.
+  const uint32_t qs = q_sign_mask(a.scale_log2);
   bf16x8 qf[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    qf[kk] = __builtin_bit_cast(bf16x8, n < G ? qraw[kk] : u32x4{0u, 0u, 0u, 0u});
+    qf[kk] = __builtin_bit_cast(bf16x8, (n < G ? qraw[kk] : u32x4{0u, 0u, 0u, 0u}) ^ qs);
 
   float m_run = -INFINITY;  // running max (log2 domain) of head n
   float l_run = 0.f;        // this lane's share of the running sum
@@ -547,7 +653,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_kernel(
     // Next chunk of this wave (none after the last).
     const bool more = it + 1 < n_w;
     const int tn = more ? t0 + kWaves * CH : t0;
-    chunk_step<D, IMPLICIT>(pv, h, t0, tn, T, T, G, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n,
+    if (tn == t_new && more) store_new_token<D>(nt, pv, h, lane);
+    chunk_step<D, IMPLICIT>(pv, h, t0, tn, T, T, G, abs_scale(a.scale_log2), qf, kf, vf, m_run, l_run, acc, n,
                             g, more);
   }
 
@@ -895,10 +1002,11 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    const uint32_t qs = q_sign_mask(a.scale_log2);
     bf16x8 qf[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[kk] = __builtin_bit_cast(bf16x8, n < G ? qraw[kk] : u32x4{0u, 0u, 0u, 0u});
+      qf[kk] = __builtin_bit_cast(bf16x8, (n < G ? qraw[kk] : u32x4{0u, 0u, 0u, 0u}) ^ qs);
 
     float m_run = -INFINITY;
     float l_run = 0.f;
@@ -943,7 +1051,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
         vmode = 1;
         have2 = true;
       }
-      chunk_step<D, IMPLICIT>(pvn, h2, k * CH, k2 * CH, T, T2, G, a.scale_log2, qf, kf, vf,
+      chunk_step<D, IMPLICIT>(pvn, h2, k * CH, k2 * CH, T, T2, G, abs_scale(a.scale_log2), qf, kf, vf,
                               m_run, l_run, acc, n, g, !last, &vf2, vmode);
       if (seg_end) {
         float l_tot = l_run + __shfl_xor(l_run, 16, 64);
@@ -984,7 +1092,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
       if (new_seg) {
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          qf[kk] = __builtin_bit_cast(bf16x8, n < G ? qnext[kk] : u32x4{0u, 0u, 0u, 0u});
+          qf[kk] = __builtin_bit_cast(bf16x8, (n < G ? qnext[kk] : u32x4{0u, 0u, 0u, 0u}) ^ qs);
       }
       if (r2 != r) pv = pvn;
       r = r2;
@@ -1151,47 +1259,15 @@ __device__ __forceinline__ void chunk_step_nt(const PoolView& pv, int h, int t0,
   if (pf) load_k<D>(kf, pv, h, tn, nb0, nb1, n, g, t_end);
 
   const int tbase = t0 + 8 * g;
+  const bool tail = t0 + CH > t_end;  // wave uniform
   bf16x8 phi[NT], plo[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float x[8];
-#pragma unroll
-    for (int at = 0; at < 2; ++at)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * at + i;
-        x[j] = (tbase + j < t_end) ? s[t][at][i] * scale_log2 : -INFINITY;
-      }
-    float cmax = x[0];
-#pragma unroll
-    for (int j = 1; j < 8; ++j) cmax = fmaxf(cmax, x[j]);
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16, 64));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32, 64));
-    const float m_new = fmaxf(m_run[t], cmax);
-    const float alpha = fast_exp2(m_run[t] - m_new);
-    m_run[t] = m_new;
-    float p[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      p[j] = (n < ncols[t]) ? fast_exp2(x[j] - m_new) : 0.f;
-      psum += p[j];
-    }
-    l_run[t] = l_run[t] * alpha + psum;
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[t][mt] *= alpha;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 hi = (__bf16)p[j];
-      phi[t][j] = hi;
-      plo[t][j] = (__bf16)(p[j] - (float)hi);
-    }
-  }
+  for (int t = 0; t < NT; ++t)
+    softmax_tile<MT>(s[t], tail, tbase, t_end, scale_log2, m_run[t], l_run[t], acc[t], phi[t],
+                     plo[t]);
 
   // Tail chunk: zero the V scalars of tokens >= t_end (they may hold NaN).
-  if (t0 + CH > t_end) {
+  if (tail) {
     const int cnt = t_end - tbase;
     u32x4 mask;
 #pragma unroll
@@ -1272,7 +1348,8 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
   for (int j = 0; j < NT; ++j) {
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      qf[j][kk] = __builtin_bit_cast(bf16x8, n < ncols[j] ? qraw[j][kk] : u32x4{0u, 0u, 0u, 0u});
+      qf[j][kk] = __builtin_bit_cast(bf16x8, (n < ncols[j] ? qraw[j][kk] : u32x4{0u, 0u, 0u, 0u}) ^
+                                                 q_sign_mask(a.scale_log2));
     m_run[j] = -INFINITY;
     l_run[j] = 0.f;
 #pragma unroll
@@ -1281,7 +1358,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
   for (int it = 0; it < n_w; ++it, t0 += stride) {
     const bool more = it + 1 < n_w;
     const int tn = more ? t0 + stride : t0;
-    chunk_step_nt<D, NT>(pv, h, t0, tn, te, ncols, a.scale_log2, qf, kf, vf, m_run, l_run, acc, n,
+    chunk_step_nt<D, NT>(pv, h, t0, tn, te, ncols, abs_scale(a.scale_log2), qf, kf, vf, m_run, l_run, acc, n,
                          g, more);
   }
 #pragma unroll
@@ -1401,7 +1478,8 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
   bf16x8 qf[1][KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
-    qf[0][kk] = __builtin_bit_cast(bf16x8, n < G ? qraw[0][kk] : u32x4{0u, 0u, 0u, 0u});
+    qf[0][kk] = __builtin_bit_cast(bf16x8, (n < G ? qraw[0][kk] : u32x4{0u, 0u, 0u, 0u}) ^
+                                               q_sign_mask(a.scale_log2));
   float m_run[1] = {-INFINITY}, l_run[1] = {0.f};
   f32x4 acc[1][MT];
 #pragma unroll
@@ -1410,8 +1488,8 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
   int t0 = pb;
   for (int it = 0; it < n_w; ++it, t0 += CH) {
     const bool more = it + 1 < n_w;
-    chunk_step_nt<D, 1>(pv, h, t0, more ? t0 + CH : t0, T, ncols, a.scale_log2, qf, kf, vf, m_run,
-                        l_run, acc, n, g, more);
+    chunk_step_nt<D, 1>(pv, h, t0, more ? t0 + CH : t0, T, ncols, abs_scale(a.scale_log2), qf, kf,
+                        vf, m_run, l_run, acc, n, g, more);
   }
   float L = l_run[0] + __shfl_xor(l_run[0], 16, 64);
   L += __shfl_xor(L, 32, 64);
@@ -1717,6 +1795,12 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     s.ws_ml = a.ws_ml ? a.ws_ml + rows * a.n_parts * 2 : nullptr;
     s.ws_u = a.ws_u ? a.ws_u + rows * a.n_parts * head_dim : nullptr;
     s.counters = a.counters ? a.counters + (int64_t)r0 * a.num_kv_heads : nullptr;
+    if (a.new_slots) {
+      const int64_t new_row = (int64_t)r0 * a.num_kv_heads * head_dim * 2;  // bytes (bf16)
+      s.new_slots = a.new_slots + r0;
+      s.k_new = static_cast<const char*>(a.k_new) + new_row;
+      s.v_new = static_cast<const char*>(a.v_new) + new_row;
+    }
     s.batch = nb;
     const dim3 grid((unsigned)a.num_kv_heads, (unsigned)nb, (unsigned)a.n_parts);
     const dim3 block(kDecodeThreads);

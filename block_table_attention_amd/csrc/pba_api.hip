@@ -558,7 +558,8 @@ int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
                 const int32_t* block_tables, const int64_t* row_offsets,
                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, float scale,
                 float* out, float* lse, int32_t partition_tokens, void* workspace,
-                size_t workspace_bytes, void* stream, int mode, const ScratchArea* scratch) {
+                size_t workspace_bytes, void* stream, int mode, const ScratchArea* scratch,
+                const NewTokens* fused) {
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
   if (mode == pba::kTablesContiguous && pool->dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
@@ -566,6 +567,8 @@ int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
   if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
+  if (fused && (!fused->slots || !fused->k || !fused->v)) return PBA_ERR_NULL_ARG;
+  if (fused && (!aligned16(fused->k) || !aligned16(fused->v))) return PBA_ERR_UNSUPPORTED;
   const bool flat = use_flat(pool, num_q_heads, batch, partition_tokens, max_blocks_per_seq);
   int32_t pt = 0, np = 0;
   if (!flat) {
@@ -635,6 +638,25 @@ int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
       }
       if ((st = pba::vkv_check_blocks(pool->k, tab.data() + base, nb))) return st;
     }
+    if (fused) {
+      // Each new token is its row's position T - 1 through the row's table
+      // (or slot); slots distinct.
+      std::vector<int64_t> ns;
+      if (!copy_to_host(ns, fused->slots, batch, s)) return PBA_ERR_HIP;
+      std::unordered_set<int64_t> seen;
+      const int P = pool->block_size;
+      for (int32_t r = 0; r < batch; ++r) {
+        if (ns[r] < 0) continue;
+        const int64_t t = lens[r] - 1;
+        int64_t blk;
+        if (mode == pba::kTablesContiguous)
+          blk = (int64_t)tab[r] * max_blocks_per_seq + t / P;
+        else
+          blk = tab[(size_t)((row_offsets ? offs[r] : (int64_t)r * max_blocks_per_seq) + t / P)];
+        if (ns[r] != blk * P + t % P) return PBA_ERR_OUT_OF_RANGE;
+        if (!seen.insert(ns[r]).second) return PBA_ERR_OVERLAP;
+      }
+    }
   }
   pba::DecodeArgs a;
   a.k = pool->k;
@@ -666,6 +688,33 @@ int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
   a.part_tokens = pt;
   a.n_parts = np;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.new_slots = nullptr;
+  a.k_new = a.v_new = nullptr;
+  if (fused) {
+    if (!flat && pool->dtype == PBA_BF16) {
+      a.new_slots = fused->slots;
+      a.k_new = fused->k;
+      a.v_new = fused->v;
+    } else {
+      // The balanced and fp32 decodes take the appends as a launch of their
+      // own, ahead of the decode on the same stream.
+      pba::AppendArgs ap;
+      ap.k = const_cast<void*>(pool->k);
+      ap.v = const_cast<void*>(pool->v);
+      ap.k_sb = pool->k_stride_block;
+      ap.k_sh = pool->k_stride_head;
+      ap.v_sb = pool->v_stride_block;
+      ap.v_sh = pool->v_stride_head;
+      ap.slots = fused->slots;
+      ap.k_new = fused->k;
+      ap.v_new = fused->v;
+      ap.n = batch;
+      ap.log2P = log2_exact(pool->block_size) + pool->split_log2;  // allocator tiles
+      ap.head_dim = pool->head_dim;
+      ap.kv_heads = pool->num_kv_heads;
+      if (pba::launch_kv_append(ap, esize_of(pool->dtype), s) != hipSuccess) return PBA_ERR_HIP;
+    }
+  }
   if (flat) {
     pba::FlatArgs f;
     f.piece_ml = ws_ml;
@@ -690,7 +739,19 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
                      void* stream) {
   return pba::decode_impl(pool, q, num_q_heads, block_tables, nullptr, max_blocks_per_seq,
                           seq_lens, batch, scale, out, lse, partition_tokens, workspace,
-                          workspace_bytes, stream, pba::kTablesDense, nullptr);
+                          workspace_bytes, stream, pba::kTablesDense, nullptr, nullptr);
+}
+
+int pba_paged_decode_append(const pba_kv_pool* pool, const int64_t* new_slots, const void* k_new,
+                            const void* v_new, const void* q, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                            float* lse, int32_t partition_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const pba::NewTokens fused{new_slots, k_new, v_new};
+  return pba::decode_impl(pool, q, num_q_heads, block_tables, nullptr, max_blocks_per_seq,
+                          seq_lens, batch, scale, out, lse, partition_tokens, workspace,
+                          workspace_bytes, stream, pba::kTablesDense, nullptr, &fused);
 }
 
 int pba_paged_decode_ragged(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
@@ -701,7 +762,7 @@ int pba_paged_decode_ragged(const pba_kv_pool* pool, const void* q, int32_t num_
   if (batch > 0 && !row_offsets) return PBA_ERR_NULL_ARG;
   return pba::decode_impl(pool, q, num_q_heads, block_entries, row_offsets, max_blocks_per_seq,
                           seq_lens, batch, scale, out, lse, partition_tokens, workspace,
-                          workspace_bytes, stream, pba::kTablesDense, nullptr);
+                          workspace_bytes, stream, pba::kTablesDense, nullptr, nullptr);
 }
 
 int pba_paged_decode_contiguous(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
@@ -713,7 +774,7 @@ int pba_paged_decode_contiguous(const pba_kv_pool* pool, const void* q, int32_t 
   if (pool && pool->split_log2) return PBA_ERR_UNSUPPORTED;
   return pba::decode_impl(pool, q, num_q_heads, slot_index, nullptr, blocks_per_slot, seq_lens,
                           batch, scale, out, lse, partition_tokens, workspace, workspace_bytes,
-                          stream, pba::kTablesContiguous, nullptr);
+                          stream, pba::kTablesContiguous, nullptr, nullptr);
 }
 
 int pba_expand_block_tables(const int32_t* src, int64_t n_entries, int32_t split_log2,
@@ -934,6 +995,8 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
   a.part_tokens = plan->partition_tokens;
   a.n_parts = plan->max_slots;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.new_slots = nullptr;
+  a.k_new = a.v_new = nullptr;
   pba::SharedArgs sa;
   sa.items = plan->items;
   sa.row_private = plan->row_private;

@@ -67,6 +67,11 @@ struct DecodeArgs {
   int32_t n_parts;
   float scale_log2;  // scale * log2(e): scores live in the log2 domain
   int32_t split_log2;  // kernel view of an allocator pool: tiles of P << split rows
+  // Fused append (nullptr: none): row r's new token -- its position T - 1 --
+  // goes to slot new_slots[r] (negative: none) from k_new / v_new [B][H_kv][D].
+  const int64_t* new_slots;
+  const void* k_new;
+  const void* v_new;
 };
 
 // Shared-prefix decode: chunk-first items (int32 x 8 each: row0, nrows, tb,
@@ -104,14 +109,24 @@ struct ScratchArea {
   size_t state_bytes;
 };
 
+// The step's new tokens, one per row, appended in the decode launch: row r's
+// token goes to slot slots[r] (negative: none), its rows k[r], v[r] [H_kv][D].
+struct NewTokens {
+  const int64_t* slots;
+  const void* k;
+  const void* v;
+};
+
 // The decode entry points' common host path (argument checks, plan, validate
 // mode, launch).  mode: kTablesDense / kTablesRagged / kTablesContiguous (a
-// dense call with row_offsets is ragged); scratch: nullptr to use `workspace`.
+// dense call with row_offsets is ragged); scratch: nullptr to use `workspace`;
+// fused: nullptr, or the step's new tokens.
 int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
                 const int32_t* block_tables, const int64_t* row_offsets,
                 int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t batch, float scale,
                 float* out, float* lse, int32_t partition_tokens, void* workspace,
-                size_t workspace_bytes, void* stream, int mode, const ScratchArea* scratch);
+                size_t workspace_bytes, void* stream, int mode, const ScratchArea* scratch,
+                const NewTokens* fused);
 
 hipError_t launch_paged_decode_flat(const DecodeArgs& a, const FlatArgs& f, int head_dim,
                                     int n_wg, hipStream_t stream);

@@ -273,6 +273,34 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
                      void* stream);
 
 /*
+ * pba_paged_decode_append -- one decode step: the step's new tokens, one per
+ * row, appended and the batch decoded in one call ("M5.3", 0x04E the appended
+ * row o is written before the decode reads it; 0x0A the decode loop).  The
+ * result equals pba_kv_append(new_slots, k_new, v_new, batch) followed by
+ * pba_paged_decode(...) on the same stream, bit for bit in the pool and in
+ * out / lse.
+ *
+ *   new_slots     device int64 [batch]: row r's new token goes to slot
+ *                 new_slots[r] (negative: row r appends nothing this step).
+ *                 That slot must be row r's last position, T_r - 1, through
+ *                 its block table (block_tables[r][(T_r - 1) / P] * P +
+ *                 (T_r - 1) % P); validate mode checks it (PBA_ERR_OUT_OF_RANGE)
+ *                 and that slots are distinct (PBA_ERR_OVERLAP)
+ *   k_new, v_new  device [batch, num_kv_heads, head_dim], pool dtype,
+ *                 contiguous, 16-byte aligned: the new tokens' K and V rows
+ * Other arguments as pba_paged_decode (the same workspace size).  bf16 pools
+ * with partitions (not PBA_PARTITIONS_BALANCED) write each new token from the
+ * decode's own work-group that reads it, in the decode launch; fp32 pools and
+ * the balanced decomposition launch the appends first, on the same stream.
+ */
+int pba_paged_decode_append(const pba_kv_pool* pool, const int64_t* new_slots, const void* k_new,
+                            const void* v_new, const void* q, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                            float* lse, int32_t partition_tokens, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/*
  * pba_paged_decode_ragged -- pba_paged_decode over a compact block table
  * ("M5.3", 0x0AB): row r's entries are block_entries[row_offsets[r] ..
  * row_offsets[r + 1]) (at least ceil(T_r / P) of them) instead of a dense
