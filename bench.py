@@ -101,8 +101,8 @@ def parse():
     ap.add_argument("--partition-tokens", type=_partition_arg, default=AUTO,
                     help="decode partitions: a length in tokens, 0 = the library's plan, "
                          "'balanced' = the batch's chunks spread evenly over the CUs; default "
-                         "'auto': chosen from the batch's lengths by "
-                         "blocks.suggest_partition_tokens")
+                         "'auto': the library chooses from the batch's lengths "
+                         "(pba_paged_decode_plan_ex with PBA_PARTITIONS_AUTO)")
     ap.add_argument("--decode", default="auto", choices=["auto", "plain", "shared"],
                     help="decode entry point: paged_decode, paged_decode_shared (shared-prefix "
                          "execution reuse), or auto = shared when the batch shares chunks")
@@ -430,9 +430,12 @@ def run_workload(args, name, pba, torch, dev):
     mb = plan.tables.shape[1] << split
     # The bench is the caller: it knows the lengths and may pick the split.
     req_pt = args.partition_tokens
-    if req_pt == AUTO:
-        from block_table_attention_amd.blocks import suggest_partition_tokens
-        req_pt = suggest_partition_tokens(plan.seq_lens, Hkv, balanced_ok=sh.dtype == "bf16")
+    # The library's dispatch decision for this batch, from a summary of its
+    # lengths (PARTITIONS_AUTO), or for the partition length asked for.
+    dispatch = pba.paged_decode_plan_ex(dpool, Hq, B, mb,
+                                        pba.PARTITIONS_AUTO if req_pt == AUTO else req_pt,
+                                        plan.seq_lens)
+    req_pt = dispatch["partition_request"]
     if host_plan is None:
         pt, n_parts = pba.paged_decode_plan(dpool, Hq, B, mb, req_pt)
         # The balanced path reports no partition size, only its wave count.
@@ -573,10 +576,12 @@ def run_workload(args, name, pba, torch, dev):
                    "num_kv_heads": Hkv, "head_dim": d, "pool_blocks": sh.num_blocks,
                    "partition_tokens": pt, "num_partitions": n_parts,
                    "partition_choice": "shared-prefix plan" if host_plan is not None else
-                   ("library plan" if req_pt == 0 else
-                    ("balanced" if req_pt == BALANCED else
-                     ("caller (suggest_partition_tokens)" if args.partition_tokens == AUTO
-                      else "fixed"))),
+                   ("library, from the lengths (PBA_PARTITIONS_AUTO)"
+                    if args.partition_tokens == AUTO else "fixed by --partition-tokens"),
+                   "dispatch": None if host_plan is not None else
+                   {"decomposition": dispatch["decomposition"], "reason": dispatch["reason"],
+                    "fallback": dispatch["fallback"],
+                    "partition_request": dispatch["partition_request"]},
                    "decode_path": "balanced" if flat else path,
                    "tables": "ragged" if row_offsets is not None else "dense",
                    "table_cells": table_cells,
@@ -586,6 +591,14 @@ def run_workload(args, name, pba, torch, dev):
                    {"chunks": len(host_plan.chunks), "items": int(host_plan.items.shape[0]),
                     "max_slots": host_plan.max_slots,
                     "chunk_rows": int(sum(b - a for a, b, _, _ in host_plan.chunks)),
+                    # Work items' 32-token chunk reads, and the partial states
+                    # the launch writes (G x (d + 2) floats per row, slot and
+                    # kv head), over all kv heads.
+                    "chunk_visits": int(host_plan.chunk_visits) * Hkv,
+                    "kv_rows_read": int(host_plan.kv_rows_read) * Hkv,
+                    "partial_states": int(host_plan.partial_states) * Hkv,
+                    "partial_state_bytes": int(host_plan.partial_states) * Hkv * (Hq // Hkv)
+                    * (d + 2) * 4,
                     "private_tokens": host_plan.private_tokens,
                     "private_ranges": "four rows per work-group"
                     if 0 < host_plan.private_tokens <= 128 else "a work-group per piece"},
@@ -755,10 +768,10 @@ def run_bundle(args, name, pba, torch, dev):
     layer_pools = [(g, grp.layer(l)) for g, grp in enumerate(groups) for l in range(grp.num_layers)]
     scale = 1.0 / math.sqrt(d)
     req_pt = args.partition_tokens
-    if req_pt == AUTO:
-        from block_table_attention_amd.blocks import suggest_partition_tokens
-        req_pt = suggest_partition_tokens(plan.seq_lens, Hkv)
     mbs = [t.shape[1] for t in plan.tables]
+    if req_pt == AUTO:
+        req_pt = pba.paged_decode_plan_ex(layer_pools[0][1], Hq, B, mbs[0], pba.PARTITIONS_AUTO,
+                                          plan.seq_lens)["partition_request"]
     ws_bytes = max(pba.paged_decode_workspace_bytes(lp, Hq, B, mbs[g], req_pt) for g, lp in layer_pools)
     pt, n_parts = pba.paged_decode_plan(layer_pools[0][1], Hq, B, mbs[0], req_pt)
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -966,8 +979,8 @@ def run_contiguous(args, name, pba, torch, dev):
     lens_d = torch.from_numpy(lens.astype(np.int32)).to(dev)
     req_pt = args.partition_tokens
     if req_pt == AUTO:
-        from block_table_attention_amd.blocks import suggest_partition_tokens
-        req_pt = suggest_partition_tokens(lens, Hkv)
+        req_pt = pba.paged_decode_plan_ex(pool, Hq, B, bps, pba.PARTITIONS_AUTO,
+                                          lens)["partition_request"]
     pt, n_parts = pba.paged_decode_plan(pool, Hq, B, bps, req_pt)
     ws = torch.zeros(max(pba.paged_decode_workspace_bytes(pool, Hq, B, bps, req_pt), 16),
                      dtype=torch.uint8, device=dev)

@@ -18,7 +18,8 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = ["KVPool", "kv_append", "block_copy", "paged_decode", "paged_decode_plan",
-           "paged_decode_noalloc", "paged_decode_append",
+           "paged_decode_noalloc", "paged_decode_append", "paged_decode_plan_ex",
+           "shared_plan_build", "PARTITIONS_AUTO",
            "paged_decode_ragged", "expand_block_tables", "pack_block_tables",
            "paged_decode_shared", "paged_decode_shared_workspace_bytes", "SharedPlan",
            "paged_decode_workspace_bytes", "decode_workspace", "KVGroup", "kv_append_bundle",
@@ -49,6 +50,12 @@ NOALLOC_COUNTER_BYTES = 256 * 1024        # PBA_NOALLOC_COUNTER_BYTES
 NOALLOC_STATE_BYTES = 32 * 1024 * 1024    # PBA_NOALLOC_STATE_BYTES
 MAX_GROUPS = 8
 PARTITIONS_BALANCED = -1   # partition_tokens: balance the batch's chunks over the CUs
+PARTITIONS_AUTO = -2       # paged_decode_plan_ex: the library chooses from the lengths
+PLAN_REASONS = {0: "none", 1: "requested", 2: "table width", 3: "uniform lengths",
+                4: "few rows", 5: "ragged lengths", 6: "mildly ragged lengths",
+                7: "fallback: fp32 pool", 8: "fallback: more than 2048 rows",
+                9: "fallback: LDS above 64 KiB", 10: "fallback: chunk count"}
+DECOMPOSITIONS = {0: "grid", 1: "balanced"}
 _DTYPES = {torch.float32: PBA_F32, torch.bfloat16: PBA_BF16}
 
 
@@ -87,6 +94,30 @@ class SharedPlanDesc(ctypes.Structure):
                 ("private_tokens", ctypes.c_int32), ("reserved0", ctypes.c_int32)]
 
 
+class LengthHint(ctypes.Structure):
+    _fields_ = [("sum_tokens", ctypes.c_int64), ("max_tokens", ctypes.c_int32),
+                ("reserved0", ctypes.c_int32)]
+
+
+class DecodePlanInfo(ctypes.Structure):
+    _fields_ = [("partition_request", ctypes.c_int32), ("decomposition", ctypes.c_int32),
+                ("partition_tokens", ctypes.c_int32), ("num_partitions", ctypes.c_int32),
+                ("reason", ctypes.c_int32), ("fallback", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+class SharedPlanParams(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "block_size", "group", "partition_tokens", "threshold", "tiles_per_item", "reserved0")]
+
+
+class SharedPlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "num_items", "num_chunks", "max_slots", "private_parts", "private_tokens",
+        "partition_tokens")] + [(n, ctypes.c_int64) for n in (
+            "chunk_rows", "kv_rows_read", "chunk_visits", "partial_states")]
+
+
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _P = ctypes.POINTER(PoolDesc)
 _SP = ctypes.POINTER(SharedPlanDesc)
@@ -99,6 +130,12 @@ _SIGS = {
     "pba_paged_decode_append": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp, _i32,
                                                ctypes.c_float, _vp, _vp, _i32, _vp, _sz, _vp]),
     "pba_paged_decode_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _i32]),
+    "pba_paged_decode_plan_ex": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32,
+                                                ctypes.POINTER(LengthHint),
+                                                ctypes.POINTER(DecodePlanInfo)]),
+    "pba_shared_plan_build": (ctypes.c_int, [_vp, _i32, _vp, _i32, ctypes.POINTER(SharedPlanParams),
+                                             _vp, _vp, _i32, _vp, _vp, _i32,
+                                             ctypes.POINTER(SharedPlanInfo)]),
     "pba_paged_decode_plan": (ctypes.c_int, [_P, _i32, _i32, _i32, _i32,
                                              ctypes.POINTER(_i32), ctypes.POINTER(_i32)]),
     "pba_paged_decode_ragged": (ctypes.c_int, [_P, _vp, _i32, _vp, _vp, _i32, _vp, _i32,
@@ -273,6 +310,64 @@ def paged_decode_workspace_bytes(pool: KVPool, num_q_heads: int, batch: int,
                                  max_blocks_per_seq: int, partition_tokens: int = 0) -> int:
     return int(_lib.pba_paged_decode_workspace_bytes(pool._ref, num_q_heads, batch,
                                                      max_blocks_per_seq, partition_tokens))
+
+
+def paged_decode_plan_ex(pool, num_q_heads: int, batch: int, max_blocks_per_seq: int,
+                         partition_tokens: int = 0, seq_lens=None) -> dict:
+    """The decomposition the decode calls will use for these arguments, and
+    why (host only).  pool: a KVPool or a PoolDesc.  With partition_tokens =
+    PARTITIONS_AUTO and the batch's lengths (any int sequence, host side), the
+    library chooses; pass the returned "partition_request" to the decode."""
+    desc = pool._ref if hasattr(pool, "_ref") else ctypes.byref(pool)
+    hint = None
+    if seq_lens is not None:
+        import numpy as np
+        lens = np.asarray(seq_lens, dtype=np.int64)
+        hint = ctypes.byref(LengthHint(int(lens.sum()), int(lens.max()) if lens.size else 0, 0))
+    info = DecodePlanInfo()
+    _check("pba_paged_decode_plan_ex", _lib.pba_paged_decode_plan_ex(
+        desc, num_q_heads, batch, max_blocks_per_seq, partition_tokens, hint, ctypes.byref(info)))
+    return {"partition_request": info.partition_request,
+            "decomposition": DECOMPOSITIONS[info.decomposition],
+            "partition_tokens": info.partition_tokens, "num_partitions": info.num_partitions,
+            "reason": PLAN_REASONS[info.reason], "fallback": PLAN_REASONS[info.fallback],
+            "workspace_bytes": int(info.workspace_bytes)}
+
+
+def shared_plan_build(tables, seq_lens, block_size: int, group: int, partition_tokens: int = 256,
+                      threshold: int = 1, tiles_per_item: int = 4) -> dict:
+    """The library's host planner of the shared-prefix decode (host numpy
+    arrays in, host arrays out; no device work): the sharing order, the
+    plan's items [n, 8] and private ranges [B, 2] (rows in sharing order),
+    the chunks [c, 4] and the plan's scalars and ledgers."""
+    import numpy as np
+    t = np.ascontiguousarray(tables, dtype=np.int32)
+    if t.ndim != 2:
+        raise ValueError("tables must be [batch, width]")
+    lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    B, width = t.shape
+    if lens.shape != (B,):
+        raise ValueError("seq_lens must be [batch]")
+    params = SharedPlanParams(block_size, group, partition_tokens, threshold, tiles_per_item, 0)
+    info = SharedPlanInfo()
+    order = np.zeros(B, dtype=np.int64)
+    row_private = np.zeros((B, 2), dtype=np.int32)
+    args = (t.ctypes.data if B else None, max(width, 1), lens.ctypes.data if B else None, B,
+            ctypes.byref(params))
+    _check("pba_shared_plan_build", _lib.pba_shared_plan_build(
+        *args, order.ctypes.data if B else None, None, 0,
+        row_private.ctypes.data if B else None, None, 0, ctypes.byref(info)))
+    items = np.zeros((info.num_items, 8), dtype=np.int32)
+    chunks = np.zeros((info.num_chunks, 4), dtype=np.int32)
+    _check("pba_shared_plan_build", _lib.pba_shared_plan_build(
+        *args, order.ctypes.data if B else None, items.ctypes.data if info.num_items else None,
+        info.num_items, row_private.ctypes.data if B else None,
+        chunks.ctypes.data if info.num_chunks else None, info.num_chunks, ctypes.byref(info)))
+    return {"order": order, "items": items, "row_private": row_private, "chunks": chunks,
+            "max_slots": info.max_slots, "private_parts": info.private_parts,
+            "private_tokens": info.private_tokens, "partition_tokens": info.partition_tokens,
+            "chunk_rows": int(info.chunk_rows), "kv_rows_read": int(info.kv_rows_read),
+            "chunk_visits": int(info.chunk_visits), "partial_states": int(info.partial_states)}
 
 
 _WORKSPACES: "OrderedDict[tuple, torch.Tensor]" = OrderedDict()

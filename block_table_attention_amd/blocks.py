@@ -214,44 +214,36 @@ class BundleManager:
 PARTITIONS_BALANCED = -1   # the library's balanced decomposition (PBA_PARTITIONS_BALANCED)
 
 
-def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus: int = 256,
-                             balanced_ok: bool = True) -> int:
-    """A partition choice for ``paged_decode`` from the lengths the caller
-    knows (the library sees only the table width and the batch).
+# ---------------------------------------------------------------------------
+# Planning: thin wrappers over the library's host planners (libpba.so), which
+# hold the decisions; these only convert between numpy arrays and the ABI.
+# ---------------------------------------------------------------------------
+def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int,
+                             balanced_ok: bool = True, num_q_heads: int = 0,
+                             head_dim: int = 128) -> int:
+    """The partition request the library chooses for a batch with these
+    lengths (``pba_paged_decode_plan_ex`` with ``PBA_PARTITIONS_AUTO``): the
+    balanced decomposition for very ragged batches that fill the CUs (or
+    partitions of about twice the mean where it is not built: fp32 pools,
+    ``balanced_ok`` False, more than 2048 rows), 512/1024-token partitions
+    for mildly ragged ones, otherwise 0 (the library's table-width plan).
+    The pool is described by its kv heads (q heads default to 4 per kv
+    head), bf16 when ``balanced_ok`` else fp32."""
+    import block_table_attention_amd as pba
 
-    * Very ragged batches -- every CU already has a (request, kv head) and the
-      longest request is over 4x the mean -- get the balanced decomposition
-      (``PARTITIONS_BALANCED``: the batch's chunks spread evenly over the CUs)
-      when ``balanced_ok`` (bf16 pools, at most 2048 rows), else partitions of
-      about twice the mean length.  Lognormal batches of 128 requests (median
-      100, max 8192 tokens): 50 / 49 / 50 us at P = 16 / 64 / 256 balanced,
-      61 / 77 / 76 us with 1024-token partitions, 102 / 139 / 140 us unsplit.
-    * Mildly ragged batches (longest over 1.3x the mean and at least 1536
-      tokens) with more (request, kv head) pairs than half the CUs get 512-token
-      partitions (1024 from 4096 tokens on): one work-group streams at most
-      ~60 GB/s from its CU, and with whole rows per work-group the CUs that
-      hold the longest rows finish last.  Measured 4-16 % faster over a grid
-      of batches (8-128 requests, 4-8 kv heads, rows up to 8192 tokens), e.g.
-      a 32-layer bundle of 40 requests of 101-2028 tokens at 4 kv heads:
-      26.7 -> 21.3 us per layer.
-    * Otherwise 0, the library's plan (uniform batches are fastest with it,
-      and so are batches that fill under half the CUs, which it splits).
-    """
     lens = np.asarray(seq_lens, dtype=np.int64)
     if lens.size == 0:
         return 0
-    units = lens.size * num_kv_heads
-    mean = float(lens.mean())
-    longest = int(lens.max())
-    if units >= num_cus and longest > 4 * mean:
-        if balanced_ok and lens.size <= 2048:
-            return PARTITIONS_BALANCED
-        pt = int(-(-int(2 * mean) // 256) * 256)
-        pt = max(512, pt)
-        return 0 if pt >= longest else pt
-    if 2 * units > num_cus and longest > 1.3 * mean and longest >= 1536:
-        return 512 if longest < 4096 else 1024
-    return 0
+    P = 16
+    desc = pba.PoolDesc(k=0x10000, v=0x20000, dtype=1 if balanced_ok else 0, num_blocks=1,
+                        block_size=P, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                        split_log2=0, k_stride_block=num_kv_heads * P * head_dim,
+                        k_stride_head=P * head_dim, v_stride_block=num_kv_heads * P * head_dim,
+                        v_stride_head=P * head_dim)
+    width = max(1, int(-(-int(lens.max()) // P)))
+    plan = pba.paged_decode_plan_ex(desc, num_q_heads or 4 * num_kv_heads, int(lens.size), width,
+                                    pba.PARTITIONS_AUTO, lens)
+    return plan["partition_request"]
 
 
 # ---------------------------------------------------------------------------
@@ -259,10 +251,12 @@ def suggest_partition_tokens(seq_lens: Sequence[int], num_kv_heads: int, num_cus
 # ---------------------------------------------------------------------------
 def sharing_order(tables: np.ndarray) -> np.ndarray:
     """A batch order in which rows that map the same leading blocks are
-    adjacent (lexicographic order of the block tables), so that each shared
-    chunk covers one contiguous range of rows."""
+    adjacent (lexicographic order of the block tables, stable), so that each
+    shared chunk covers one contiguous range of rows."""
+    import block_table_attention_amd as pba
+
     t = np.asarray(tables)
-    return np.lexsort(t.T[::-1]).astype(np.int64)
+    return pba.shared_plan_build(t, np.zeros(t.shape[0], np.int32), 16, 1)["order"]
 
 
 def shared_chunks(tables: np.ndarray, seq_lens: Sequence[int], block_size: int,
@@ -275,38 +269,18 @@ def shared_chunks(tables: np.ndarray, seq_lens: Sequence[int], block_size: int,
     than ``threshold`` rows become chunks (0x0BD's coverage threshold).  Rows
     sharing leading blocks must be adjacent (see ``sharing_order``).
     """
-    t = np.asarray(tables)
-    lens = np.asarray(seq_lens, dtype=np.int64)
-    P = block_size
-    full = lens // P                         # whole blocks each row can see
-    B = len(lens)
-    chunks = []
-    private = np.zeros(B, dtype=np.int64)
+    import block_table_attention_amd as pba
 
-    def visit(a: int, b: int, j0: int) -> None:
-        if b - a <= threshold:
-            private[a:b] = j0 * P
-            return
-        lim = int(full[a:b].min())
-        j = j0
-        while j < lim and bool((t[a:b, j] == t[a, j]).all()):
-            j += 1
-        if j > j0:
-            chunks.append((a, b, j0 * P, j * P))
-        r = a
-        while r < b:
-            if full[r] <= j:
-                private[r] = j * P
-                r += 1
-                continue
-            e = r + 1
-            while e < b and full[e] > j and t[e, j] == t[r, j]:
-                e += 1
-            visit(r, e, j)
-            r = e
+    r = pba.shared_plan_build(tables, seq_lens, block_size, 1, 256, threshold, 1)
+    _require_identity(r["order"])
+    return ([tuple(int(x) for x in c) for c in r["chunks"]],
+            r["row_private"][:, 0].astype(np.int64))
 
-    visit(0, B, 0)
-    return chunks, private
+
+def _require_identity(order: np.ndarray) -> None:
+    if not np.array_equal(order, np.arange(order.size)):
+        raise ValueError("rows sharing leading blocks must be adjacent: order the batch with "
+                         "sharing_order first")
 
 
 @dataclass
@@ -318,58 +292,31 @@ class HostSharedPlan:
     chunks: List[Tuple[int, int, int, int]]
     private_parts: int = 0     # most private pieces of any row
     private_tokens: int = 0    # most private positions of any row (0: none given)
+    kv_rows_read: int = 0      # key positions read per kv head (library ledger)
+    chunk_visits: int = 0      # 32-token chunk reads per kv head
+    partial_states: int = 0    # (row, slot) partial states written per kv head
 
 
 def shared_plan(tables: np.ndarray, seq_lens: Sequence[int], block_size: int, group: int,
                 partition_tokens: int = 256, threshold: int = 1,
                 tiles_per_item: int = 4) -> HostSharedPlan:
-    """The work items of ``paged_decode_shared`` for a batch.
+    """The work items of ``paged_decode_shared`` for a batch already in
+    sharing order (``pba_shared_plan_build``): every chunk cut into pieces of
+    ``partition_tokens`` keys, its rows in 16-column tiles of 16 // group rows,
+    up to ``tiles_per_item`` tiles per item; each row's private range after
+    its last chunk; the plan's bounds and ledgers."""
+    import block_table_attention_amd as pba
 
-    Every chunk is cut into pieces of ``partition_tokens`` keys from its first
-    key; each piece is one partial state (slot) of every row it covers.  Rows
-    of a piece go in 16-column tiles of 16 // group rows, up to
-    ``tiles_per_item`` (1, 2 or 4) tiles per item: one K/V read serves them
-    all (tiles go in groups of two whose waves split the keys).  A row's
-    slots: its chunks' pieces in path order, then its private pieces.  The
-    plan also bounds every row's private positions, which lets the library
-    walk short private ranges four rows per work-group.
-    """
     if tiles_per_item not in (1, 2, 4):
         raise ValueError("tiles_per_item must be 1, 2 or 4")
     if partition_tokens <= 0 or partition_tokens % 256:
         raise ValueError("partition_tokens must be a positive multiple of 256")
-    lens = np.asarray(seq_lens, dtype=np.int64)
-    chunks, private = shared_chunks(tables, lens, block_size, threshold)
-    pt = partition_tokens
-    rpt = 16 // group
-    if rpt < 1:
+    if not 1 <= group <= 16:
         raise ValueError("group (q-heads per kv head) must be at most 16")
-    next_slot = np.zeros(len(lens), dtype=np.int64)
-    items = []
-    for a, b, t0, t1 in chunks:
-        base = int(next_slot[a])
-        if not (next_slot[a:b] == base).all():
-            raise AssertionError("rows of a chunk disagree on their ancestors")
-        pieces = -(-(t1 - t0) // pt)
-        tiles = -(-(b - a) // rpt)
-        for k in range(pieces):
-            tb = t0 + k * pt
-            te = min(t1, tb + pt)
-            ti = 0
-            while ti < tiles:
-                left = tiles - ti
-                n_t = min(tiles_per_item, 4 if left >= 4 else (2 if left >= 2 else 1))
-                row0 = a + ti * rpt
-                nrows = min(b, a + (ti + n_t) * rpt) - row0
-                items.append((row0, nrows, tb, te, base + k, n_t, 0, 0))
-                ti += n_t
-        next_slot[a:b] += pieces
-    row_private = np.stack([private, next_slot], axis=1).astype(np.int32)
-    priv_pieces = -(-np.maximum(lens - private, 0) // pt)
-    max_slots = int(max(1, (next_slot + priv_pieces).max()))
-    arr = np.array(items, dtype=np.int32).reshape(-1, 8)
-    # The launch holds one grid plane per possible private piece; the true
-    # bound keeps it from filling with empty work-groups.
-    return HostSharedPlan(arr, row_private, max_slots, pt, chunks,
-                          int(max(1, priv_pieces.max())),
-                          int(max(1, np.maximum(lens - private, 0).max())))
+    r = pba.shared_plan_build(tables, seq_lens, block_size, group, partition_tokens, threshold,
+                              tiles_per_item)
+    _require_identity(r["order"])
+    return HostSharedPlan(r["items"].reshape(-1, 8), r["row_private"], r["max_slots"],
+                          r["partition_tokens"], [tuple(int(x) for x in c) for c in r["chunks"]],
+                          r["private_parts"], r["private_tokens"], r["kv_rows_read"],
+                          r["chunk_visits"], r["partial_states"])

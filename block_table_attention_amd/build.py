@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libpba.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["pba_api.hip", "kv_append.hip", "block_copy.hip", "paged_decode.hip", "tables.hip",
-           "bundle.hip", "vkv.hip", "noalloc.hip"]
+           "bundle.hip", "vkv.hip", "noalloc.hip", "plan.cpp"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          # MFMA accumulators in arch VGPRs: the online-softmax rescale is VALU
@@ -51,10 +51,10 @@ def build(asm: bool = False, verbose: bool = True) -> str:
     objs = []
     for src in SOURCES:
         path = os.path.join(CSRC, src)
-        obj = os.path.join(objdir, src.replace(".hip", ".o"))
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         _run([HIPCC, *FLAGS, "-c", path, "-o", obj])
         objs.append(obj)
-        if asm:
+        if asm and src.endswith(".hip"):
             _run([HIPCC, *FLAGS, "--cuda-device-only", "-S", path,
                   "-o", os.path.join(objdir, src.replace(".hip", ".s"))])
     tmp = LIB + ".tmp"

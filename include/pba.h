@@ -60,6 +60,9 @@ typedef enum pba_dtype { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
 /* partition_tokens value of the decode calls: balance the batch's work over
  * the CUs instead of cutting rows into equal partitions. */
 #define PBA_PARTITIONS_BALANCED (-1)
+/* partition_tokens value of pba_paged_decode_plan_ex only: let the library
+ * choose from the caller's summary of the row lengths. */
+#define PBA_PARTITIONS_AUTO (-2)
 
 /*
  * The K/V pool of one layer (one cache group): a fixed set of physical blocks
@@ -397,6 +400,66 @@ int pba_paged_decode_plan(const pba_kv_pool* pool, int32_t num_q_heads, int32_t 
                           int32_t* partition_tokens_out, int32_t* num_partitions_out);
 
 /*
+ * pba_paged_decode_plan_ex -- the decomposition a decode call will use, and
+ * why ("M5.3", 0x0A: a row's keys cut into partitions merged by the LSE rule;
+ * 0x0BL: the dispatch's selected decomposition and its fallback reason are
+ * part of what a run must report).  Host only.
+ *
+ * partition_tokens: as the decode calls take it (0, a length, or
+ * PBA_PARTITIONS_BALANCED), or PBA_PARTITIONS_AUTO: the library chooses from
+ * `hint`, the caller's summary of the batch's row lengths (the decode calls
+ * cannot see them without a device synchronisation):
+ *   - every CU holds a (row, kv head) and the longest row is over 4x the
+ *     mean: the balanced decomposition (reason PBA_PLAN_RAGGED), or where it
+ *     is not built partitions of about twice the mean (fallback says why);
+ *   - the longest row is over 1.3x the mean and at least 1536 tokens and the
+ *     batch covers over half the CUs: 512-token partitions, 1024 from 4096
+ *     tokens on (PBA_PLAN_MILD);
+ *   - otherwise the table-width plan (PBA_PLAN_UNIFORM, or PBA_PLAN_FEW_ROWS
+ *     when the batch covers at most half the CUs).
+ * Without a hint AUTO is the table-width plan (PBA_PLAN_WIDTH).  The decode
+ * calls do not take PBA_PARTITIONS_AUTO: pass out->partition_request.
+ */
+typedef struct pba_length_hint {
+  int64_t sum_tokens;   /* sum over the batch of seq_lens */
+  int32_t max_tokens;   /* largest seq_lens */
+  int32_t reserved0;    /* 0 */
+} pba_length_hint;
+
+typedef enum pba_decomposition {
+  PBA_DECOMP_GRID = 0,      /* (kv head, request, partition) work-groups */
+  PBA_DECOMP_BALANCED = 1   /* the batch's chunks split evenly, one work-group per CU */
+} pba_decomposition;
+
+typedef enum pba_plan_reason {
+  PBA_PLAN_OK = 0,               /* (fallback) none */
+  PBA_PLAN_REQUESTED = 1,        /* the caller's partition length or balanced request */
+  PBA_PLAN_WIDTH = 2,            /* library plan from the table width, no lengths given */
+  PBA_PLAN_UNIFORM = 3,          /* lengths near uniform: the table-width plan */
+  PBA_PLAN_FEW_ROWS = 4,         /* at most half the CUs have a (row, kv head) */
+  PBA_PLAN_RAGGED = 5,           /* longest row over 4x the mean, CUs full */
+  PBA_PLAN_MILD = 6,             /* mildly ragged, over half the CUs */
+  PBA_PLAN_FALLBACK_DTYPE = 7,   /* balanced not built: fp32 pool */
+  PBA_PLAN_FALLBACK_BATCH = 8,   /* balanced not built: more than 2048 rows */
+  PBA_PLAN_FALLBACK_LDS = 9,     /* balanced not built: its LDS exceeds 64 KiB (G 16, d 128) */
+  PBA_PLAN_FALLBACK_CHUNKS = 10  /* balanced not built: 2^31 chunks or more */
+} pba_plan_reason;
+
+typedef struct pba_decode_plan_info {
+  int32_t partition_request;  /* the partition_tokens value to pass to the decode calls */
+  int32_t decomposition;      /* pba_decomposition */
+  int32_t partition_tokens;   /* grid: partition length; balanced: 0 */
+  int32_t num_partitions;     /* grid: partitions per row; balanced: waves */
+  int32_t reason;             /* pba_plan_reason: why this partition request */
+  int32_t fallback;           /* pba_plan_reason: why a balanced choice became the grid (0: none) */
+  uint64_t workspace_bytes;   /* pba_paged_decode_workspace_bytes for the request */
+} pba_decode_plan_info;
+
+int pba_paged_decode_plan_ex(const pba_kv_pool* pool, int32_t num_q_heads, int32_t batch,
+                             int32_t max_blocks_per_seq, int32_t partition_tokens,
+                             const pba_length_hint* hint, pba_decode_plan_info* out);
+
+/*
  * Shared-prefix execution reuse ("M5.3", 0x0BA-0x0BE: disjoint key partitions
  * of one score row merged by log-sum-exp; Hydragen's batching of the queries
  * that share K/V; ChunkAttention's chunk-first / sequence-first phases).
@@ -447,6 +510,64 @@ typedef struct pba_shared_plan {
                                 private piece */
   int32_t reserved0;         /* 0 */
 } pba_shared_plan;
+
+/*
+ * pba_shared_plan_build -- the host side of the shared-prefix decode: from the
+ * batch's block tables and lengths (host memory), the order in which rows that
+ * share leading blocks are adjacent, the shared chunks, and the plan's items
+ * and private ranges ("M5.3", 0x0BB: chunks over a coverage interval of
+ * sequences, each sequence's ordered chunk path; 0x0BD: the chunk-first /
+ * sequence-first metadata is built on the host before the launch).  Host only.
+ *
+ *   tables      host int32 [batch][width], the caller's row order
+ *   seq_lens    host int32 [batch], 0 <= T <= width * P
+ *   order       out, host int64 [batch]: row i of the plan is caller row
+ *               order[i] (rows sorted lexicographically by table row, stable).
+ *               items, row_private and chunks refer to rows in this order: the
+ *               decode gets tables, seq_lens and q permuted the same way
+ *   items       out, host int32 [items_capacity][8] (pba_shared_plan.items), or
+ *               NULL to only size the plan
+ *   row_private out, host int32 [batch][2]
+ *   chunks      out, host int32 [chunks_capacity][4] (row_begin, row_end,
+ *               tok_begin, tok_end) in tree pre-order, or NULL
+ *   info        out: the plan's scalars and ledgers
+ * A chunk is a maximal run of whole, fully visible blocks that every row of a
+ * contiguous row range maps to the same physical ids, below its ancestors'
+ * chunks; runs covering more than params->threshold rows become chunks.
+ * Every chunk is cut into pieces of partition_tokens keys from its first key;
+ * the rows of a piece form 16-column tiles of 16 / G rows, up to
+ * tiles_per_item per item.  A row's slots are its chunks' pieces in path
+ * order, then its private pieces.  Returns PBA_ERR_WORKSPACE_TOO_SMALL (info
+ * filled, nothing else written) when items or chunks exceed their capacity.
+ */
+typedef struct pba_shared_plan_params {
+  int32_t block_size;        /* P of the tables (kernel blocks) */
+  int32_t group;             /* G = num_q_heads / num_kv_heads, 1 .. 16 */
+  int32_t partition_tokens;  /* piece length, a positive multiple of 256 */
+  int32_t threshold;         /* chunks cover more than this many rows (>= 0) */
+  int32_t tiles_per_item;    /* 1, 2 or 4 */
+  int32_t reserved0;         /* 0 */
+} pba_shared_plan_params;
+
+typedef struct pba_shared_plan_info {
+  int32_t num_items;         /* items of the plan */
+  int32_t num_chunks;        /* shared chunks */
+  int32_t max_slots;         /* the pba_shared_plan fields of the same names */
+  int32_t private_parts;
+  int32_t private_tokens;
+  int32_t partition_tokens;
+  int64_t chunk_rows;        /* rows covered, summed over chunks */
+  int64_t kv_rows_read;      /* key positions the plan's work-groups read per kv head
+                                (a piece once per pair of tiles, private ranges once) */
+  int64_t chunk_visits;      /* 32-token chunk reads per kv head, counted the same way */
+  int64_t partial_states;    /* (row, slot) partial states written per kv head (rows of
+                                more than one slot): G * (head_dim + 2) floats each */
+} pba_shared_plan_info;
+
+int pba_shared_plan_build(const int32_t* tables, int32_t width, const int32_t* seq_lens,
+                          int32_t batch, const pba_shared_plan_params* params, int64_t* order,
+                          int32_t* items, int32_t items_capacity, int32_t* row_private,
+                          int32_t* chunks, int32_t chunks_capacity, pba_shared_plan_info* info);
 
 /* Workspace bytes pba_paged_decode_shared needs (0 when max_slots == 1);
  * returns 0 for arguments it would reject.  The first 4 * batch *

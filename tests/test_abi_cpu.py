@@ -361,3 +361,47 @@ def test_noalloc_limits_rejected_on_the_host():
                                         ctypes.c_float(0.1), 0x60000, NULL, 256, NULL) == -1
     assert pba.STATUS[-11] == "PBA_ERR_SCRATCH_LIMIT"
     assert "scratch" in lib.pba_status_string(-11).decode()
+
+
+def test_decode_plan_reasons_and_fallbacks():
+    """pba_paged_decode_plan_ex reports the decomposition, the partition
+    request to pass on, and why -- including why a balanced choice became the
+    grid -- from a summary of the lengths (no GPU: 256 CUs assumed)."""
+    import block_table_attention_amd as pba
+
+    bf = _desc(num_kv_heads=8, k_stride_block=8 * 16 * 128, v_stride_block=8 * 16 * 128)
+    f32 = _desc(dtype=0, num_kv_heads=8, k_stride_block=8 * 16 * 128, v_stride_block=8 * 16 * 128)
+    auto = pba.PARTITIONS_AUTO
+    ragged = [100] * 127 + [8192]
+    p = pba.paged_decode_plan_ex(bf, 32, 128, 512, auto, ragged)
+    assert (p["decomposition"], p["partition_request"], p["reason"], p["fallback"]) == \
+        ("balanced", -1, "ragged lengths", "none")
+    assert p["workspace_bytes"] == _lib().pba_paged_decode_workspace_bytes(ctypes.byref(bf), 32, 128,
+                                                                           512, -1) > 0
+    p = pba.paged_decode_plan_ex(f32, 32, 128, 512, auto, ragged)
+    assert p["decomposition"] == "grid" and p["fallback"] == "fallback: fp32 pool"
+    assert p["partition_request"] == 512 and p["partition_tokens"] == 512
+    p = pba.paged_decode_plan_ex(bf, 32, 4001, 512, auto, [100] * 4000 + [8192])
+    assert p["fallback"] == "fallback: more than 2048 rows" and p["partition_request"] == 512
+    p = pba.paged_decode_plan_ex(bf, 128, 128, 512, auto, ragged)        # G = 16 at d = 128
+    assert p["fallback"] == "fallback: LDS above 64 KiB" and p["decomposition"] == "grid"
+    p = pba.paged_decode_plan_ex(bf, 32, 128, 512, pba.PARTITIONS_BALANCED)
+    assert p["decomposition"] == "balanced" and p["reason"] == "requested"
+    p = pba.paged_decode_plan_ex(f32, 32, 128, 512, pba.PARTITIONS_BALANCED)
+    assert p["decomposition"] == "grid" and p["fallback"] == "fallback: fp32 pool"
+    mild = list(range(400, 2400, 12))                                   # 167 rows, longest 2392
+    p = pba.paged_decode_plan_ex(bf, 32, len(mild), 150, auto, mild)
+    assert p["reason"] == "mildly ragged lengths" and p["partition_request"] == 512
+    p = pba.paged_decode_plan_ex(bf, 32, 64, 128, auto, [2000] * 64)
+    assert p["reason"] == "uniform lengths" and p["partition_request"] == 0
+    p = pba.paged_decode_plan_ex(bf, 32, 8, 1024, auto, [16384] * 8)
+    assert p["reason"] == "few rows" and p["num_partitions"] == 4       # 64 pairs, 4 per row
+    p = pba.paged_decode_plan_ex(bf, 32, 8, 1024, auto)
+    assert p["reason"] == "table width"
+    p = pba.paged_decode_plan_ex(bf, 32, 8, 1024, 512)
+    assert p["reason"] == "requested" and p["partition_tokens"] == 512
+    # The decode calls take the resolved request, never AUTO.
+    lib = _lib()
+    assert lib.pba_paged_decode(ctypes.byref(bf), 0x30000, 32, 0x40000, 4, 0x50000, 2,
+                                ctypes.c_float(0.1), 0x60000, NULL, auto, 0x70000, 1 << 30,
+                                NULL) == -3

@@ -205,3 +205,109 @@ def test_plan_slots_merge_to_monolithic():
             O, L = att.merge_states(states)
             assert np.max(np.abs(O - ref[r, h * G:(h + 1) * G])) <= 1e-13
             assert np.max(np.abs(L - ref_lse[r, h * G:(h + 1) * G])) <= 1e-13
+
+
+# ---------------------------------------------------------------------------
+# The library's planner (pba_shared_plan_build) through ctypes, pinned to the
+# oracle's shared-execution ledgers on the pages' four-sequence tree.
+# ---------------------------------------------------------------------------
+def _fixture_tables(golden):
+    """The pages' chunk tree (0x0BB) as block tables with one 16-token block
+    per fixture row: chunk c of n rows gets n consecutive block ids, and each
+    sequence's table is its path's blocks in order."""
+    t = golden("shared_execution.json")["tree"]
+    ids, nxt = {}, 0
+    for name in sorted(t["chunks"]):
+        n = t["chunks"][name][0]
+        ids[name] = list(range(nxt, nxt + n))
+        nxt += n
+    rows = [[b for c in path for b in ids[c]] for path in t["paths"]]
+    width = max(len(r) for r in rows)
+    tables = np.full((len(rows), width), -1, dtype=np.int32)
+    for i, r in enumerate(rows):
+        tables[i, :len(r)] = r
+    lens = np.array([16 * len(r) for r in rows], dtype=np.int32)
+    tree = [(t["chunks"][c][0], tuple(t["chunks"][c][1])) for c in sorted(t["chunks"])]
+    return tables, lens, tree, t["expect"]
+
+
+@pytest.mark.parametrize("threshold", [0, 1, 2, 3, 4])
+def test_library_planner_matches_oracle_ledgers(golden, threshold):
+    """Chunk-first partial rows and K/V rows read by the library's plan equal
+    the oracle's ChunkAttention ledgers (in 16-token blocks) at every
+    threshold; threshold 1 gives the pages' 8 partial rows and 10 unique rows
+    out of 19 logical ones."""
+    import ctypes
+    import block_table_attention_amd as pba
+    from oracle import shared as S
+
+    tables, lens, tree, expect = _fixture_tables(golden)
+    snap = S.random_snapshot(np.random.default_rng(3), tree, G=1, d_qk=2, d_v=3)
+    res = S.chunk_attention(snap, 1.0, threshold)
+    B, width = tables.shape
+    params = pba.SharedPlanParams(16, 1, 256, threshold, 1, 0)
+    info = pba.SharedPlanInfo()
+    order = np.zeros(B, np.int64)
+    priv = np.zeros((B, 2), np.int32)
+    st = pba._lib.pba_shared_plan_build(tables.ctypes.data, width, lens.ctypes.data, B,
+                                        ctypes.byref(params), order.ctypes.data, None, 0,
+                                        priv.ctypes.data, None, 0, ctypes.byref(info))
+    assert st == 0
+    assert np.array_equal(order, np.arange(B))      # the fixture's rows are already in order
+    assert int(lens.sum()) // 16 == expect["logical_pairs"] == 19
+    assert info.chunk_rows == res.partial_rows
+    assert info.kv_rows_read == 16 * res.kv_rows_read
+    if threshold == 1:
+        assert info.chunk_rows == expect["partial_rows"] == 8
+        assert info.kv_rows_read // 16 == expect["unique_rows"] == 10
+        items = np.zeros((info.num_items, 8), np.int32)
+        chunks = np.zeros((info.num_chunks, 4), np.int32)
+        st = pba._lib.pba_shared_plan_build(tables.ctypes.data, width, lens.ctypes.data, B,
+                                            ctypes.byref(params), order.ctypes.data,
+                                            items.ctypes.data, info.num_items, priv.ctypes.data,
+                                            chunks.ctypes.data, info.num_chunks,
+                                            ctypes.byref(info))
+        assert st == 0
+        assert chunks.tolist() == [[0, 4, 0, 32], [0, 2, 32, 48], [2, 4, 32, 64]]
+        assert priv[:, 0].tolist() == [48, 48, 64, 64]
+        # Slots: C0, then C1 or C2, then the private range.
+        assert priv[:, 1].tolist() == [2, 2, 2, 2] and info.max_slots == 3
+
+
+def test_library_planner_sizes_and_rejects():
+    """A short item buffer returns PBA_ERR_WORKSPACE_TOO_SMALL with the needed
+    count and writes nothing; bad parameters are rejected."""
+    import ctypes
+    import block_table_attention_amd as pba
+
+    m = BlockManager(64, 16)
+    root = m.new_request()
+    m.append(root, 64)
+    kids = [m.fork(root) for _ in range(3)]
+    for k in kids:
+        m.append(k, 20)
+    tables = m.block_tables(kids).astype(np.int32)
+    lens = m.seq_lens(kids).astype(np.int32)
+    B, width = tables.shape
+    info = pba.SharedPlanInfo()
+    order = np.full(B, -7, np.int64)
+    priv = np.full((B, 2), -7, np.int32)
+    items = np.full((1, 8), -7, np.int32)
+
+    def call(params, cap=0, items_ptr=None):
+        return pba._lib.pba_shared_plan_build(tables.ctypes.data, width, lens.ctypes.data, B,
+                                              ctypes.byref(params), order.ctypes.data, items_ptr,
+                                              cap, priv.ctypes.data, None, 0, ctypes.byref(info))
+
+    good = pba.SharedPlanParams(16, 4, 256, 1, 2, 0)
+    assert call(good) == 0 and info.num_items == 1 and info.num_chunks == 1
+    bigger = pba.SharedPlanParams(16, 4, 256, 0, 1, 0)     # threshold 0: the private runs too
+    assert call(bigger, 1, items.ctypes.data) == -5 and info.num_items > 1
+    assert (items == -7).all()
+    for bad, status in ((pba.SharedPlanParams(24, 4, 256, 1, 2, 0), -4),
+                        (pba.SharedPlanParams(16, 4, 300, 1, 2, 0), -4),
+                        (pba.SharedPlanParams(16, 4, 256, 1, 3, 0), -4),
+                        (pba.SharedPlanParams(16, 32, 256, 1, 2, 0), -4),
+                        (pba.SharedPlanParams(16, 4, 256, -1, 2, 0), -3),
+                        (pba.SharedPlanParams(16, 4, 256, 1, 2, 5), -3)):
+        assert call(bad) == status
