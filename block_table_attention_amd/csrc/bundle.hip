@@ -8,18 +8,23 @@
 // Work is flattened over the groups: group g owns the tasks (or work-groups)
 // [task0_g, task0_{g+1}), and a thread finds its group by comparing its index
 // with the at most eight starts held in the kernel arguments.
+#include "append_internal.h"
 #include "bundle_internal.h"
 
 namespace pba {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Append: one thread moves one 16-byte piece of one (token, layer, head) row.
-//   K tasks (piece fastest): a K row is head_dim consecutive scalars of the
-//      token-major tile; neighbouring lanes copy neighbouring pieces.
-//   V tasks (token fastest): the V tile is dim major, a row becomes head_dim
-//      scalars P apart; neighbouring lanes hold neighbouring tokens, which a
-//      prefill's consecutive slots place side by side in each dim run.
+// Append, per group:
+//   K tasks (piece fastest): one thread moves one 16-byte piece of one
+//      (token, layer, head) row; a K row is head_dim consecutive scalars of
+//      the token-major tile, so neighbouring lanes copy neighbouring pieces.
+//   V tasks, appends of fewer than kVBlockedMinTokens tokens (token
+//      fastest): one thread moves one 16-byte piece of one row into the
+//      dim-major V tile, head_dim scalars P apart;
+//   V tasks, larger appends (piece, then 8 token groups, then head, then layer
+//      fastest): one thread moves piece c of 16 / es consecutive tokens' rows,
+//      as kv_append does (append_v_block).
 __global__ __launch_bounds__(256) void kv_append_bundle_kernel(BundleAppendArgs a) {
   const int32_t t = (int32_t)(blockIdx.x * 256u + threadIdx.x);
   if (t >= a.total) return;
@@ -51,7 +56,7 @@ __global__ __launch_bounds__(256) void kv_append_bundle_kernel(BundleAppendArgs 
     const int64_t blk = s >> G.log2P, off = s & (P - 1);
     *reinterpret_cast<u32x4*>(G.k + (l * G.k_sl + blk * G.k_sb + h * G.k_sh + off * D) * es +
                               16 * c) = val;
-  } else {
+  } else if (a.n < kVBlockedMinTokens) {
     local -= G.per_kind;
     const int i = local % a.n;
     int32_t r = local / a.n;
@@ -76,6 +81,29 @@ __global__ __launch_bounds__(256) void kv_append_bundle_kernel(BundleAppendArgs 
 #pragma unroll
       for (int e = 0; e < 4; ++e) dst[(int64_t)e * P] = piece[e];
     }
+  } else {
+    // V: piece c of a group of 16 / es tokens, the groups in runs of 8 inside
+    // two neighbouring waves (append_v_block).
+    local -= G.per_kind;
+    if (local >= G.v_tasks) return;
+    const int c = local % pieces;
+    int32_t r = local / pieces;
+    const int gl = r % kVGroupRun;
+    r /= kVGroupRun;
+    const int h = r % H;
+    r /= H;
+    const int l = r % L;
+    const int64_t i0 = ((int64_t)(r / L) * kVGroupRun + gl) * (16 / es);
+    if (i0 >= a.n) return;
+    const int64_t row = (int64_t)L * H * D;                       // scalars between tokens
+    const int64_t src0 = ((int64_t)l * H + h) * D + (int64_t)c * (16 / es);
+    const int64_t dst0 = l * G.v_sl + h * G.v_sh + (int64_t)c * (16 / es) * P;
+    if (es == 2)
+      append_v_block<uint16_t>(reinterpret_cast<const uint16_t*>(G.v_new) + src0, row, G.slots,
+                               i0, a.n, reinterpret_cast<uint16_t*>(G.v) + dst0, G.v_sb, G.log2P);
+    else
+      append_v_block<uint32_t>(reinterpret_cast<const uint32_t*>(G.v_new) + src0, row, G.slots,
+                               i0, a.n, reinterpret_cast<uint32_t*>(G.v) + dst0, G.v_sb, G.log2P);
   }
 }
 

@@ -18,9 +18,9 @@ struct GroupAppend {
   const int64_t* slots;   // [n]
   int64_t k_sl, k_sb, k_sh, v_sl, v_sb, v_sh;
   int32_t task0;          // first task of the group: K tasks, then V tasks
-  int32_t per_kind;       // n * layers * heads * pieces
+  int32_t per_kind;       // K tasks: n * layers * heads * pieces
+  int32_t v_tasks;        // V tasks: token groups (runs of 8) * layers * heads * pieces
   int32_t layers, heads, head_dim, log2P, esize;
-  int32_t pad;
 };
 
 struct BundleAppendArgs {

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "bundle_internal.h"
+#include "append_internal.h"
 #include "pba_internal.h"
 #include "vkv_internal.h"
 
@@ -303,7 +304,10 @@ int pba_kv_append(const pba_kv_pool* pool, const int64_t* slot_mapping, int64_t 
   if (n_tokens == 0) return PBA_OK;
   if (!slot_mapping || !k_new || !v_new) return PBA_ERR_NULL_ARG;
   if (!aligned16(k_new) || !aligned16(v_new)) return PBA_ERR_UNSUPPORTED;
-  const int64_t tasks = 2 * n_tokens * pool->num_kv_heads * (pool->head_dim * esize_of(pool->dtype) / 16);
+  // K tasks: one per 16-byte piece; V tasks: one per piece of E tokens (runs
+  // of 8 groups), at most n_tokens + 64 tokens' worth.
+  const int64_t tasks =
+      (2 * n_tokens + 64) * pool->num_kv_heads * (pool->head_dim * esize_of(pool->dtype) / 16);
   if ((tasks + 255) / 256 > INT32_MAX) return PBA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g_validate.load()) {
@@ -400,8 +404,9 @@ int pba_kv_append_bundle(const pba_kv_group* groups, int32_t num_groups,
     const pba_kv_pool& p = groups[g].pool;
     tasks_per_token += 2LL * groups[g].num_layers * p.num_kv_heads * (p.head_dim * esize_of(p.dtype) / 16);
   }
-  // Tokens per launch: every task index of a launch fits in int32.
-  const int64_t chunk = std::min<int64_t>(n_tokens, (INT32_MAX - 256) / tasks_per_token);
+  // Tokens per launch: every task index of a launch fits in int32 (the V
+  // tasks of a group cover up to 64 tokens past the launch's).
+  const int64_t chunk = std::min<int64_t>(n_tokens, (INT32_MAX - 256) / tasks_per_token - 64);
   if (chunk < 1) return PBA_ERR_UNSUPPORTED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (g_validate.load()) {
@@ -452,8 +457,12 @@ int pba_kv_append_bundle(const pba_kv_group* groups, int32_t num_groups,
       A.log2P = log2_exact(p.block_size);
       A.esize = es;
       A.task0 = (int32_t)task;
-      A.per_kind = (int32_t)(n * G.num_layers * p.num_kv_heads * (p.head_dim * es / 16));
-      task += 2LL * A.per_kind;
+      const int64_t lhp = (int64_t)G.num_layers * p.num_kv_heads * (p.head_dim * es / 16);
+      A.per_kind = (int32_t)(n * lhp);
+      A.v_tasks = (int32_t)((n < pba::kVBlockedMinTokens ? n
+                             : es == 2 ? pba::v_append_groups<uint16_t>(n)
+                                       : pba::v_append_groups<uint32_t>(n)) * lhp);
+      task += (int64_t)A.per_kind + A.v_tasks;
     }
     a.total = (int32_t)task;
     if (pba::launch_kv_append_bundle(a, s) != hipSuccess) return PBA_ERR_HIP;
