@@ -13,8 +13,8 @@
 //      V tile is dim major ([d][P]), so the row becomes d scalars P apart.
 //   V tasks of a larger append (piece fastest, then 8 token groups, then
 //      head): one thread moves an E x E block -- piece c of the rows of E
-//      consecutive tokens -- and transposes it in registers.  The V tile is dim major ([d][P]), so when
-//      the E tokens' slots are consecutive and start at a multiple of E (a
+//      consecutive tokens -- and transposes it in registers.  When the E
+//      tokens' slots are consecutive and start at a multiple of E (a
 //      prefill), each of the E dims becomes one 16-byte store; otherwise the
 //      block's scalars are stored one by one.  Neighbouring lanes read
 //      neighbouring pieces of a row, and the 8 groups of 8 E consecutive
