@@ -379,8 +379,14 @@ def run_workload(args, name, pba, torch, dev):
                           for r, T in enumerate(plan.seq_lens)], dtype=np.int64)
     row_of_slot = {int(sl): r for r, sl in enumerate(last_slot)}
     step_row = [row_of_slot.get(int(sl), -1) for sl in plan.step_slots]
+    # ... in a block no other row of the batch reads (the copy-on-write rule).
+    refs = {}
+    for r, T in enumerate(plan.seq_lens):
+        for b in plan.tables[r, :-(-int(T) // P)]:
+            refs[int(b)] = refs.get(int(b), 0) + 1
     fusable = (len(plan.step_slots) > 0 and min(step_row) >= 0 and
-               len(set(step_row)) == len(step_row))
+               len(set(step_row)) == len(step_row) and
+               all(refs[int(sl) // P] == 1 for sl in plan.step_slots))
     tables, lens_h = plan.tables, plan.seq_lens
     # Shared-prefix execution: the caller orders the batch so rows sharing
     # leading blocks are adjacent and describes the shared chunks.
@@ -395,6 +401,12 @@ def run_workload(args, name, pba, torch, dev):
             cand.private_tokens = 0
         if path == "shared" or any(b - a > 1 for a, b, _, _ in cand.chunks):
             tables, lens_h, qb, host_plan = tables[order], lens_h[order], qb[order], cand
+            # Decode rows in sharing order; the fused step also needs each new
+            # token inside its row's private range.
+            pos = np.empty(B, dtype=np.int64)
+            pos[order] = np.arange(B)
+            step_row = [int(pos[r]) for r in step_row]
+            fusable = fusable and all(cand.row_private[r, 0] <= lens_h[r] - 1 for r in step_row)
     path = "shared" if host_plan is not None else "plain"
     q = dev_bits(qb)
     tab_d = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)
@@ -449,8 +461,7 @@ def run_workload(args, name, pba, torch, dev):
     # Zero-filled once: the library keeps the completion counters at zero.
     ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    fused = (args.step == "fused" and fusable and host_plan is None and row_offsets is None
-             and not args.decode_only)
+    fused = (args.step == "fused" and fusable and row_offsets is None and not args.decode_only)
     if fused:
         ns = np.full(B, -1, dtype=np.int64)
         ns[step_row] = plan.step_slots
@@ -463,7 +474,10 @@ def run_workload(args, name, pba, torch, dev):
     torch.cuda.synchronize()
 
     def decode(st=stream):
-        if fused:   # the step's call: appends its new tokens again (same bytes, same slots)
+        if fused and host_plan is not None:   # (each call appends the same bytes again)
+            pba.paged_decode_shared_append(pool, new_slots, knew, vnew, q, tab_d, lens_d, splan,
+                                           scale, out=out, lse=lse, workspace=ws, stream=st)
+        elif fused:
             pba.paged_decode_append(dpool, new_slots, knew, vnew, q, tab_d, lens_d, scale,
                                     out=out, lse=lse, partition_tokens=req_pt, workspace=ws,
                                     stream=st)
@@ -603,8 +617,9 @@ def run_workload(args, name, pba, torch, dev):
                     "private_ranges": "four rows per work-group"
                     if 0 < host_plan.private_tokens <= 128 else "a work-group per piece"},
                    "step": f"block_copy({len(plan.step_src)} pairs) + " +
-                           (f"paged_decode_append({len(plan.step_slots)} new tokens appended "
-                            f"in the decode launch)" if fused else
+                           (f"{'paged_decode_shared_append' if host_plan is not None else 'paged_decode_append'}"
+                            f"({len(plan.step_slots)} new tokens appended in the decode launch)"
+                            if fused else
                             f"kv_append({len(plan.step_slots)} tokens) + "
                             f"{'paged_decode_shared' if host_plan is not None else 'paged_decode'}"),
                    "step_fused": fused,
@@ -635,7 +650,8 @@ def run_workload(args, name, pba, torch, dev):
                      "frac_cold": None if cold1_ms is None else
                      round(alg_bytes / (cold1_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": (f"decode_bf16_shared_kernel<{d}> (chunk-first + sequence-first, "
-                                "merge fused in)") if host_plan is not None else
+                                "merge fused in" + (", the step's appends too)" if fused else ")"))
+                     if host_plan is not None else
                                (f"decode_bf16_flat_kernel<{d}> (balanced chunk ranges, cut rows "
                                 "merged in)" if flat else
                                 f"decode_{sh.dtype}_kernel<{d}> (partition merge fused in"

@@ -145,6 +145,9 @@ _SIGS = {
     "pba_paged_decode_shared_workspace_bytes": (_sz, [_P, _i32, _i32, _i32, _SP]),
     "pba_paged_decode_shared": (ctypes.c_int, [_P, _vp, _i32, _vp, _i32, _vp, _i32, ctypes.c_float,
                                                _vp, _vp, _SP, _vp, _sz, _vp]),
+    "pba_paged_decode_shared_append": (ctypes.c_int, [_P, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                                      _vp, _i32, ctypes.c_float, _vp, _vp, _SP,
+                                                      _vp, _sz, _vp]),
     "pba_group_layer_pool": (ctypes.c_int, [_GP, _i32, _P]),
     "pba_kv_append_bundle": (ctypes.c_int, [_GP, _i32, _vp, _vp, _vp, _i64, _vp]),
     "pba_block_copy_bundle": (ctypes.c_int, [_GP, _i32, _vp, _vp, _vp, _vp]),
@@ -620,6 +623,58 @@ def paged_decode_shared(pool: KVPool, q: torch.Tensor, block_tables: torch.Tenso
         pool._ref, q.data_ptr(), Hq, block_tables.data_ptr(), max_blocks, seq_lens.data_ptr(), B,
         ctypes.c_float(scale), out.data_ptr(), None if lse is None else lse.data_ptr(),
         plan._ref, ws_ptr, ws_bytes, _stream(stream)))
+    return out, lse
+
+
+def paged_decode_shared_append(pool: KVPool, new_slots: torch.Tensor, k_new: torch.Tensor,
+                               v_new: torch.Tensor, q: torch.Tensor, block_tables: torch.Tensor,
+                               seq_lens: torch.Tensor, plan: SharedPlan,
+                               scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                               lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                               workspace: Optional[torch.Tensor] = None, stream=None):
+    """One shared-prefix decode step: row r's new token (new_slots[r], its
+    last position, inside its private range, or negative for none; k_new /
+    v_new [B, H_kv, d], rows in the batch's order) is appended and the batch
+    decoded in one call -- the same result as kv_append then
+    paged_decode_shared."""
+    dev = pool.device
+    _require(q, "q", pool.dtype, dev, 3)
+    _require(block_tables, "block_tables", torch.int32, dev, 2)
+    _require(seq_lens, "seq_lens", torch.int32, dev, 1)
+    _require(new_slots, "new_slots", torch.int64, dev, 1)
+    _require(k_new, "k_new", pool.dtype, dev, 3)
+    _require(v_new, "v_new", pool.dtype, dev, 3)
+    B, Hq, D = q.shape
+    if D != pool.head_dim or block_tables.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, block_tables, seq_lens and the pool")
+    if new_slots.shape[0] != B or tuple(k_new.shape) != (B, pool.num_kv_heads, D) \
+            or k_new.shape != v_new.shape:
+        raise ValueError("new_slots [B] and k_new / v_new [B, H_kv, d] must match the batch")
+    if plan.row_private.shape[0] != B:
+        raise ValueError("the plan describes another batch")
+    max_blocks = block_tables.shape[1]
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    else:
+        _require(out, "out", torch.float32, dev, 3)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    elif lse is not None:
+        _require(lse, "lse", torch.float32, dev, 2)
+    if workspace is None and B > 0:
+        need = paged_decode_shared_workspace_bytes(pool, Hq, B, max_blocks, plan)
+        if need:
+            layout = ("shared", B, pool.num_kv_heads, Hq, D, plan.max_slots)
+            workspace = _cached_workspace(dev, stream, layout, need)
+    ws_ptr = None if workspace is None else workspace.data_ptr()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("pba_paged_decode_shared_append", _lib.pba_paged_decode_shared_append(
+        pool._ref, new_slots.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), q.data_ptr(), Hq,
+        block_tables.data_ptr(), max_blocks, seq_lens.data_ptr(), B, ctypes.c_float(scale),
+        out.data_ptr(), None if lse is None else lse.data_ptr(), plan._ref, ws_ptr, ws_bytes,
+        _stream(stream)))
     return out, lse
 
 

@@ -1294,11 +1294,15 @@ __device__ __forceinline__ void chunk_step_nt(const PoolView& pv, int h, int t0,
 // chunks and each wave serves all NT tiles of its group from one K/V load,
 // so a wave walks piece / (32 * waves per group) chunks whatever the tiles.
 // The states go through LDS one tile of each group at a time.
-template <int D, int NT>
+// kFused (a fused step's kernel) and new_slot >= 0 (a private piece holding
+// its row's position te - 1): the wave that reads te - 1 first writes the
+// row's new token there, as the grid kernel does.
+template <int D, int NT, bool kFused = false>
 __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& st, int* s_slots,
                                             const PoolView& pv, int h, int row0, int nrows, int tb,
                                             int te, int tiles, int slot, int rT, int rpb, int rps,
-                                            int part_tokens, int wave, int n, int g) {
+                                            int part_tokens, int wave, int n, int g,
+                                            int64_t new_slot = -1) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
   constexpr int CH = 32;
@@ -1318,6 +1322,22 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
   const int n_w = (span > 0 && ncols[0] > 0) ? (span + stride - 1) / stride : 0;
 
   int t0 = first;
+  // Fused append: the chunk holding te - 1 is this wave's if it is one of
+  // first + k stride.
+  const int lane = threadIdx.x & 63;
+  NewToken nt;
+  nt.slot = -1;
+  int t_new = -1;
+  if (kFused && new_slot >= 0 && n_w > 0) {
+    const int c_new = (te - 1 - tb) / CH;
+    if (c_new % wpg == sub) {
+      nt.slot = new_slot;
+      t_new = tb + c_new * CH;
+    }
+  }
+  // The token's rows are requested with the chunk's table entries, so a
+  // write into the wave's first chunk costs no round trip of its own.
+  if (kFused && t_new >= 0) load_new_token<D>(nt, a, row0, h, lane);
   u32x4 qraw[NT][KK];
   u32x4 kf[2][KK];
   u32x4 vf[MT];
@@ -1325,6 +1345,10 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
     int64_t pb0, pb1;
     chunk_blocks(pv, t0, pb0, pb1);
     if (t0 + 16 >= te) pb1 = pb0;  // no block past the piece's last one is read
+    if (kFused && t_new == first) {  // the wave's first chunk: written before its loads
+      store_new_token<D>(nt, pv, h, lane);
+      t_new = -1;
+    }
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
       const int cn = n < ncols[j] ? n : 0;
@@ -1358,6 +1382,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
   for (int it = 0; it < n_w; ++it, t0 += stride) {
     const bool more = it + 1 < n_w;
     const int tn = more ? t0 + stride : t0;
+    if (kFused && tn == t_new && more) store_new_token<D>(nt, pv, h, lane);
     chunk_step_nt<D, NT>(pv, h, t0, tn, te, ncols, abs_scale(a.scale_log2), qf, kf, vf, m_run, l_run, acc, n,
                          g, more);
   }
@@ -1433,7 +1458,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
 // row0 + w's positions [pb, T) alone and writes the state to the row's slot,
 // or the row itself when that is its only slot.  s_slots[w] gets the row's
 // slot count, 0 when the row has no private position (nothing to count).
-template <int D>
+template <int D, bool kFused>
 __device__ __forceinline__ void packed_private(const DecodeArgs& a, const SharedArgs& sa,
                                                int* s_slots, const int32_t* tables,
                                                const PoolView& pv0, int h, int row0, int nrows,
@@ -1444,10 +1469,17 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
   const int G = a.G;
   const int r = row0 + wave;
   int T = 0, pb = 0, ps = -1;
+  // Fused step: the row's new slot and rows are requested with its length.
+  NewToken nt;
+  nt.slot = -1;
   if (wave < nrows) {
     T = a.seq_lens[r];
     pb = sa.row_private[2 * r];
     ps = sa.row_private[2 * r + 1];
+    if (kFused) {
+      nt.slot = a.new_slots[r];
+      load_new_token<D>(nt, a, r, h, lane);
+    }
   }
   const bool work = wave < nrows && pb >= 0 && pb < T && ps >= 0 && ps < a.n_parts;
   const int ns = work ? min(ps + (T - pb + part_tokens - 1) / part_tokens, a.n_parts) : 0;
@@ -1457,6 +1489,9 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
   PoolView pv = pv0;
   pv.trow = (table_t*)(tables + (int64_t)r * pv0.max_blocks);
   const int ncols[1] = {G};
+  // Fused append: the row's new token, at position T - 1 of this range, is
+  // written just before the wave requests the chunk holding it.
+  const int t_new = kFused && nt.slot >= 0 ? pb + (T - 1 - pb) / CH * CH : -1;
   u32x4 qraw[1][KK];
   u32x4 kf[2][KK];
   u32x4 vf[MT];
@@ -1464,6 +1499,7 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
     int64_t pb0, pb1;
     chunk_blocks(pv, pb, pb0, pb1);
     if (pb + 16 >= T) pb1 = pb0;  // no block past the row's last one is read
+    if (kFused && t_new == pb) store_new_token<D>(nt, pv, h, lane);
     const uint16_t* qrow = static_cast<const uint16_t*>(a.q) +
                            ((int64_t)r * a.num_q_heads + (int64_t)h * G + (n < G ? n : 0)) * D;
 #pragma unroll
@@ -1488,6 +1524,7 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
   int t0 = pb;
   for (int it = 0; it < n_w; ++it, t0 += CH) {
     const bool more = it + 1 < n_w;
+    if (kFused && more && t0 + CH == t_new) store_new_token<D>(nt, pv, h, lane);
     chunk_step_nt<D, 1>(pv, h, t0, more ? t0 + CH : t0, T, ncols, abs_scale(a.scale_log2), qf, kf,
                         vf, m_run, l_run, acc, n, g, more);
   }
@@ -1515,7 +1552,9 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
   }
 }
 
-template <int D>
+// kFused: a fused step (a.new_slots set), in a kernel of its own so that the
+// plain decode keeps its registers.
+template <int D, bool kFused>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
     const void* __restrict__ kbase, const void* __restrict__ vbase, int32_t max_blocks,
@@ -1536,6 +1575,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   const int rpt = 16 / G;  // rows per 16-column tile
 
   int row0, nrows, tb = 0, te = 0, slot = 0, tiles = 1;
+  int64_t new_slot = -1;  // fused step: the row's new token, for its last private piece
   bool packed = false;
   if ((int)blockIdx.z < sa.nz_items) {
     const int fa = blockIdx.y + gridDim.y * blockIdx.z;
@@ -1566,6 +1606,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     item_t* rp = (item_t*)(sa.row_private + 2 * (int64_t)r);
     const int T = seq_lens[r];
     const int pbeg = rp[0];
+    // Fused step: the row's new slot, requested with its length.
+    const int64_t slot_r =
+        kFused ? ((const int64_t __attribute__((address_space(4)))*)a.new_slots)[r] : -1;
     tb = pbeg + part * part_tokens;
     if (tb >= T || pbeg < 0) return;  // empty piece: never counted, never read
     te = min(T, tb + part_tokens);
@@ -1573,6 +1616,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
     nrows = 1;
     slot = rp[1] + part;
     tiles = 1;
+    if (kFused && te == T) new_slot = slot_r;
   }
   if (slot < 0 || slot >= a.n_parts) return;
   // Length and private range of the item's rows: requested now, used after
@@ -1589,13 +1633,13 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
                     static_cast<const uint16_t*>(kbase), static_cast<const uint16_t*>(vbase),
                     k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P, a.split_log2};
   if (packed)
-    packed_private<D>(a, sa, s_slots, tables, pv, h, row0, nrows, part_tokens, wave, lane, n, g);
+    packed_private<D, kFused>(a, sa, s_slots, tables, pv, h, row0, nrows, part_tokens, wave, lane, n, g);
   else if (tiles >= 2)
     shared_item<D, 2>(a, st, s_slots, pv, h, row0, nrows, tb, te, tiles, slot, rT, rpb, rps,
                       part_tokens, wave, n, g);
   else
-    shared_item<D, 1>(a, st, s_slots, pv, h, row0, nrows, tb, te, tiles, slot, rT, rpb, rps,
-                      part_tokens, wave, n, g);
+    shared_item<D, 1, kFused>(a, st, s_slots, pv, h, row0, nrows, tb, te, tiles, slot, rT, rpb,
+                              rps, part_tokens, wave, n, g, new_slot);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);  // this wave's state stores are complete
   __syncthreads();
   if ((int)threadIdx.x < nrows) {
@@ -1852,7 +1896,10 @@ hipError_t launch_paged_decode_shared(const DecodeArgs& a, const SharedArgs& sa,
   const dim3 grid((unsigned)a.num_kv_heads, (unsigned)a.batch,
                   (unsigned)(sa.nz_items + private_parts));
   const dim3 block(kDecodeThreads);
-  auto kern = head_dim == 128 ? decode_bf16_shared_kernel<128> : decode_bf16_shared_kernel<64>;
+  auto kern = a.new_slots ? (head_dim == 128 ? decode_bf16_shared_kernel<128, true>
+                                              : decode_bf16_shared_kernel<64, true>)
+                          : (head_dim == 128 ? decode_bf16_shared_kernel<128, false>
+                                              : decode_bf16_shared_kernel<64, false>);
   hipLaunchKernelGGL(kern, grid, block, 0, stream, a.tables, a.seq_lens, a.k, a.v, a.max_blocks,
                      a.part_tokens, a.log2P, a.num_blocks - 1, (int32_t)a.k_sb, (int32_t)a.k_sh, a,
                      sa);

@@ -8,6 +8,7 @@
 #include <atomic>
 #include <cstring>
 #include <mutex>
+#include <unordered_map>
 #include <unordered_set>
 #include <vector>
 
@@ -644,6 +645,34 @@ int pba_paged_decode_plan_ex(const pba_kv_pool* pool, int32_t num_q_heads, int32
 
 namespace pba {
 
+// Validate mode, fused steps: each new token is its row's position T - 1
+// through the row's table (block_of(r, j) = row r's j-th block), the slots
+// are distinct, and no other row of the batch references a new token's block
+// (a block that several rows share is copied before it is written, so a new
+// position is visible to its own row alone and no work-group reads it while
+// another writes it).
+template <typename BlockOf>
+int check_new_tokens(const std::vector<int64_t>& ns, const std::vector<int32_t>& lens,
+                     int32_t batch, int P, BlockOf block_of) {
+  std::unordered_set<int64_t> seen;
+  std::unordered_map<int64_t, int32_t> owner;
+  for (int32_t r = 0; r < batch; ++r) {
+    if (ns[r] < 0) continue;
+    const int64_t t = lens[r] - 1;
+    const int64_t blk = block_of(r, t / P);
+    if (ns[r] != blk * P + t % P) return PBA_ERR_OUT_OF_RANGE;
+    if (!seen.insert(ns[r]).second || !owner.emplace(blk, r).second) return PBA_ERR_OVERLAP;
+  }
+  for (int32_t r = 0; r < batch && !owner.empty(); ++r) {
+    const int64_t nb = (lens[r] + P - 1) / P;
+    for (int64_t j = 0; j < nb; ++j) {
+      const auto it = owner.find(block_of(r, j));
+      if (it != owner.end() && it->second != r) return PBA_ERR_OVERLAP;
+    }
+  }
+  return PBA_OK;
+}
+
 // Dense (row r at r * max_blocks_per_seq), ragged (row r =
 // block_tables[row_offsets[r] .. row_offsets[r + 1])) or contiguous
 // (block_tables = slot index, max_blocks_per_seq = blocks per slot) decode.
@@ -734,23 +763,14 @@ int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
       if ((st = pba::vkv_check_blocks(pool->k, tab.data() + base, nb))) return st;
     }
     if (fused) {
-      // Each new token is its row's position T - 1 through the row's table
-      // (or slot); slots distinct.
       std::vector<int64_t> ns;
       if (!copy_to_host(ns, fused->slots, batch, s)) return PBA_ERR_HIP;
-      std::unordered_set<int64_t> seen;
-      const int P = pool->block_size;
-      for (int32_t r = 0; r < batch; ++r) {
-        if (ns[r] < 0) continue;
-        const int64_t t = lens[r] - 1;
-        int64_t blk;
-        if (mode == pba::kTablesContiguous)
-          blk = (int64_t)tab[r] * max_blocks_per_seq + t / P;
-        else
-          blk = tab[(size_t)((row_offsets ? offs[r] : (int64_t)r * max_blocks_per_seq) + t / P)];
-        if (ns[r] != blk * P + t % P) return PBA_ERR_OUT_OF_RANGE;
-        if (!seen.insert(ns[r]).second) return PBA_ERR_OVERLAP;
-      }
+      const int64_t mb = max_blocks_per_seq;
+      st = check_new_tokens(ns, lens, batch, pool->block_size, [&](int32_t r, int64_t j) {
+        if (mode == pba::kTablesContiguous) return (int64_t)tab[r] * mb + j;
+        return (int64_t)tab[(size_t)((row_offsets ? offs[r] : r * mb) + j)];
+      });
+      if (st) return st;
     }
   }
   pba::DecodeArgs a;
@@ -1025,11 +1045,16 @@ size_t pba_paged_decode_shared_workspace_bytes(const pba_kv_pool* pool, int32_t 
                           plan->max_slots, pool->head_dim).bytes;
 }
 
-int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
-                            const int32_t* block_tables, int32_t max_blocks_per_seq,
-                            const int32_t* seq_lens, int32_t batch, float scale, float* out,
-                            float* lse, const pba_shared_plan* plan, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// pba_paged_decode_shared, and with `fused` pba_paged_decode_shared_append.
+int shared_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                  int32_t batch, float scale, float* out, float* lse, const pba_shared_plan* plan,
+                  void* workspace, size_t workspace_bytes, void* stream,
+                  const pba::NewTokens* fused) {
   int st = check_decode_shape(pool, num_q_heads, batch, max_blocks_per_seq);
   if (st) return st;
   int32_t nz = 0, pp = 0, npk = 0;
@@ -1038,6 +1063,8 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
   if (batch == 0) return PBA_OK;
   if (!q || !block_tables || !seq_lens || !out) return PBA_ERR_NULL_ARG;
   if (!aligned16(q)) return PBA_ERR_UNSUPPORTED;
+  if (fused && (!fused->slots || !fused->k || !fused->v)) return PBA_ERR_NULL_ARG;
+  if (fused && (!aligned16(fused->k) || !aligned16(fused->v))) return PBA_ERR_UNSUPPORTED;
   const int64_t rows = (int64_t)batch * num_q_heads;
   const WsLayout ws = workspace_layout(batch, pool->num_kv_heads, rows, plan->max_slots,
                                        pool->head_dim);
@@ -1060,6 +1087,21 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
     }
     st = validate_shared_plan(pool, num_q_heads, batch, max_blocks_per_seq, plan, lens, tab, s);
     if (st) return st;
+    if (fused) {
+      // Besides check_new_tokens: the new position lies in the row's private
+      // range (a chunk's work-groups do not write).
+      std::vector<int64_t> ns;
+      std::vector<int32_t> priv;
+      if (!copy_to_host(ns, fused->slots, batch, s)) return PBA_ERR_HIP;
+      if (!copy_to_host(priv, plan->row_private, (int64_t)batch * 2, s)) return PBA_ERR_HIP;
+      for (int32_t r = 0; r < batch; ++r)
+        if (ns[r] >= 0 && priv[2 * (size_t)r] > lens[r] - 1) return PBA_ERR_OUT_OF_RANGE;
+      const int64_t mb = max_blocks_per_seq;
+      st = pba::check_new_tokens(ns, lens, batch, pool->block_size, [&](int32_t r, int64_t j) {
+        return (int64_t)tab[(size_t)(r * mb + j)];
+      });
+      if (st) return st;
+    }
   }
   pba::DecodeArgs a;
   a.k = pool->k;
@@ -1090,8 +1132,9 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
   a.part_tokens = plan->partition_tokens;
   a.n_parts = plan->max_slots;
   a.scale_log2 = scale * 1.4426950408889634f;
-  a.new_slots = nullptr;
-  a.k_new = a.v_new = nullptr;
+  a.new_slots = fused ? fused->slots : nullptr;
+  a.k_new = fused ? fused->k : nullptr;
+  a.v_new = fused ? fused->v : nullptr;
   pba::SharedArgs sa;
   sa.items = plan->items;
   sa.row_private = plan->row_private;
@@ -1101,6 +1144,31 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
   return pba::launch_paged_decode_shared(a, sa, pool->head_dim, (int)pp, s) == hipSuccess
              ? PBA_OK
              : PBA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
+                            const int32_t* block_tables, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t batch, float scale, float* out,
+                            float* lse, const pba_shared_plan* plan, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return shared_decode(pool, q, num_q_heads, block_tables, max_blocks_per_seq, seq_lens, batch,
+                       scale, out, lse, plan, workspace, workspace_bytes, stream, nullptr);
+}
+
+int pba_paged_decode_shared_append(const pba_kv_pool* pool, const int64_t* new_slots,
+                                   const void* k_new, const void* v_new, const void* q,
+                                   int32_t num_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t batch, float scale, float* out, float* lse,
+                                   const pba_shared_plan* plan, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  const pba::NewTokens fused{new_slots, k_new, v_new};
+  return shared_decode(pool, q, num_q_heads, block_tables, max_blocks_per_seq, seq_lens, batch,
+                       scale, out, lse, plan, workspace, workspace_bytes, stream, &fused);
 }
 
 }  // extern "C"

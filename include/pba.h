@@ -287,8 +287,13 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
  *                 new_slots[r] (negative: row r appends nothing this step).
  *                 That slot must be row r's last position, T_r - 1, through
  *                 its block table (block_tables[r][(T_r - 1) / P] * P +
- *                 (T_r - 1) % P); validate mode checks it (PBA_ERR_OUT_OF_RANGE)
- *                 and that slots are distinct (PBA_ERR_OVERLAP)
+ *                 (T_r - 1) % P), in a block no other row of the batch
+ *                 references (a shared block is copied before it is written,
+ *                 so no work-group reads a position another one writes).
+ *                 Validate mode checks the position (PBA_ERR_OUT_OF_RANGE),
+ *                 that slots are distinct and that the block is the row's
+ *                 alone (PBA_ERR_OVERLAP); outside it, another slot is
+ *                 undefined
  *   k_new, v_new  device [batch, num_kv_heads, head_dim], pool dtype,
  *                 contiguous, 16-byte aligned: the new tokens' K and V rows
  * Other arguments as pba_paged_decode (the same workspace size).  bf16 pools
@@ -584,6 +589,26 @@ int pba_paged_decode_shared(const pba_kv_pool* pool, const void* q, int32_t num_
                             const int32_t* seq_lens, int32_t batch, float scale, float* out,
                             float* lse, const pba_shared_plan* plan, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* pba_paged_decode_shared_append -- one shared-prefix decode step: the
+ * step's new tokens appended and the batch decoded in one launch, as
+ * pba_paged_decode_append does for pba_paged_decode ("M5.3", 0x03C-0x03D:
+ * slot s is block s div P, offset s mod P; 0x0BA-0x0BE: the shared-prefix
+ * decode).  new_slots, k_new, v_new: as pba_paged_decode_append, rows in the
+ * batch's (sharing) order and under the same rules (the row's position
+ * T - 1, in a block only that row references); the position must also lie
+ * in the row's private range (row_private pb <= T - 1: a chunk's blocks are
+ * shared), where the wave that reads T - 1 writes it first.  Validate mode
+ * checks all three (PBA_ERR_OUT_OF_RANGE, PBA_ERR_OVERLAP) with nothing
+ * written; outside it, a slot elsewhere is undefined.  Other arguments as
+ * pba_paged_decode_shared. */
+int pba_paged_decode_shared_append(const pba_kv_pool* pool, const int64_t* new_slots,
+                                   const void* k_new, const void* v_new, const void* q,
+                                   int32_t num_q_heads, const int32_t* block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                                   int32_t batch, float scale, float* out, float* lse,
+                                   const pba_shared_plan* plan, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 /*
  * Contiguous virtual K/V ("M5.3", 0x06A-0x06F; vAttention): a second kernel

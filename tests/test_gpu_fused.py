@@ -10,8 +10,8 @@ new token appended and the batch decoded in one call.
   their own launch), fp32 pools (likewise), rows that append nothing, rows
   whose new token falls in a wave's first chunk, a kernel view of an
   allocator pool, and the 8 x 16,384-token workload at full size.
-* Validate mode rejects a slot that is not the row's last position, with
-  nothing written.
+* Validate mode rejects a slot that is not the row's last position, and a
+  new token in a block another row references, with nothing written.
 Every case prints its name, shapes and seed (flushed) before its GPU work.
 """
 import math
@@ -171,3 +171,14 @@ def test_fused_step_validate_rejects(pba, gpu):
         torch.cuda.synchronize()
         assert torch.equal(pool.k.view(torch.int16), kb.view(torch.int16))
         assert torch.equal(pool.v.view(torch.int16), vb.view(torch.int16))
+    # Row 1's table made to reference row 0's last block: row 0's new token
+    # would be visible to row 1 (a shared block is copied before a write).
+    shared = ex.tables.copy()
+    shared[1][0] = shared[0][(lengths[0] - 1) // 16]
+    with pytest.raises(pba.PBAError) as e:
+        pba.paged_decode_append(pool, torch.from_numpy(good).to(gpu), knew, vnew, q,
+                                torch.from_numpy(shared).to(gpu), lens)
+    assert e.value.status == -7
+    torch.cuda.synchronize()
+    assert torch.equal(pool.k.view(torch.int16), kb.view(torch.int16))
+    assert torch.equal(pool.v.view(torch.int16), vb.view(torch.int16))
