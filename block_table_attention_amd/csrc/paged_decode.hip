@@ -88,6 +88,12 @@ __device__ __forceinline__ void st_state(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Two neighbouring state words in one 8-byte store (p 8-byte aligned).
+__device__ __forceinline__ void st_state2(float* p, float lo, float hi) {
+  const uint64_t v = (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float ld_state(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -1444,10 +1450,7 @@ __device__ __forceinline__ void shared_item(const DecodeArgs& a, WaveStates<D>& 
         const int64_t prow = row * a.n_parts + slot;
 #pragma unroll
         for (int e = 0; e < 4; ++e) st_state(a.ws_u + prow * D + c + C4 * e, O[e]);
-        if (c == 0) {
-          st_state(a.ws_ml + prow * 2 + 0, M);
-          st_state(a.ws_ml + prow * 2 + 1, L);
-        }
+        if (c == 0) st_state2(a.ws_ml + prow * 2, M, L);
       }
     }
   }
@@ -1462,7 +1465,8 @@ template <int D, bool kFused>
 __device__ __forceinline__ void packed_private(const DecodeArgs& a, const SharedArgs& sa,
                                                int* s_slots, const int32_t* tables,
                                                const PoolView& pv0, int h, int row0, int nrows,
-                                               int part_tokens, int wave, int lane, int n, int g) {
+                                               int part_tokens, int wave, int lane, int n, int g,
+                                               float (*o)[D + 4]) {
   constexpr int KK = D / 32;
   constexpr int MT = D / 16;
   constexpr int CH = 32;
@@ -1531,23 +1535,34 @@ __device__ __forceinline__ void packed_private(const DecodeArgs& a, const Shared
   float L = l_run[0] + __shfl_xor(l_run[0], 16, 64);
   L += __shfl_xor(L, 32, 64);
   const float M = m_run[0];
-  if (n >= G) return;
-  const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
   if (ns == 1) {
+    if (n >= G) return;
+    const int64_t row = (int64_t)r * a.num_q_heads + (int64_t)h * G + n;
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
       *reinterpret_cast<f32x4*>(a.out + row * D + 16 * mt + 4 * g) = acc[0][mt] * inv;
     if (a.lse && g == 0) a.lse[row] = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
   } else {
-    const int64_t prow = row * a.n_parts + ps;
+    // The state goes out through the wave's own LDS rows: each lane holds 4
+    // dims of a head 16 bytes apart from its neighbours', so stored directly
+    // every 64-byte write request would carry 16 bytes; read back, a store
+    // instruction writes whole runs of D words (8 bytes per lane).
+    const int64_t prow0 = ((int64_t)r * a.num_q_heads + (int64_t)h * G) * a.n_parts + ps;
+    if (n < G) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) st_state(a.ws_u + prow * D + 16 * mt + 4 * g + i, acc[0][mt][i]);
-    if (g == 0) {
-      st_state(a.ws_ml + prow * 2 + 0, M);
-      st_state(a.ws_ml + prow * 2 + 1, L);
+      for (int mt = 0; mt < MT; ++mt) *reinterpret_cast<f32x4*>(&o[n][16 * mt + 4 * g]) = acc[0][mt];
+      if (g == 0) st_state2(a.ws_ml + (prow0 + (int64_t)n * a.n_parts) * 2, M, L);
+    }
+    // The LDS writes of every lane precede the reads (one wave: in order).
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    for (int e = lane; e < G * (D / 2); e += 64) {
+      const int cn = e / (D / 2);
+      const int d = 2 * (e - cn * (D / 2));
+      const f32x2 v = *reinterpret_cast<const f32x2*>(&o[cn][d]);
+      st_state2(a.ws_u + (prow0 + (int64_t)cn * a.n_parts) * D + d, v[0], v[1]);
     }
   }
 }
@@ -1633,7 +1648,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
                     static_cast<const uint16_t*>(kbase), static_cast<const uint16_t*>(vbase),
                     k_sb, k_sh, a.v_sb, a.v_sh, max_blocks, last_block, log2P, a.split_log2};
   if (packed)
-    packed_private<D, kFused>(a, sa, s_slots, tables, pv, h, row0, nrows, part_tokens, wave, lane, n, g);
+    packed_private<D, kFused>(a, sa, s_slots, tables, pv, h, row0, nrows, part_tokens, wave, lane,
+                              n, g, st.o[wave]);
   else if (tiles >= 2)
     shared_item<D, 2>(a, st, s_slots, pv, h, row0, nrows, tb, te, tiles, slot, rT, rpb, rps,
                       part_tokens, wave, n, g);
