@@ -113,7 +113,8 @@ def test_fused_shared_prefix_step(pba, gpu, packed):
     run_case(pba, step_on(w, list(w.decode)), gpu, list(w.decode), pt=512, packed=packed)
 
 
-@pytest.mark.parametrize("G,P,d", [(4, 16, 128), (8, 32, 64), (1, 64, 128), (2, 256, 64)])
+@pytest.mark.parametrize("G,P,d", [(4, 16, 128), (8, 32, 64), (1, 64, 128), (2, 256, 64),
+                                   (16, 16, 128)])
 def test_fused_long_private_ranges(pba, gpu, G, P, d):
     """Private ranges of several 256-position pieces (no packing): the new
     token lies in a row's last piece, in the chunk of any of its four waves;
@@ -130,6 +131,58 @@ def test_fused_long_private_ranges(pba, gpu, G, P, d):
         leaves.append(1 + i)
     w.decode = leaves
     run_case(pba, step_on(w, leaves[::2]), gpu, leaves[::2], pt=256, packed=False)
+
+
+def _edge_workload(P, G, d, seed):
+    """Two forks of a two-block prefix (5 and 40 tokens of their own), and
+    three rows of their own: empty, P - 1 and P tokens before the step."""
+    Hkv = 2
+    w = wl.Workload(f"fused_edges_g{G}_p{P}_d{d}", wl.Shape(P, G * Hkv, Hkv, d, "bf16", 256), seed)
+    w.actions = [("new",), ("prefill", 0, 2 * P), ("fork", 0), ("fork", 0), ("release", 0),
+                 ("prefill", 1, 5), ("prefill", 2, 40),
+                 ("new",), ("prefill", 3, 0), ("new",), ("prefill", 4, P - 1),
+                 ("new",), ("prefill", 5, P)]
+    w.decode = [1, 2, 3, 4, 5]
+    return w
+
+
+@pytest.mark.parametrize("packed", [True, False])
+@pytest.mark.parametrize("tiles", [1, 2])
+@pytest.mark.parametrize("G,P,d", [(4, 16, 128), (2, 64, 64)])
+def test_fused_shared_edges(pba, gpu, packed, tiles, G, P, d):
+    """A row whose only position is the new token (T = 1), a new token at a
+    block's last offset (T = P) and at a fresh block's first (T = P + 1), a
+    shared-prefix row that appends and one that does not."""
+    w = _edge_workload(P, G, d, 20261202 + 9800 + G + P)
+    appending = [3, 4, 5, 2]
+    run_case(pba, step_on(w, appending), gpu, appending, pt=256, tiles=tiles, packed=packed)
+
+
+def test_fused_shared_no_new_tokens(pba, gpu):
+    """Every new slot negative: the pool is untouched and out / lse equal
+    paged_decode_shared's bit for bit."""
+    w = step_on(_edge_workload(16, 4, 128, 20261202 + 9900), [3, 4, 5, 2])
+    say(w.name, w.shape, "seed", w.seed, "no new tokens")
+    ex = execute(w)
+    k_rows, v_rows = wl.kv_rows(w, ex.n_writes)
+    pool = gpu_pool(ex, gpu)
+    gpu_replay(ex, pool, to_device(k_rows, "bf16", gpu), to_device(v_rows, "bf16", gpu))
+    order = sharing_order(ex.tables)
+    tables = np.ascontiguousarray(ex.tables[order])
+    lens = np.ascontiguousarray(ex.seq_lens[order])
+    plan = pba.SharedPlan.from_host(shared_plan(tables, lens, 16, 4, 256, tiles_per_item=2), gpu)
+    B = len(w.decode)
+    q = to_device(np.ascontiguousarray(wl.q_bits(w)[order]), "bf16", gpu)
+    tab, ln = torch.from_numpy(tables).to(gpu), torch.from_numpy(lens).to(gpu)
+    none = torch.full((B,), -1, dtype=torch.int64, device=gpu)
+    kn = torch.zeros((B, 2, 128), dtype=torch.bfloat16, device=gpu)
+    kb, vb = pool.k.clone(), pool.v.clone()
+    out, lse = pba.paged_decode_shared_append(pool, none, kn, kn, q, tab, ln, plan)
+    out2, lse2 = pba.paged_decode_shared(pool, q, tab, ln, plan)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
+    assert torch.equal(pool.k.view(torch.int16), kb.view(torch.int16))
+    assert torch.equal(pool.v.view(torch.int16), vb.view(torch.int16))
 
 
 def test_fused_shared_validate_rejects(pba, gpu):
