@@ -243,3 +243,96 @@ def test_fused_shared_validate_rejects(pba, gpu):
         torch.cuda.synchronize()
         assert torch.equal(pool.k.view(torch.int16), kb.view(torch.int16))
         assert torch.equal(pool.v.view(torch.int16), vb.view(torch.int16))
+
+
+def test_fused_shared_graph_replay(pba, gpu):
+    """The shared-prefix step (block_copy of the copy-on-write pairs, then
+    paged_decode_shared_append) captured in a HIP graph: every replay, with
+    eager calls and synchronisations between replays, equals the eager step
+    bit for bit (pool bytes, out, lse) and leaves the counters at zero; the
+    result matches the oracle."""
+    import bench
+
+    w = wl.shared_prefix(children=6, prefix=300, lo=3, hi=40, num_blocks=160)
+    say("fused shared graph replay", w.shape, "seed", w.seed)
+    plan = bench.plan_script(w)
+    assert len(plan.step_src) > 0 and len(plan.step_slots) == 6
+    ex = execute(w)
+    k_rows, v_rows = wl.kv_rows(w, ex.n_writes)
+    opool = oracle_pool(ex, k_rows, v_rows)
+    kd, vd = to_device(k_rows, "bf16", gpu), to_device(v_rows, "bf16", gpu)
+    k0, v0 = wl.pool_poison(w)
+    pools = [pba.KVPool(to_device(k0, "bf16", gpu), to_device(v0, "bf16", gpu)) for _ in range(2)]
+    for pool in pools:
+        for op in plan.setup:
+            if op[0] == "copy":
+                pba.block_copy(pool, torch.from_numpy(op[1]).to(gpu), torch.from_numpy(op[2]).to(gpu))
+            else:
+                pba.kv_append(pool, torch.from_numpy(op[1]).to(gpu), kd[op[2]:op[3]], vd[op[2]:op[3]])
+    P, Hkv, D = w.shape.block_size, w.shape.num_kv_heads, w.shape.head_dim
+    Hq = w.shape.num_q_heads
+    order = sharing_order(plan.tables)
+    tables = np.ascontiguousarray(plan.tables[order])
+    lens = np.ascontiguousarray(plan.seq_lens[order])
+    B = len(lens)
+    splan = pba.SharedPlan.from_host(shared_plan(tables, lens, P, Hq // Hkv, 256,
+                                                 tiles_per_item=2), gpu)
+    # Row (sharing order) of each new token: the row whose last position it is.
+    last = {int(tables[r, (T - 1) // P]) * P + (T - 1) % P: r for r, T in enumerate(lens)}
+    rows = [last[int(s)] for s in plan.step_slots]
+    ns = np.full(B, -1, dtype=np.int64)
+    ns[rows] = plan.step_slots
+    lo, hi = plan.step_rows
+    knew = torch.zeros((B, Hkv, D), dtype=torch.bfloat16, device=gpu)
+    vnew = torch.zeros_like(knew)
+    idx = torch.tensor(rows, dtype=torch.int64, device=gpu)
+    knew[idx] = kd[lo:hi]
+    vnew[idx] = vd[lo:hi]
+    new_slots = torch.from_numpy(ns).to(gpu)
+    src = torch.from_numpy(plan.step_src).to(gpu)
+    dst = torch.from_numpy(plan.step_dst).to(gpu)
+    qb = np.ascontiguousarray(wl.q_bits(w)[order])
+    q = to_device(qb, "bf16", gpu)
+    tab, ln = torch.from_numpy(tables).to(gpu), torch.from_numpy(lens).to(gpu)
+    ws_bytes = pba.paged_decode_shared_workspace_bytes(pools[0], Hq, B, tables.shape[1], splan)
+    assert ws_bytes > 0
+    bufs = [dict(out=torch.empty((B, Hq, D), dtype=torch.float32, device=gpu),
+                 lse=torch.empty((B, Hq), dtype=torch.float32, device=gpu),
+                 ws=torch.zeros(ws_bytes, dtype=torch.uint8, device=gpu)) for _ in range(2)]
+
+    def step(pool, b):
+        pba.block_copy(pool, src, dst)
+        pba.paged_decode_shared_append(pool, new_slots, knew, vnew, q, tab, ln, splan,
+                                       out=b["out"], lse=b["lse"], workspace=b["ws"])
+
+    step(pools[0], bufs[0])                    # eager reference, validated
+    torch.cuda.synchronize()
+    pba.set_validate(False)
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(pools[1], bufs[1])            # warm the graph's buffers once
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(pools[1], bufs[1])
+        for rep in range(3):
+            bufs[1]["out"].fill_(float("nan"))
+            bufs[1]["lse"].fill_(float("nan"))
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(bufs[1]["out"], bufs[0]["out"]), rep
+            assert torch.equal(bufs[1]["lse"], bufs[0]["lse"]), rep
+            assert torch.equal(pools[1].k.view(torch.int16), pools[0].k.view(torch.int16)), rep
+            assert torch.equal(pools[1].v.view(torch.int16), pools[0].v.view(torch.int16)), rep
+            assert torch.count_nonzero(bufs[1]["ws"][:4 * B * Hkv]).item() == 0
+            step(pools[0], bufs[0])            # eager work between replays
+            torch.cuda.synchronize()
+    finally:
+        pba.set_validate(True)
+    assert np.array_equal(to_bits(pools[1].k), opool.k) and np.array_equal(to_bits(pools[1].v), opool.v)
+    ref, ref_lse = att.paged_decode(opool, qb, list(tables), lens, 1 / math.sqrt(D))
+    assert np.max(np.abs(bufs[1]["out"].cpu().numpy() - ref)) <= TOL
+    assert np.max(np.abs(bufs[1]["lse"].cpu().numpy() - ref_lse)) <= TOL
