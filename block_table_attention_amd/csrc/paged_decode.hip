@@ -1595,14 +1595,16 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_shared_kernel(
   if ((int)blockIdx.z < sa.nz_items) {
     const int fa = blockIdx.y + gridDim.y * blockIdx.z;
     if (fa >= sa.n_items + sa.n_packed) return;
-    packed = fa >= sa.n_items;
+    packed = fa < sa.n_packed;
   }
   if (packed) {
-    // Four rows' private ranges, one wave each (after the items, same planes).
-    row0 = 4 * (blockIdx.y + gridDim.y * blockIdx.z - sa.n_items);
+    // Four rows' private ranges, one wave each, ahead of the items in the
+    // same planes: short groups that store their states and leave, so that
+    // the rows' merges fall to the items (longest first) that end last.
+    row0 = 4 * (blockIdx.y + gridDim.y * blockIdx.z);
     nrows = min(4, a.batch - row0);
   } else if ((int)blockIdx.z < sa.nz_items) {
-    const int fa = blockIdx.y + gridDim.y * blockIdx.z;
+    const int fa = blockIdx.y + gridDim.y * blockIdx.z - sa.n_packed;
     item_t* it = (item_t*)(sa.items + (int64_t)kItemInts * fa);
     row0 = it[0];
     nrows = it[1];

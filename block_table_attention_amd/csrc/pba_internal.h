@@ -80,7 +80,7 @@ struct SharedArgs {
   const int32_t* items;
   const int32_t* row_private;  // [batch][2]
   int32_t n_items;
-  int32_t n_packed;  // work-groups of four rows' private ranges after the items (0: none)
+  int32_t n_packed;  // work-groups of four rows' private ranges before the items (0: none)
   int32_t nz_items;  // grid z planes of items and packed groups: ceil((n_items + n_packed) / batch)
 };
 

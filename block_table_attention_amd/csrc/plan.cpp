@@ -151,6 +151,30 @@ extern "C" int pba_shared_plan_build(const int32_t* tables, int32_t width, const
     }
     for (int r = c.row_begin; r < c.row_end; ++r) next_slot[r] += pieces;
   }
+  // Longest walk first: a work-group's waves split an item's 32-key chunks
+  // (all four waves over one or two tiles, two waves per tile pair of a
+  // four-tile item), and the grid starts items in array order as CUs free
+  // up, so an item with many steps per wave that came last would finish
+  // last.  Slots are fixed per item, so the order changes no result.
+  {
+    const int64_t n = (int64_t)its.size() / 8;
+    std::vector<int64_t> perm(n), steps(n);
+    for (int64_t i = 0; i < n; ++i) {
+      const int32_t* it = &its[(size_t)i * 8];
+      const int64_t chunks = ((int64_t)it[3] - it[2] + 31) / 32;
+      const int waves = it[5] == 4 ? 2 : 4;  // waves that split one tile group's chunks
+      steps[i] = (chunks + waves - 1) / waves;
+      perm[i] = i;
+    }
+    std::stable_sort(perm.begin(), perm.end(), [&](int64_t x, int64_t y) {
+      if (steps[x] != steps[y]) return steps[x] > steps[y];
+      return its[(size_t)x * 8 + 5] > its[(size_t)y * 8 + 5];
+    });
+    std::vector<int32_t> sorted(its.size());
+    for (int64_t i = 0; i < n; ++i)
+      std::copy(&its[(size_t)perm[i] * 8], &its[(size_t)perm[i] * 8] + 8, &sorted[(size_t)i * 8]);
+    its.swap(sorted);
+  }
   int64_t max_slots = 1, priv_parts = 1, priv_tokens = 1, partial = 0;
   for (int32_t r = 0; r < batch; ++r) {
     const int64_t rest = std::max<int64_t>(0, (int64_t)lens[r] - priv[r]);

@@ -542,7 +542,9 @@ typedef struct pba_shared_plan {
  * Every chunk is cut into pieces of partition_tokens keys from its first key;
  * the rows of a piece form 16-column tiles of 16 / G rows, up to
  * tiles_per_item per item.  A row's slots are its chunks' pieces in path
- * order, then its private pieces.  Returns PBA_ERR_WORKSPACE_TOO_SMALL (info
+ * order, then its private pieces.  Items are listed longest walk first (32-key
+ * chunks per wave, then tiles), the order the decode starts them in; their
+ * slots do not depend on it.  Returns PBA_ERR_WORKSPACE_TOO_SMALL (info
  * filled, nothing else written) when items or chunks exceed their capacity.
  */
 typedef struct pba_shared_plan_params {
