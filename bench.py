@@ -4,7 +4,11 @@
 A step is one pass of the whole hot path over the decode batch:
   block_copy of the step's copy-on-write pairs, kv_append of the step's new
   tokens (the trailing one-token appends of the workload's script), and
-  paged_decode of one query row per request of the batch.
+  paged_decode of one query row per request of the batch.  When every new
+  token is its row's last position in a block only that row reads, the
+  appends ride in the decode call (paged_decode_append, or
+  paged_decode_shared_append under a shared-prefix plan); --step separate
+  keeps kv_append as a launch of its own.
 
 Default workload: long16k -- 8 requests x 16,384 tokens of context at decode
 (16,383 prefilled + 1 appended per step), block size 64, 64 q-heads / 8
