@@ -226,6 +226,40 @@ def visible_slots(tables: np.ndarray, lens: np.ndarray, P: int) -> np.ndarray:
     return np.concatenate(out)
 
 
+def step_rows_if_fusable(plan: Plan, P: int):
+    """Decode row of each of the step's new tokens, in the step's order, when
+    the decode call can append them (None otherwise): every new token is its
+    row's last position (one token per row) in a block no other row of the
+    batch reads -- the copy-on-write rule, so no work-group reads a position
+    that another one writes."""
+    if len(plan.step_slots) == 0:
+        return None
+    last = {int(plan.tables[r, (T - 1) // P]) * P + (T - 1) % P: r
+            for r, T in enumerate(plan.seq_lens)}
+    rows = [last.get(int(sl), -1) for sl in plan.step_slots]
+    if min(rows) < 0 or len(set(rows)) != len(rows):
+        return None
+    refs = {}
+    for r, T in enumerate(plan.seq_lens):
+        for b in plan.tables[r, :-(-int(T) // P)]:
+            refs[int(b)] = refs.get(int(b), 0) + 1
+    if any(refs[int(sl) // P] != 1 for sl in plan.step_slots):
+        return None
+    return rows
+
+
+def shared_step_rows(rows, order, host_plan, lens_sorted):
+    """The same rows in the sharing order of a shared-prefix plan, or None
+    when a new token lies outside its row's private range (a chunk's blocks
+    are shared)."""
+    pos = np.empty(len(order), dtype=np.int64)
+    pos[order] = np.arange(len(order))
+    rows = [int(pos[r]) for r in rows]
+    if any(host_plan.row_private[r, 0] > lens_sorted[r] - 1 for r in rows):
+        return None
+    return rows
+
+
 def decode_bytes(plan: Plan, shape):
     """(unique K/V bytes, logical K/V bytes, algorithmic bytes of one decode)."""
     P, Hq, Hkv, d = shape.block_size, shape.num_q_heads, shape.num_kv_heads, shape.head_dim
@@ -378,20 +412,8 @@ def run_workload(args, name, pba, torch, dev):
     copy_dst = torch.from_numpy(plan.step_dst).to(dev)
     qb = wl.q_bits(w)
     B = len(plan.seq_lens)
-    # Fused step: each new token of the step is its decode row's last position
-    # (the appends of a decode step), so the decode call appends them.
-    last_slot = np.array([int(plan.tables[r, (T - 1) // P]) * P + (T - 1) % P
-                          for r, T in enumerate(plan.seq_lens)], dtype=np.int64)
-    row_of_slot = {int(sl): r for r, sl in enumerate(last_slot)}
-    step_row = [row_of_slot.get(int(sl), -1) for sl in plan.step_slots]
-    # ... in a block no other row of the batch reads (the copy-on-write rule).
-    refs = {}
-    for r, T in enumerate(plan.seq_lens):
-        for b in plan.tables[r, :-(-int(T) // P)]:
-            refs[int(b)] = refs.get(int(b), 0) + 1
-    fusable = (len(plan.step_slots) > 0 and min(step_row) >= 0 and
-               len(set(step_row)) == len(step_row) and
-               all(refs[int(sl) // P] == 1 for sl in plan.step_slots))
+    step_row = step_rows_if_fusable(plan, P)
+    fusable = step_row is not None
     tables, lens_h = plan.tables, plan.seq_lens
     # Shared-prefix execution: the caller orders the batch so rows sharing
     # leading blocks are adjacent and describes the shared chunks.
@@ -408,10 +430,9 @@ def run_workload(args, name, pba, torch, dev):
             tables, lens_h, qb, host_plan = tables[order], lens_h[order], qb[order], cand
             # Decode rows in sharing order; the fused step also needs each new
             # token inside its row's private range.
-            pos = np.empty(B, dtype=np.int64)
-            pos[order] = np.arange(B)
-            step_row = [int(pos[r]) for r in step_row]
-            fusable = fusable and all(cand.row_private[r, 0] <= lens_h[r] - 1 for r in step_row)
+            if fusable:
+                step_row = shared_step_rows(step_row, order, cand, lens_h)
+                fusable = step_row is not None
     path = "shared" if host_plan is not None else "plain"
     q = dev_bits(qb)
     tab_d = torch.from_numpy(np.ascontiguousarray(tables)).to(dev)

@@ -103,3 +103,46 @@ def test_planner_edit_voids_profiled_traffic():
             assert bench.profiled_traffic("long16k", tmp) == 1234, rel
     finally:
         shutil.rmtree(tmp)
+
+
+def test_fused_step_eligibility():
+    """The bench fuses the step's appends into the decode call only when every
+    new token is its row's last position in a block no other row reads, and,
+    under a shared-prefix plan, inside its row's private range."""
+    import numpy as np
+
+    import bench
+    from block_table_attention_amd.blocks import shared_plan, sharing_order
+
+    w = bench.make_workload("long16k")
+    plan = bench.plan_script(w)
+    assert bench.step_rows_if_fusable(plan, 64) == list(range(8))
+
+    w = bench.make_workload("shared_prefix")
+    plan = bench.plan_script(w)
+    rows = bench.step_rows_if_fusable(plan, 16)
+    assert rows is not None and len(rows) == 64 and len(plan.step_src) > 0
+    order = sharing_order(plan.tables)
+    lens = plan.seq_lens[order]
+    hp = shared_plan(plan.tables[order], lens, 16, 4, 1024, tiles_per_item=2)
+    srows = bench.shared_step_rows(rows, order, hp, lens)
+    assert srows is not None and sorted(order[srows].tolist()) == sorted(rows)
+    # A plan whose range starts past a new token: the token would sit in a chunk.
+    hp.row_private = hp.row_private.copy()
+    hp.row_private[srows[0], 0] = lens[srows[0]]
+    assert bench.shared_step_rows(rows, order, hp, lens) is None
+
+    def plan_of(tables, lens, slots):
+        t = np.array(tables, np.int32)
+        return bench.Plan([], np.zeros(0, np.int32), np.zeros(0, np.int32),
+                          np.array(slots, np.int64), (0, len(slots)), t,
+                          np.array(lens, np.int32), len(slots))
+
+    # Two rows ending in one block (a fork that has not written yet): no.
+    assert bench.step_rows_if_fusable(plan_of([[4, 5], [4, 5]], [20, 20], [5 * 16 + 3]), 16) is None
+    # Row 1 reads row 0's last block: no.
+    assert bench.step_rows_if_fusable(plan_of([[4, 5], [5, 6]], [20, 20], [5 * 16 + 3]), 16) is None
+    # A slot that is not a last position: no.  Each row alone: yes.
+    assert bench.step_rows_if_fusable(plan_of([[4, 5], [7, 6]], [20, 20], [5 * 16 + 2]), 16) is None
+    assert bench.step_rows_if_fusable(plan_of([[4, 5], [7, 6]], [20, 20], [6 * 16 + 3, 5 * 16 + 3]),
+                                      16) == [1, 0]
