@@ -1219,12 +1219,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
 //    both tiles from one K/V load, so one read serves up to 64 query columns.
 //  * sequence-first item (grid z >= nz_items): a piece of one row's private
 //    range [private_begin, T), split from private_begin.  These planes come
-//    last in dispatch order: the long chunk-first items start first (putting
-//    the short private tails first made the launch 10-40 % longer).
-//  * packed private group (item index n_items .. n_items + n_packed - 1, in
-//    the chunk-first planes; only when the plan bounds every private range
-//    to a few chunks): the private ranges of four consecutive rows, one wave
-//    each, in place of the sequence-first planes.
+//    last in dispatch order, after the chunk-first items (which the planner
+//    lists longest walk first).
+//  * packed private group (flat index 0 .. n_packed - 1 of the chunk-first
+//    planes, ahead of the items; only when the plan bounds every private
+//    range to a few chunks): the private ranges of four consecutive rows,
+//    one wave each, in place of the sequence-first planes.  Short and first,
+//    they store their states and leave, so the rows' merges fall to the
+//    items that end last.
 // Every item leaves one partial state per column in its row's slot list; the
 // last contributor of a (row, kv head) merges the row's slots in slot order,
 // so the result does not depend on which work-group finishes last.
