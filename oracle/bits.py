@@ -15,13 +15,17 @@ SCALAR_BYTES = {"bf16": 2, "f32": 4}
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
-    """bfloat16 is the upper half of a binary32: shift into place, widen."""
+    """bfloat16 is the upper half of a binary32: shift into place, widen.
+    Signalling-NaN payloads (poisoned pool rows) widen to NaN; numpy's
+    warning about them is silenced."""
     wide = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return wide.view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return wide.view(np.float32).astype(np.float64)
 
 
 def f32_bits_to_f64(bits) -> np.ndarray:
-    return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
+    with np.errstate(invalid="ignore"):
+        return np.asarray(bits, dtype=np.uint32).view(np.float32).astype(np.float64)
 
 
 def bits_to_f64(bits, dtype: str) -> np.ndarray:

@@ -33,7 +33,7 @@ each B R bytes, so base(V_1) = 3 B R as in the pages' fixture.
 """
 from __future__ import annotations
 
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np

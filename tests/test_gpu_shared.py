@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import workloads as wl
-from block_table_attention_amd.blocks import BlockManager, shared_plan, sharing_order
+from block_table_attention_amd.blocks import shared_plan, sharing_order
 from harness import execute, gpu_pool, gpu_replay, oracle_pool, to_device
 from oracle import attention as att
 

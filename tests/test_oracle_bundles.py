@@ -16,7 +16,6 @@ appends and copies, and the all-or-nothing bundle allocator.
   of a layered pool equals a single-layer pool replayed with that layer's rows.
 * Half bundles are rejected before any group changes.
 """
-import itertools
 
 import numpy as np
 import pytest
@@ -24,7 +23,7 @@ import pytest
 from oracle import attention as att
 from oracle import bundles as bd
 from oracle.allocator import BlockAllocator, OutOfBlocks
-from oracle.pool import BitPool, replay
+from oracle.pool import replay
 
 
 def manifests(P0=16, P1=16, nb0=8, nb1=8, layers=(24, 8), H=4, d=128, dtype="bf16",

@@ -1,7 +1,6 @@
 """Pins for oracle.vattention: the pages' vAttention address algebra and
 ledgers, the slot/page lifecycle (retention, reclamation, all-or-nothing
 mapping), and decode over contiguous slot rows."""
-import math
 
 import numpy as np
 import pytest
