@@ -817,7 +817,14 @@ __device__ void lds_merge_item(const DecodeArgs& a, const FlatArgs& f, const flo
   }
 }
 
-template <int D, int MODE>
+// kFused (dense tables): the step's new tokens are written in the launch.  A
+// row's token for kv head h goes to the pool from the wave that walks the
+// last chunk of segment (row, h), before that wave requests the chunk (with
+// 64-token or larger blocks, before the request of the even chunk whose V
+// load also brings the last chunk's V).  Each wave keeps the token of the
+// segment it is walking in registers and requests the next segment's token
+// when it writes one, so the rows arrive a step ahead of their store.
+template <int D, int MODE, bool kFused = false>
 __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     const int32_t* __restrict__ tables, const int32_t* __restrict__ seq_lens,
     const void* __restrict__ kbase, const void* __restrict__ vbase, int32_t max_blocks,
@@ -992,6 +999,41 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
     // block holds 64 tokens or more: the even chunk's load brings both.
     const bool pairs = log2P >= 6;
     bool have2 = false;  // vf2 holds the V of the chunk after the one in vf
+    // Fused step: the token of segment (nt_r, nt_h), written before the
+    // request of chunk kx of that segment when kx (or, in pairs, kx + 1) is
+    // its last chunk.
+    NewToken nt;
+    nt.slot = -1;
+    int nt_r = -1, nt_h = 0;
+    auto load_token = [&](int rr, int hh) {
+      nt_r = rr;
+      nt_h = hh;
+      nt.slot = -1;
+      if (rr >= 0) {
+        nt.slot = ((const int64_t __attribute__((address_space(4)))*)a.new_slots)[rr];
+        load_new_token<D>(nt, a, rr, hh, lane);
+      }
+    };
+    auto write_token_before = [&](const PoolView& pw, int rx, int hx, int kx, int nchx) {
+      if (rx == nt_r && hx == nt_h &&
+          (kx == nchx - 1 || (pairs && !(kx & 1) && kx + 1 == nchx - 1))) {
+        if (nt.slot >= 0) store_new_token<D>(nt, pw, hx, lane);
+        // The next segment: the next kv head, else the next row with tokens.
+        int r3 = rx, h3 = hx + 1;
+        if (h3 == H) {
+          h3 = 0;
+          do {
+            ++r3;
+          } while (r3 < B && uni(s_T[r3]) <= 0);
+          if (r3 >= B) r3 = -1;
+        }
+        load_token(r3, h3);
+      }
+    };
+    if constexpr (kFused) {
+      load_token(r, h);
+      write_token_before(pv, r, h, k, nch);
+    }
     {
       load_q(qraw, r, h);
       int64_t pb0, pb1;
@@ -1045,6 +1087,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_bf16_flat_kernel(
         }
       }
       const PoolView pvn = r2 == r ? pv : view(r2, T2);
+      if constexpr (kFused) {
+        if (!last) write_token_before(pvn, r2, h2, k2, nch2);
+      }
       u32x4 qnext[KK];
       if (new_seg) load_q(qnext, r2, h2);
       // The prefetched chunk (k2): its V came with the previous load, or it
@@ -1898,6 +1943,18 @@ hipError_t launch_paged_decode_flat(const DecodeArgs& a, const FlatArgs& f, int 
   hipLaunchKernelGGL((decode_bf16_flat_kernel<DD, MM>), grid, block, lds, stream, a.tables,     \
                      a.seq_lens, a.k, a.v, a.max_blocks, a.log2P, a.num_blocks - 1,            \
                      (int32_t)a.k_sb, (int32_t)a.k_sh, a, f)
+  if (a.new_slots) {  // fused steps come with dense tables only
+    if (a.table_mode != kTablesDense) return hipErrorInvalidValue;
+    if (head_dim == 128)
+      hipLaunchKernelGGL((decode_bf16_flat_kernel<128, kTablesDense, true>), grid, block, lds,
+                         stream, a.tables, a.seq_lens, a.k, a.v, a.max_blocks, a.log2P,
+                         a.num_blocks - 1, (int32_t)a.k_sb, (int32_t)a.k_sh, a, f);
+    else
+      hipLaunchKernelGGL((decode_bf16_flat_kernel<64, kTablesDense, true>), grid, block, lds,
+                         stream, a.tables, a.seq_lens, a.k, a.v, a.max_blocks, a.log2P,
+                         a.num_blocks - 1, (int32_t)a.k_sb, (int32_t)a.k_sh, a, f);
+    return hipGetLastError();
+  }
   if (head_dim == 128) {
     if (a.table_mode == kTablesRagged) PBA_FLAT(128, kTablesRagged);
     else if (a.table_mode == kTablesContiguous) PBA_FLAT(128, kTablesContiguous);

@@ -806,13 +806,13 @@ int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
   a.new_slots = nullptr;
   a.k_new = a.v_new = nullptr;
   if (fused) {
-    if (!flat && pool->dtype == PBA_BF16) {
+    if (pool->dtype == PBA_BF16 && (!flat || a.table_mode == pba::kTablesDense)) {
       a.new_slots = fused->slots;
       a.k_new = fused->k;
       a.v_new = fused->v;
     } else {
-      // The balanced and fp32 decodes take the appends as a launch of their
-      // own, ahead of the decode on the same stream.
+      // The fp32 decode takes the appends as a launch of its own, ahead of
+      // the decode on the same stream.
       pba::AppendArgs ap;
       ap.k = const_cast<void*>(pool->k);
       ap.v = const_cast<void*>(pool->v);

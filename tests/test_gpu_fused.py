@@ -6,10 +6,11 @@ new token appended and the batch decoded in one call.
 * Against the oracle: the pool bit for bit (after every append of the
   workload), the decode within 2e-3.
 * Shapes: block sizes 16-256, head_dim 64 and 128, G 1-16, partitions of the
-  library plan, 256 and 512 tokens and the balanced decomposition (appends in
-  their own launch), fp32 pools (likewise), rows that append nothing, rows
-  whose new token falls in a wave's first chunk, a kernel view of an
-  allocator pool, and the 8 x 16,384-token workload at full size.
+  library plan, 256 and 512 tokens and the balanced decomposition (bf16: the
+  appends in its launch), fp32 pools (the appends in a launch of their own),
+  rows that append nothing, rows whose new token falls in a wave's first
+  chunk, a kernel view of an allocator pool, the balanced decomposition over
+  hundreds of short rows, and the 8 x 16,384-token workload at full size.
 * Validate mode rejects a slot that is not the row's last position, and a
   new token in a block another row references, with nothing written.
 Every case prints its name, shapes and seed (flushed) before its GPU work.
@@ -126,6 +127,23 @@ def test_fused_step_matches_separate_calls(pba, gpu, case, partition_tokens):
     appends[0] = 1
     w = step_workload(dtype, P, d, Hkv, G, lengths, appends, 20261202 + 5000 + case)
     run_fused(pba, w, gpu, appends, partition_tokens)
+
+
+@pytest.mark.parametrize("P,rows,longest", [(16, 400, 300), (64, 1200, 120), (256, 400, 300),
+                                             (64, 400, 300)])
+def test_fused_step_balanced_many_segments(pba, gpu, P, rows, longest):
+    """The balanced decomposition with the appends in its launch: hundreds of
+    rows of 1 to a few hundred tokens, so waves cross many (request, kv head)
+    segments, start and end inside them, and (P >= 64) meet last chunks of
+    both parities behind paired V loads; two rows in three append."""
+    rng = np.random.default_rng(20261202 + 5300 + P + rows)
+    lengths = [int(x) for x in rng.integers(1, longest + 1, size=rows)]
+    appends = [1 if r % 3 else 0 for r in range(rows)]
+    for r, T in enumerate(lengths):
+        if T == 1:
+            appends[r] = 1          # a row whose only token is the step's
+    w = step_workload("bf16", P, 128, 2, 4, lengths, appends, 20261202 + 5300 + P + rows)
+    run_fused(pba, w, gpu, appends, -1)
 
 
 def test_fused_step_kernel_view(pba, gpu):
