@@ -146,13 +146,15 @@ def test_fused_step_balanced_many_segments(pba, gpu, P, rows, longest):
     run_fused(pba, w, gpu, appends, -1)
 
 
-def test_fused_step_kernel_view(pba, gpu):
-    """A 64-token allocator pool read as 16-token kernel blocks: the new
-    token's slot is the same in both views."""
+@pytest.mark.parametrize("partition_tokens", [512, -1])
+def test_fused_step_kernel_view(pba, gpu, partition_tokens):
+    """A 64-token allocator pool read as 16-token kernel blocks, with
+    partitions and with the balanced decomposition: the new token's slot is
+    the same in both views."""
     lengths = [3, 64, 65, 700, 1500]
     appends = [1] * len(lengths)
     w = step_workload("bf16", 64, 128, 2, 4, lengths, appends, 20261202 + 5100)
-    run_fused(pba, w, gpu, appends, 512, kernel_block=16)
+    run_fused(pba, w, gpu, appends, partition_tokens, kernel_block=16)
 
 
 def test_fused_step_long16k(pba, gpu):
