@@ -1799,7 +1799,37 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_f32_kernel(DecodeArgs a
     for (int e = 0; e < DPL; ++e) u[gg][e] = 0.f;
   }
 
+  // Fused step: the wave whose chunk holds T - 1 writes the row's new token
+  // (K: D / 4 lanes of four floats; V: a lane per dim, P apart) just before
+  // it reads that chunk.
+  int t_new = -1;
+  int64_t slot_new = -1;
+  if (a.new_slots && p_end == T) {
+    slot_new = a.new_slots[r];
+    const int c_new = (T - 1 - p_begin) / CH;
+    if (slot_new >= 0 && c_new % kWaves == wave) t_new = p_begin + c_new * CH;
+  }
+
   for (int t0 = p_begin + wave * CH; t0 < p_end; t0 += kWaves * CH) {
+    if (t0 == t_new) {
+      const int64_t pbn = slot_new >> log2P;
+      const int offn = (int)(slot_new & (P - 1));
+      const int rown = ((int)(pbn & qmask) << log2P) + offn;
+      const int64_t src = ((int64_t)r * a.num_kv_heads + h) * D;
+      if (lane < D / 4)
+        *reinterpret_cast<f32x4*>(const_cast<float*>(kpool) + (pbn >> split) * a.k_sb +
+                                  (int64_t)h * a.k_sh + (int64_t)rown * D + 4 * lane) =
+            *reinterpret_cast<const f32x4*>(static_cast<const float*>(a.k_new) + src + 4 * lane);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        const int c = lane + 64 * e;
+        const_cast<float*>(vpool)[(pbn >> split) * a.v_sb + (int64_t)h * a.v_sh +
+                                  (int64_t)c * (P << split) + rown] =
+            static_cast<const float*>(a.v_new)[src + c];
+      }
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
     const int t = t0 + lane;
     const bool valid = t < T;
     const int j = min(t >> log2P, nblk - 1);
@@ -1905,7 +1935,8 @@ hipError_t launch_paged_decode(const DecodeArgs& a, int dtype, int head_dim, hip
     s.ws_u = a.ws_u ? a.ws_u + rows * a.n_parts * head_dim : nullptr;
     s.counters = a.counters ? a.counters + (int64_t)r0 * a.num_kv_heads : nullptr;
     if (a.new_slots) {
-      const int64_t new_row = (int64_t)r0 * a.num_kv_heads * head_dim * 2;  // bytes (bf16)
+      const int64_t new_row =
+          (int64_t)r0 * a.num_kv_heads * head_dim * (dtype == PBA_BF16 ? 2 : 4);  // bytes
       s.new_slots = a.new_slots + r0;
       s.k_new = static_cast<const char*>(a.k_new) + new_row;
       s.v_new = static_cast<const char*>(a.v_new) + new_row;

@@ -806,29 +806,12 @@ int decode_impl(const pba_kv_pool* pool, const void* q, int32_t num_q_heads,
   a.new_slots = nullptr;
   a.k_new = a.v_new = nullptr;
   if (fused) {
-    if (pool->dtype == PBA_BF16 && (!flat || a.table_mode == pba::kTablesDense)) {
-      a.new_slots = fused->slots;
-      a.k_new = fused->k;
-      a.v_new = fused->v;
-    } else {
-      // The fp32 decode takes the appends as a launch of its own, ahead of
-      // the decode on the same stream.
-      pba::AppendArgs ap;
-      ap.k = const_cast<void*>(pool->k);
-      ap.v = const_cast<void*>(pool->v);
-      ap.k_sb = pool->k_stride_block;
-      ap.k_sh = pool->k_stride_head;
-      ap.v_sb = pool->v_stride_block;
-      ap.v_sh = pool->v_stride_head;
-      ap.slots = fused->slots;
-      ap.k_new = fused->k;
-      ap.v_new = fused->v;
-      ap.n = batch;
-      ap.log2P = log2_exact(pool->block_size) + pool->split_log2;  // allocator tiles
-      ap.head_dim = pool->head_dim;
-      ap.kv_heads = pool->num_kv_heads;
-      if (pba::launch_kv_append(ap, esize_of(pool->dtype), s) != hipSuccess) return PBA_ERR_HIP;
-    }
+    // Every decomposition writes the step's tokens in its own launch, from
+    // the wave that reads each of them (fused steps come with dense tables).
+    if (a.table_mode != pba::kTablesDense) return PBA_ERR_UNSUPPORTED;
+    a.new_slots = fused->slots;
+    a.k_new = fused->k;
+    a.v_new = fused->v;
   }
   if (flat) {
     pba::FlatArgs f;

@@ -296,10 +296,9 @@ int pba_paged_decode(const pba_kv_pool* pool, const void* q, int32_t num_q_heads
  *                 undefined
  *   k_new, v_new  device [batch, num_kv_heads, head_dim], pool dtype,
  *                 contiguous, 16-byte aligned: the new tokens' K and V rows
- * Other arguments as pba_paged_decode (the same workspace size).  bf16 pools
- * write each new token from the wave that reads it, in the decode launch
- * (with partitions, and with PBA_PARTITIONS_BALANCED); fp32 pools launch the
- * appends first, on the same stream.
+ * Other arguments as pba_paged_decode (the same workspace size).  Each new
+ * token is written, in the decode launch, by the wave that reads it (bf16
+ * and fp32 pools; partitions and PBA_PARTITIONS_BALANCED alike).
  */
 int pba_paged_decode_append(const pba_kv_pool* pool, const int64_t* new_slots, const void* k_new,
                             const void* v_new, const void* q, int32_t num_q_heads,

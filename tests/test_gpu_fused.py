@@ -6,11 +6,11 @@ new token appended and the batch decoded in one call.
 * Against the oracle: the pool bit for bit (after every append of the
   workload), the decode within 2e-3.
 * Shapes: block sizes 16-256, head_dim 64 and 128, G 1-16, partitions of the
-  library plan, 256 and 512 tokens and the balanced decomposition (bf16: the
-  appends in its launch), fp32 pools (the appends in a launch of their own),
-  rows that append nothing, rows whose new token falls in a wave's first
-  chunk, a kernel view of an allocator pool, the balanced decomposition over
-  hundreds of short rows, and the 8 x 16,384-token workload at full size.
+  library plan, 256 and 512 tokens and the balanced decomposition, fp32 pools
+  (every one of them appends in the decode launch), rows that append
+  nothing, rows whose new token falls in a wave's first chunk, kernel views
+  of an allocator pool, the balanced decomposition over hundreds of short
+  rows, and the 8 x 16,384-token workload at full size.
 * Validate mode rejects a slot that is not the row's last position, and a
   new token in a block another row references, with nothing written.
 Every case prints its name, shapes and seed (flushed) before its GPU work.
